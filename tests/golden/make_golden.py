@@ -1,0 +1,58 @@
+"""Writes the closed-form fixtures in this folder. Run: python tests/golden/make_golden.py
+
+The values are computed in exact rational arithmetic (Python's fractions), from
+the definition of the odd quintic p(s) = a*s + b*s^3 + c*s^5 with
+(a, b, c) = (3.4445, -4.7750, 2.0315). Nothing here calls the GPU path or the
+oracle's matrix code; the fixtures pin the oracle from the outside.
+"""
+from fractions import Fraction
+from pathlib import Path
+
+A, B, C = Fraction("3.4445"), Fraction("-4.7750"), Fraction("2.0315")
+
+
+def p(s: Fraction) -> Fraction:
+    return A * s + B * s ** 3 + C * s ** 5
+
+
+def orbit(s0: Fraction, n: int):
+    out, s = [s0], s0
+    for _ in range(n):
+        s = p(s)
+        out.append(s)
+    return out
+
+
+def main() -> None:
+    here = Path(__file__).resolve().parent
+    lines = [
+        "# p^k(s0) for the Newton-Schulz quintic p(s) = a s + b s^3 + c s^5,",
+        "# (a, b, c) = (3.4445, -4.7750, 2.0315); exact rationals rounded to 17 digits.",
+        "# Citation: closed form of the per-singular-value map of the iteration",
+        "# X <- aX + b(XX^T)X + c(XX^T)^2 X (the odd-quintic reading of the",
+        "# Newton-Schulz step the digest page names in its footnote 4).",
+        "# columns: s0 k value",
+    ]
+    for s0 in (Fraction(1), Fraction(1, 2), Fraction(1, 10), Fraction(1, 100)):
+        for k, v in enumerate(orbit(s0, 8)):
+            lines.append(f"{s0} {k} {float(v):.17g}")
+    (here / "quintic_orbit.txt").write_text("\n".join(lines) + "\n")
+
+    # A 2x3 worked projection example, exact: W = [[3,4,0],[0,0,0]], O = [[1,0,0],[0,0,2]],
+    # lr = 1, R = 5: W' = [[2,4,0],[0,0,-2]], ||W'||^2 = 24, W_new = (5/sqrt(24)) W'.
+    lines = [
+        "# Hand-checkable hyperball projection: W <- R (W - lr O) / ||W - lr O||_F",
+        "# (digest page, section \"The load-bearing tricks aren't in the abstract\").",
+        "# W = [[3,4,0],[0,0,0]], O = [[1,0,0],[0,0,2]], lr = 1, R = 5",
+        "# W' = [[2,4,0],[0,0,-2]], ||W'||_F^2 = 24; expected = 5/sqrt(24) * W'",
+        "# row-major expected values:",
+    ]
+    import math
+    s = 5.0 / math.sqrt(24.0)
+    vals = [2 * s, 4 * s, 0.0, 0.0, 0.0, -2 * s]
+    lines.append(" ".join(f"{v:.17g}" for v in vals))
+    (here / "projection_2x3.txt").write_text("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()

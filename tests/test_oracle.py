@@ -1,0 +1,400 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Nothing here compares the oracle with a retyped copy of its own formulas. The
+pins are: the singular-value closed form (SVD brute force on tiny matrices),
+exact-rational orbits of the scalar quintic (tests/golden), hand-checkable
+projection values (tests/golden), invariants of the Newton-Schulz map
+(transpose, scale and orthogonal equivariance), the band the quintic maps
+singular values into, and the special cases the method reduces to (zero
+gradient, zero learning rate, beta = 0, zero iterations). The last section
+plants plausible mistakes in copies of the oracle's Newton-Schulz and
+projection steps and checks that at least one pin fails for each.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+# The quintic coefficients, written here independently of the oracle's copy.
+A_, B_, C_ = 3.4445, -4.7750, 2.0315
+
+
+def p_scalar(s, k):
+    s = np.asarray(s, dtype=np.float64)
+    for _ in range(k):
+        s = A_ * s + B_ * s ** 3 + C_ * s ** 5
+    return s
+
+
+def load_orbit():
+    rows = {}
+    for line in (GOLDEN / "quintic_orbit.txt").read_text().splitlines():
+        if not line or line.startswith("#"):
+            continue
+        s0, k, v = line.split()
+        rows[(float(Fraction(s0)), int(k))] = float(v)
+    return rows
+
+
+def rand(shape, key, std=1.0):
+    return workloads.host_custom(shape, std, key).astype(np.float64)
+
+
+def random_orthogonal(n, key):
+    q, r = np.linalg.qr(rand((n, n), key))
+    return q * np.sign(np.diag(r))
+
+
+# ----------------------------------------------------------------------------
+# Pin checks, written against an arbitrary Newton-Schulz callable so the
+# mutation tests at the bottom can reuse them.
+# ----------------------------------------------------------------------------
+
+def svd_closed_form_error(ns, m, k, eps=oracle.NS_EPS):
+    """Max abs error of ns(m, k) vs U diag(p^k(sigma/(||M||+eps))) V^T."""
+    u, s, vt = np.linalg.svd(m, full_matrices=False)
+    scale = np.linalg.norm(m) + eps
+    expected = (u * p_scalar(s / scale, k)) @ vt
+    return float(np.max(np.abs(ns(m, k) - expected)))
+
+
+def check_svd_closed_form(ns):
+    for idx, (r, c) in enumerate([(24, 40), (40, 24), (17, 17), (64, 96), (5, 3)]):
+        m = rand((r, c), (1, idx))
+        for k in (0, 1, 2, 5, 8):
+            if svd_closed_form_error(ns, m, k) > 1e-11:
+                return False
+    return True
+
+
+def check_rank_one_orbit(ns):
+    orbit = load_orbit()
+    u = rand((12, 1), (2, 0))
+    v = rand((1, 20), (2, 1))
+    m = 3.7 * (u / np.linalg.norm(u)) @ (v / np.linalg.norm(v))
+    uv = m / 3.7
+    for k in range(9):
+        o = ns(m, k, eps=0.0)
+        # rounding grows about 3.5x per iteration (|p'| along the orbit)
+        if np.max(np.abs(o - orbit[(1.0, k)] * uv)) > 1e-11:
+            return False
+    return True
+
+
+def check_orthonormal_rows(ns):
+    q = random_orthogonal(96, (3, 0))
+    for mrows in (8, 32):
+        m = q[:mrows, :]                      # M M^T = I, ||M||_F = sqrt(mrows)
+        for k in (1, 5):
+            expected = p_scalar(1.0 / (math.sqrt(mrows) + oracle.NS_EPS), k) * m
+            if np.max(np.abs(ns(m, k) - expected)) > 1e-12:
+                return False
+            if np.max(np.abs(ns(m.T, k) - expected.T)) > 1e-12:
+                return False
+    return True
+
+
+def check_diagonal(ns):
+    d = np.array([3.0, -1.0, 0.5, 2.0, -0.25])
+    m = np.zeros((5, 7))
+    m[np.arange(5), np.arange(5)] = d
+    for k in (1, 3, 5):
+        expected = np.zeros_like(m)
+        expected[np.arange(5), np.arange(5)] = p_scalar(d / (np.linalg.norm(d) + oracle.NS_EPS), k)
+        if np.max(np.abs(ns(m, k) - expected)) > 1e-12:
+            return False
+    return True
+
+
+def check_equivariance(ns):
+    m = rand((20, 36), (4, 0))
+    o = ns(m, 5)
+    if np.max(np.abs(ns(m.T, 5) - o.T)) > 1e-12:
+        return False
+    q1, q2 = random_orthogonal(20, (4, 1)), random_orthogonal(36, (4, 2))
+    if np.max(np.abs(ns(q1 @ m @ q2, 5) - q1 @ o @ q2)) > 1e-11:
+        return False
+    if np.max(np.abs(ns(7.5 * m, 5, eps=0.0) - ns(m, 5, eps=0.0))) > 1e-12:
+        return False
+    return True
+
+
+def check_projection_golden(project):
+    lines = [l for l in (GOLDEN / "projection_2x3.txt").read_text().splitlines()
+             if l and not l.startswith("#")]
+    expected = np.array([float(v) for v in lines[0].split()]).reshape(2, 3)
+    w = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 0.0]])
+    o = np.array([[1.0, 0.0, 0.0], [0.0, 0.0, 2.0]])
+    got = project(w, o, 5.0, 1.0)
+    return bool(np.max(np.abs(got - expected)) <= 1e-15 * 8)
+
+
+def check_projection_sphere(project):
+    for idx, (r, c) in enumerate([(16, 48), (48, 16), (33, 33)]):
+        w = rand((r, c), (5, idx), 0.02)
+        o = oracle.newton_schulz(rand((r, c), (5, 10 + idx)), 5)
+        radius = 0.7
+        wn = project(w, o, radius, 0.02)
+        if abs(np.linalg.norm(wn) - radius) > 1e-13:
+            return False
+        trial = w - 0.02 * o
+        cos = np.sum(wn * trial) / (np.linalg.norm(wn) * np.linalg.norm(trial))
+        if abs(cos - 1.0) > 1e-13:
+            return False
+    return True
+
+
+# ----------------------------------------------------------------------------
+# The pins applied to the oracle.
+# ----------------------------------------------------------------------------
+
+def test_coefficients_are_the_quintic():
+    assert oracle.NS_COEFFS == (A_, B_, C_)
+    assert oracle.NS_EPS == 1e-7
+    # p(1) = a + b + c
+    assert abs(p_scalar(1.0, 1) - 0.701) < 1e-15
+
+
+def test_golden_orbit_matches_float_iteration():
+    orbit = load_orbit()
+    for (s0, k), v in orbit.items():
+        assert abs(float(p_scalar(s0, k)) - v) < 1e-14
+
+
+def test_ns_svd_closed_form():
+    assert check_svd_closed_form(oracle.newton_schulz)
+
+
+def test_ns_svd_closed_form_large_rectangular():
+    m = rand((64, 160), (6, 0), 0.01)
+    assert svd_closed_form_error(oracle.newton_schulz, m, 5) < 1e-12
+    assert svd_closed_form_error(oracle.newton_schulz, m.T, 8) < 1e-12
+
+
+def test_ns_rank_one_golden():
+    assert check_rank_one_orbit(oracle.newton_schulz)
+
+
+def test_ns_orthonormal_rows():
+    assert check_orthonormal_rows(oracle.newton_schulz)
+
+
+def test_ns_diagonal_entrywise():
+    assert check_diagonal(oracle.newton_schulz)
+
+
+def test_ns_equivariances():
+    assert check_equivariance(oracle.newton_schulz)
+
+
+@pytest.mark.parametrize("k", [5, 8])
+def test_ns_band(k):
+    # Normalised singular values >= 1e-2 land in [0.6818, 1.1344] after 5 or 8
+    # iterations: the quintic maps that interval into itself (next test) and
+    # lifts every value >= 1e-2 into it within 5 steps.
+    n = 48
+    u = random_orthogonal(n, (7, 0))
+    v = random_orthogonal(80, (7, 1))[:n, :]
+    sig = np.geomspace(1.0, 0.05, n)
+    m = (u * sig) @ v
+    sig_hat = sig / (np.linalg.norm(sig) + oracle.NS_EPS)
+    assert sig_hat.min() >= 1e-2
+    o = oracle.newton_schulz(m, k)
+    s = np.linalg.svd(o, compute_uv=False)
+    assert s.min() >= 0.6818 - 1e-9 and s.max() <= 1.1344 + 1e-9
+    # every output singular value is the scalar map of an input one
+    np.testing.assert_allclose(np.sort(s), np.sort(np.abs(p_scalar(sig_hat, k))), rtol=0, atol=1e-12)
+
+
+def test_quintic_band_is_invariant():
+    grid = np.linspace(0.6818, 1.1344, 200001)
+    img = p_scalar(grid, 1)
+    assert img.min() >= 0.6818 - 1e-6 and img.max() <= 1.1344 + 1e-6
+    # fixed points 0.8680 (repelling within the band) and 1.2637
+    for fp in (0.8680, 1.2637):
+        assert abs(float(p_scalar(fp, 1)) - fp) < 2e-4
+
+
+def test_ns_zero_iterations_is_normalised_momentum():
+    m = rand((9, 13), (8, 0))
+    o = oracle.newton_schulz(m, 0)
+    np.testing.assert_allclose(o, m / (np.linalg.norm(m) + 1e-7), rtol=0, atol=1e-15)
+
+
+def test_ns_zero_input():
+    o = oracle.newton_schulz(np.zeros((6, 10)), 5)
+    assert np.all(o == 0.0)
+
+
+def test_projection_golden():
+    assert check_projection_golden(oracle.hyperball_project)
+
+
+def test_projection_sphere_and_direction():
+    assert check_projection_sphere(oracle.hyperball_project)
+
+
+def test_projection_degenerate_zero_radius():
+    w = np.zeros((3, 4))
+    o = np.zeros((3, 4))
+    assert np.all(oracle.hyperball_project(w, o, 0.0, 0.02) == 0.0)
+
+
+def test_momentum_hand_values():
+    m = np.array([[1.0, -2.0], [0.5, 0.0]])
+    g = np.array([[2.0, 1.0], [-1.0, 3.0]])
+    np.testing.assert_array_equal(oracle.momentum_update(m, g, 0.5),
+                                  np.array([[2.5, 0.0], [-0.75, 3.0]]))
+    np.testing.assert_array_equal(oracle.momentum_update(m, g, 0.0), g)
+
+
+def test_step_zero_gradient_zero_momentum_keeps_w():
+    w = rand((12, 20), (9, 0), 0.02)
+    r = oracle.init_radius(w)
+    w1, m1, o = oracle.muonh_step(w, np.zeros_like(w), np.zeros_like(w), r, 0.02, 0.95, 5)
+    assert np.all(m1 == 0.0) and np.all(o == 0.0)
+    np.testing.assert_allclose(w1, w, rtol=1e-14, atol=0)
+
+
+def test_step_zero_gradient_momentum_only():
+    # G = 0, M != 0: the update is NS(beta*M) = NS(M) (scale invariance), and
+    # W moves by that momentum term, then returns to the sphere.
+    w = rand((12, 20), (10, 0), 0.02)
+    m = rand((12, 20), (10, 1), 0.01)
+    r = oracle.init_radius(w)
+    # eps = 0 makes the scale invariance exact (eps only enters as eps/||M||)
+    w1, m1, o = oracle.muonh_step(w, np.zeros_like(w), m, r, 0.02, 0.9, 5, eps=0.0)
+    np.testing.assert_allclose(m1, 0.9 * m, rtol=1e-15)
+    np.testing.assert_allclose(o, oracle.newton_schulz(m, 5, eps=0.0), rtol=0, atol=1e-12)
+    assert abs(np.linalg.norm(w1) - r) < 1e-13
+
+
+def test_step_zero_lr_keeps_w_on_sphere():
+    w = rand((16, 8), (11, 0), 0.02)
+    r = oracle.init_radius(w)
+    w1, _, _ = oracle.muonh_step(w, rand((16, 8), (11, 1), 0.01), np.zeros_like(w), r, 0.0, 0.95, 5)
+    np.testing.assert_allclose(w1, w, rtol=1e-14, atol=0)
+
+
+def test_step_beta_zero_momentum_is_gradient():
+    w = rand((8, 8), (12, 0), 0.02)
+    g = rand((8, 8), (12, 1), 0.01)
+    m = rand((8, 8), (12, 2), 0.01)
+    _, m1, _ = oracle.muonh_step(w, g, m, oracle.init_radius(w), 0.02, 0.0, 5)
+    np.testing.assert_array_equal(m1, g)
+
+
+def test_trajectory_stays_on_sphere_small_workload():
+    wl = workloads.WORKLOADS["single_128x256"]
+    w = workloads.host_weight(wl, 0).astype(np.float64)
+    r = oracle.init_radius(w)
+    m = np.zeros_like(w)
+    for step in range(wl.steps):
+        g = workloads.host_grad(wl, 0, step)
+        w, m, o = oracle.muonh_step(w, g, m, r, wl.lr, wl.beta, wl.ns_iters[0])
+        assert abs(np.linalg.norm(w) / r - 1.0) < 1e-12
+        s = np.linalg.svd(o, compute_uv=False)
+        assert s.max() < 1.2025 and s.min() > 0.0
+
+
+# ----------------------------------------------------------------------------
+# Planted mistakes: each mutant differs from the oracle by one plausible bug
+# and must be caught by at least one pin.
+# ----------------------------------------------------------------------------
+
+def _ns_mutant(kind):
+    a, b, c = oracle.NS_COEFFS
+
+    def ns(m, k, eps=oracle.NS_EPS):
+        x = np.asarray(m, dtype=np.float64)
+        t = x.shape[0] > x.shape[1]
+        if t and kind != "no_transpose_back":
+            x = x.T
+        elif t:
+            x = x.T
+        nrm = np.linalg.norm(x)
+        if kind == "eps_inside_sqrt":
+            x = x / math.sqrt(nrm * nrm + eps)
+        elif kind == "no_normalise":
+            pass
+        elif kind == "max_norm":
+            x = x / (np.abs(x).max() + eps)
+        else:
+            x = x / (nrm + eps)
+        for _ in range(k):
+            g = x @ x.T
+            if kind == "swap_bc":
+                poly = c * g + b * (g @ g)
+            elif kind == "drop_quintic":
+                poly = b * g
+            elif kind == "minus_b":
+                poly = -b * g + c * (g @ g)
+            else:
+                poly = b * g + c * (g @ g)
+            if kind == "a_times_poly":
+                x = a * (x + poly @ x)
+            elif kind == "extra_iteration":
+                x = a * x + poly @ x
+                g = x @ x.T
+                x = a * x + (b * g + c * (g @ g)) @ x
+            else:
+                x = a * x + poly @ x
+        if t and kind == "no_transpose_back":
+            return x.reshape(m.shape)
+        return x.T if t else x
+
+    return ns
+
+
+NS_MUTANTS = ["no_transpose_back", "eps_inside_sqrt", "no_normalise", "max_norm", "swap_bc",
+              "drop_quintic", "minus_b", "a_times_poly", "extra_iteration"]
+
+
+@pytest.mark.parametrize("kind", NS_MUTANTS)
+def test_planted_ns_mistake_is_caught(kind):
+    ns = _ns_mutant(kind)
+    caught = (not check_svd_closed_form(ns) or not check_rank_one_orbit(ns)
+              or not check_orthonormal_rows(ns) or not check_diagonal(ns)
+              or not check_equivariance(ns))
+    assert caught, f"mutant {kind} passed every pin"
+
+
+def test_unmutated_copy_passes_every_pin():
+    ns = _ns_mutant("none")
+    assert check_svd_closed_form(ns) and check_rank_one_orbit(ns)
+    assert check_orthonormal_rows(ns) and check_diagonal(ns) and check_equivariance(ns)
+
+
+def _project_mutant(kind):
+    def project(w, o, radius, lr):
+        w = np.asarray(w, dtype=np.float64)
+        o = np.asarray(o, dtype=np.float64)
+        trial = w + lr * o if kind == "plus_lr" else w - lr * o
+        if kind == "norm_of_w":
+            n = np.linalg.norm(w)
+        elif kind == "squared_norm":
+            n = np.sum(trial * trial)
+        else:
+            n = np.linalg.norm(trial)
+        if kind == "no_radius":
+            return trial / n
+        if kind == "scale_w_only":
+            return (radius / n) * w - lr * o
+        return (radius / n) * trial
+
+    return project
+
+
+@pytest.mark.parametrize("kind", ["plus_lr", "norm_of_w", "squared_norm", "no_radius", "scale_w_only"])
+def test_planted_projection_mistake_is_caught(kind):
+    pr = _project_mutant(kind)
+    assert not (check_projection_golden(pr) and check_projection_sphere(pr))
