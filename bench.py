@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""MuonH optimizer-step benchmark on one MI355X.
+
+A step is one full MuonH step over the whole matrix set: momentum, the
+normalised bf16 cast, 5 Newton-Schulz iterations (Gram, polynomial, apply) on
+bf16 MFMA with fp32 accumulation, the trial update and the projection onto
+each matrix's init-norm sphere. Inputs are synthetic and seeded (workloads.py)
+and already resident in HBM when the timed region starts.
+
+Prints ONE JSON line: params updated per second for the whole set, step time,
+the roofline of the dominant kernel (from HIP events recorded inside the
+timed steps), and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload qwen3_2b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "MuonH step time & params updated/s (2B-shaped set); NS TFLOP/s % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def ns_flops(shapes, k):
+    """Algorithmic Newton-Schulz flops per launch of each phase (one iteration).
+
+    Per matrix with short side s and long side l: the Gram X X^T is symmetric,
+    s^2 l; the polynomial's A A is symmetric, s^3; the apply B X is 2 s^2 l.
+    """
+    gram = poly = apply = 0.0
+    for r, c in shapes:
+        s, l = min(r, c), max(r, c)
+        gram += float(s) * s * l
+        poly += float(s) ** 3
+        apply += 2.0 * s * s * l
+    return {"gram": gram, "poly": poly, "apply": apply}
+
+
+def elementwise_bytes(n_params, ns_bytes):
+    """Algorithmic HBM bytes of the streaming phases, per step.
+
+    before Newton-Schulz: momentum reads G, M and writes M (12 B/param);
+      the cast reads M and writes X and X^T (4 + 2*ns_bytes B/param);
+    after: the trial-norm pass reads W and O (4 + ns_bytes), the projection
+      reads W and O and writes W (8 + ns_bytes).
+    """
+    pre = n_params * (12 + 4 + 2 * ns_bytes)
+    post = n_params * (4 + ns_bytes + 8 + ns_bytes)
+    return pre, post
+
+
+def cpu_baseline(wl, k, budget_s):
+    """The fp64 oracle on the host, on one matrix of each distinct shape,
+    extrapolated by count to the whole set (matrices are independent)."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    groups = wl.shape_groups()
+    per_shape_budget = budget_s / max(len(groups), 1)
+    total = 0.0
+    used = 0.0
+    parts = []
+    for (r, c), idx in groups:
+        i = idx[0]
+        w = workloads.host_weight(wl, i)
+        g = workloads.host_grad(wl, i, 0)
+        m = np.zeros_like(w)
+        radius = oracle.init_radius(w)
+        runs = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.muonh_step(w, g, m, radius, wl.lr, wl.beta, k)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= per_shape_budget or runs >= 5:
+                break
+        t = el / runs
+        used += el
+        total += t * len(idx)
+        parts.append(f"{r}x{c}: {t:.3f} s x {len(idx)}")
+    return {
+        "value": wl.n_params / total,
+        "unit": "params/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": ("one fp64 oracle step (momentum, Newton-Schulz k=%d, projection) of one matrix "
+                   "per distinct shape, timed over %.1f s and extrapolated by matrix count to the "
+                   "full set (%s); est. %.1f s per full step" % (k, used, "; ".join(parts), total)),
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_2b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--ns-iters", type=int, default=None)
+    ap.add_argument("--ns-fp32", action="store_true", help="fp32 Newton-Schulz (debug mode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this MuonH build runs on one GPU only (no collectives); "
+              f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import orthogonalized_updates_amd as mh
+    if not mh.LIB_PATH.exists():
+        import __graft_entry__
+        __graft_entry__.build()
+
+    wl = workloads.WORKLOADS[args.workload]
+    k = args.ns_iters if args.ns_iters is not None else wl.ns_iters[0]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    opt = mh.MuonH(wl.shapes, ns_fp32=args.ns_fp32, device=dev)
+
+    print(f"[bench] {wl.name}: {wl.n_matrices} matrices, {wl.n_params} params, k={k}, "
+          f"workspace {opt.plan.workspace_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+    W = [workloads.device_weight_(wl, i, torch.empty(s, device=dev)) for i, s in enumerate(wl.shapes)]
+    M = [torch.zeros(s, device=dev) for s in wl.shapes]
+    # Distinct gradients per step (pool bounded to ~96 GB), generated before timing.
+    per_set = 4 * wl.n_params
+    pool = max(1, min(args.warmup + args.steps, int(96e9 // per_set)))
+    G = []
+    for p in range(pool):
+        G.append([workloads.device_grad_(wl, i, p, torch.empty(s, device=dev))
+                  for i, s in enumerate(wl.shapes)])
+    opt.init(W)
+    torch.cuda.synchronize(dev)
+
+    for w in range(args.warmup):
+        opt.step(W, G[w % pool], M, wl.lr, wl.beta, k)
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps), gradient pool {pool}", file=sys.stderr,
+          flush=True)
+
+    n_ev = 3 * k + 3
+    events = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        for e in evs:
+            e.record()  # creates the HIP event
+        events.append(evs)
+    torch.cuda.synchronize(dev)
+
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    # Phase durations from the events recorded inside the timed steps.
+    pre = post = 0.0
+    phase = {"gram": 0.0, "poly": 0.0, "apply": 0.0}
+    for evs in events:
+        pre += evs[0].elapsed_time(evs[1])
+        for it in range(k):
+            phase["gram"] += evs[1 + 3 * it].elapsed_time(evs[2 + 3 * it])
+            phase["poly"] += evs[2 + 3 * it].elapsed_time(evs[3 + 3 * it])
+            phase["apply"] += evs[3 + 3 * it].elapsed_time(evs[4 + 3 * it])
+        post += evs[n_ev - 2].elapsed_time(evs[n_ev - 1])
+    nst = args.steps
+    launches = nst * k
+    flops = ns_flops(wl.shapes, k)
+    ns_ms = sum(phase.values()) / nst
+    ns_tflops = (sum(flops.values()) * k) / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+    peak_mfma = PEAK_FP32_MFMA_TFLOPS if args.ns_fp32 else PEAK_BF16_TFLOPS
+    ns_bytes = 4 if args.ns_fp32 else 2
+    pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes)
+    pre_ms, post_ms = pre / nst, post / nst
+    dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
+
+    kernel_names = {"gram": "k_ns_gemm<Gram>", "poly": "k_ns_gemm<Poly>", "apply": "k_ns_gemm<Apply>"}
+    if dom is not None:
+        avg_ms = phase[dom] / launches
+        achieved = flops[dom] / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4), "traffic": None,
+                    "kernel": kernel_names[dom], "avg_launch_ms": round(avg_ms, 4),
+                    "algorithmic_flop_per_launch": flops[dom]}
+    else:
+        gbs = (pre_b + post_b) / ((pre_ms + post_ms) * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": wl.n_params * nst / elapsed,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": nst,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if args.ns_fp32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.notes}", "matrices": wl.n_matrices,
+                   "params": wl.n_params, "ns_iters": k, "lr": wl.lr, "beta": wl.beta,
+                   "master_weights": "fp32", "ns_operands": "fp32" if args.ns_fp32 else "bf16"},
+        "roofline": roofline,
+        "phases": {
+            "ns_ms": round(ns_ms, 4),
+            "ns_tflops_algorithmic": round(ns_tflops, 2),
+            "ns_frac_of_peak": round(ns_tflops / peak_mfma, 4),
+            "gram_ms": round(phase["gram"] / nst, 4), "poly_ms": round(phase["poly"] / nst, 4),
+            "apply_ms": round(phase["apply"] / nst, 4),
+            "pre_ns_ms": round(pre_ms, 4), "post_ns_ms": round(post_ms, 4),
+            "pre_ns_gbs": round(pre_b / (pre_ms * 1e-3) / 1e9, 1) if pre_ms > 0 else None,
+            "post_ns_gbs": round(post_b / (post_ms * 1e-3) / 1e9, 1) if post_ms > 0 else None,
+            "elementwise_frac_of_hbm": round((pre_b + post_b) / ((pre_ms + post_ms) * 1e-3) / 1e9
+                                             / PEAK_HBM_GBS, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, k, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,175 @@
+/*
+ * muonh.h - C ABI of the MI355X (gfx950) MuonH optimizer step.
+ *
+ * MuonH updates a set of weight matrices with Muon's orthogonalized momentum
+ * update and then puts every matrix back on the sphere of the Frobenius norm
+ * it had at initialization. Sources, cited by page title and section:
+ *   - digest page "Puro-2B trains for $6.9K, attention sinks hit 99%,
+ *     LoopArena tops at 24.69%", section "The load-bearing tricks aren't in
+ *     the abstract" and footnotes 3-4: MuonH extends Muon, fixes each matrix's
+ *     Frobenius norm at its initialization value by projecting updates onto a
+ *     fixed hypersphere; Muon's overhead is its Newton-Schulz iterations;
+ *   - model card "Puro", section "Training": MuonH with hyperball projection
+ *     and zero weight decay on the matrix group; FP32 master weights and
+ *     optimizer state.
+ *
+ * One step, per matrix (rows x cols, row-major fp32):
+ *   M  <- beta*M + G                                  (heavy-ball momentum)
+ *   X0  = M / (||M||_F + 1e-7), transposed when rows > cols
+ *   ns_iters times:  A = X X^T;  B = b*A + c*A*A;  X <- a*X + B*X
+ *                    (a, b, c) = (3.4445, -4.7750, 2.0315)
+ *   O   = X (transposed back)
+ *   W'  = W - lr*O
+ *   W  <- (R / ||W'||_F) * W'        (W <- W' when ||W'||_F == 0)
+ * with R = ||W0||_F captured once by muonh_init. The pages give neither the
+ * momentum rule, nor the polynomial, nor the normalisation: the readings above
+ * are the plainest ones consistent with the pages (no update scale, no weight
+ * decay, no Nesterov).
+ *
+ * Conventions for every call below
+ *   - Matrices are grouped by shape: a plan lists groups {rows, cols, count};
+ *     matrix index i runs over group 0's matrices, then group 1's, etc.
+ *   - W, G, M are DEVICE arrays of n_matrices DEVICE pointers (the layout of
+ *     batched-BLAS pointer arrays); each points to a contiguous row-major
+ *     rows x cols fp32 matrix. R is a DEVICE array of n_matrices floats.
+ *     Pointers that are 16-byte aligned take the vector path; others work
+ *     through a scalar path. W, G and M must not overlap.
+ *   - The workspace is a DEVICE buffer of at least muonh_workspace_bytes(plan)
+ *     bytes, 256-byte aligned, owned by the caller. It holds the bf16 (or fp32)
+ *     Newton-Schulz operands and the norm partials. Its contents after a step
+ *     hold that step's update O until the next call that uses it.
+ *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
+ *     NULL is the default stream). No call synchronises the device.
+ *   - Calls that share a workspace must be ordered by the caller (same stream,
+ *     or events). A plan itself is read-only after creation and may be shared.
+ *   - All argument checks run before any work is enqueued; a call that returns
+ *     an error has enqueued nothing. Negative return values are errors;
+ *     muonh_last_error() gives a message for the calling thread.
+ *   - Non-finite inputs are not errors: they propagate into the results.
+ */
+#ifndef MUONH_H
+#define MUONH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUONH_ABI_VERSION 1
+
+typedef struct muonh_plan muonh_plan;
+
+typedef struct {
+  int32_t rows;   /* rows of every matrix in the group, >= 1 */
+  int32_t cols;   /* columns of every matrix in the group, >= 1 */
+  int32_t count;  /* number of matrices in the group, >= 1 */
+} muonh_group_desc;
+
+enum {
+  MUONH_OK = 0,
+  MUONH_EINVAL = -1,     /* bad argument (null pointer, value out of range) */
+  MUONH_ESHAPE = -2,     /* bad group description or matrix index */
+  MUONH_EWORKSPACE = -3, /* workspace missing, too small or misaligned */
+  MUONH_EHIP = -4,       /* a HIP runtime call failed (see muonh_last_error) */
+  MUONH_ENOMEM = -5      /* host allocation failed */
+};
+
+/* Plan flags. */
+enum {
+  /* Run Newton-Schulz in fp32 (fp32 MFMA) instead of bf16 MFMA with fp32
+   * accumulation. Debug/reference mode: about 16x slower, ~1e-6 accurate. */
+  MUONH_NS_FP32 = 1u
+};
+
+/* Limits. */
+#define MUONH_MAX_GROUPS 4096
+#define MUONH_MAX_MATRICES (1 << 20)
+#define MUONH_MAX_DIM 65536      /* rows and cols */
+#define MUONH_MAX_NS_ITERS 32
+
+/* Library ABI version (MUONH_ABI_VERSION of the built library). */
+int32_t muonh_abi_version(void);
+
+/*
+ * Create a plan for `n_groups` shape groups. Host-only: no HIP call.
+ * flags: 0 or MUONH_NS_FP32. On success *out owns a plan that must be
+ * released with muonh_plan_destroy. Errors: MUONH_EINVAL (null out/groups,
+ * n_groups out of [1, MUONH_MAX_GROUPS], unknown flag), MUONH_ESHAPE (a dim out
+ * of [1, MUONH_MAX_DIM], count < 1, too many matrices), MUONH_ENOMEM.
+ */
+int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t n_groups,
+                      uint32_t flags);
+
+/* Release a plan (NULL is ignored). The caller must not have work in flight
+ * that still needs it: plans hold no device memory, so this never syncs. */
+void muonh_plan_destroy(muonh_plan* plan);
+
+/* Number of matrices, and of matrix entries (parameters), in the plan. */
+int64_t muonh_plan_num_matrices(const muonh_plan* plan);
+int64_t muonh_plan_num_params(const muonh_plan* plan);
+
+/* Bytes of device workspace that muonh_init/muonh_step need. */
+size_t muonh_workspace_bytes(const muonh_plan* plan);
+
+/*
+ * R[i] <- ||W[i]||_F for every matrix (fp32 result of a fixed-order
+ * reduction: fp32 squares within a block, fp64 across blocks). Capture the
+ * radius once, from the initial weights. Deterministic.
+ * Errors: MUONH_EINVAL (null plan/W/R), MUONH_EWORKSPACE, MUONH_EHIP.
+ */
+int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/*
+ * One MuonH step over every matrix of the plan (formula at the top of this
+ * file). W and M are updated in place; G and R are read only.
+ * lr: finite, >= 0 (the caller's effective rate; the model card applies a
+ *     10x multiplier to the matrix group, section "Training").
+ * beta: in [0, 1).  ns_iters: in [0, MUONH_MAX_NS_ITERS].
+ * Results are bitwise deterministic for a given plan and input.
+ * Errors: MUONH_EINVAL, MUONH_EWORKSPACE, MUONH_EHIP.
+ */
+int muonh_step(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
+               const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/*
+ * muonh_step plus phase timing: the same work, with hipEventRecord of the
+ * caller's events on `stream` at the phase boundaries, for profiling.
+ * events: host array of n_events hipEvent_t (created by the caller, with
+ * timing enabled); n_events must be 3*ns_iters + 3. Recorded, in order:
+ *   [0] before the momentum update,
+ *   [1] after momentum, its norm and the normalised cast (Newton-Schulz input),
+ *   [2+3i], [3+3i], [4+3i] after iteration i's Gram, polynomial and apply,
+ *   [3*ns_iters+2] after the trial update, its norm and the projection.
+ * Errors: as muonh_step, plus MUONH_EINVAL for a NULL events array, a NULL
+ * event or a wrong n_events.
+ */
+int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const* G,
+                     float* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+                     void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                     int32_t n_events);
+
+/*
+ * Copy the update O of matrix `index` computed by the last muonh_step that
+ * used this workspace into dst, a DEVICE buffer of rows x cols fp32
+ * (row-major, the matrix's own orientation). For inspection and tests.
+ * Errors: MUONH_EINVAL, MUONH_ESHAPE (index out of range), MUONH_EWORKSPACE,
+ * MUONH_EHIP.
+ */
+int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* muonh_status_string(int status);
+
+/* Message of the last error raised on the calling thread ("" if none). */
+const char* muonh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUONH_H */

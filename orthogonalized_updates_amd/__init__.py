@@ -1,0 +1,251 @@
+"""MI355X (gfx950) MuonH optimizer step: Python binding of libmuonh.so.
+
+The binding only marshals arguments: it groups matrices by shape, builds the
+device arrays of device pointers the C ABI takes (include/muonh.h), allocates
+the workspace with torch and passes torch's current HIP stream. Every step of
+the optimizer runs in the library's HIP kernels. There is no fallback: if the
+library is missing, the first call into it raises ImportError.
+
+MuonH (digest page "Puro-2B trains for $6.9K, attention sinks hit 99%,
+LoopArena tops at 24.69%", section "The load-bearing tricks aren't in the
+abstract"; model card "Puro", section "Training"): momentum, Newton-Schulz
+orthogonalization, then projection of every weight matrix back onto the
+sphere of its initial Frobenius norm, with no weight decay.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Dict, List, Optional, Sequence, Tuple
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libmuonh.so"
+HEADER_PATH = _PKG.parent / "include" / "muonh.h"
+
+MUONH_OK = 0
+MUONH_EINVAL = -1
+MUONH_ESHAPE = -2
+MUONH_EWORKSPACE = -3
+MUONH_EHIP = -4
+MUONH_ENOMEM = -5
+MUONH_NS_FP32 = 1
+
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+class MuonHError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"muonh error {status}: {message}")
+        self.status = status
+
+
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("count", ctypes.c_int32)]
+
+
+def _load_library() -> ctypes.CDLL:
+    if not LIB_PATH.exists():
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m orthogonalized_updates_amd.build` "
+            "(the MuonH step has no non-HIP implementation)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                             ctypes.c_float)
+    sig = {
+        "muonh_abi_version": (i32, []),
+        "muonh_plan_create": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.POINTER(GroupDesc), i32,
+                                             ctypes.c_uint32]),
+        "muonh_plan_destroy": (None, [vp]),
+        "muonh_plan_num_matrices": (i64, [vp]),
+        "muonh_plan_num_params": (i64, [vp]),
+        "muonh_workspace_bytes": (sz, [vp]),
+        "muonh_init": (ctypes.c_int, [vp, vp, vp, vp, sz, vp]),
+        "muonh_step": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp, sz, vp]),
+        "muonh_step_timed": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp, sz, vp,
+                                            ctypes.POINTER(vp), i32]),
+        "muonh_read_update": (ctypes.c_int, [vp, i64, vp, vp, sz, vp]),
+        "muonh_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "muonh_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def get_lib() -> ctypes.CDLL:
+    """The loaded libmuonh.so (loaded on first use; ImportError if not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load_library()
+    return _LIB
+
+
+def __getattr__(name):
+    if name == "lib":
+        return get_lib()
+    raise AttributeError(name)
+
+
+def check(status: int) -> None:
+    if status != MUONH_OK:
+        lib = get_lib()
+        raise MuonHError(status, lib.muonh_last_error().decode(errors="replace")
+                         or lib.muonh_status_string(status).decode())
+
+
+class Plan:
+    """Owns a muonh_plan for shape groups [(rows, cols, count), ...]."""
+
+    def __init__(self, groups: Sequence[Tuple[int, int, int]], ns_fp32: bool = False):
+        arr = (GroupDesc * len(groups))(*[GroupDesc(int(r), int(c), int(n)) for r, c, n in groups])
+        handle = ctypes.c_void_p()
+        check(get_lib().muonh_plan_create(ctypes.byref(handle), arr, len(groups),
+                                    MUONH_NS_FP32 if ns_fp32 else 0))
+        self.handle = handle
+        self.groups = [tuple(int(v) for v in g) for g in groups]
+        self.ns_fp32 = bool(ns_fp32)
+
+    @property
+    def num_matrices(self) -> int:
+        return int(get_lib().muonh_plan_num_matrices(self.handle))
+
+    @property
+    def num_params(self) -> int:
+        return int(get_lib().muonh_plan_num_params(self.handle))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(get_lib().muonh_workspace_bytes(self.handle))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            get_lib().muonh_plan_destroy(h)
+            self.handle = None
+
+
+class MuonH:
+    """MuonH over a list of fp32 weight matrices on one GPU.
+
+    shapes: (rows, cols) of each matrix, in the caller's order. Matrices are
+    grouped by shape internally; every method takes and returns lists in the
+    caller's order.
+    """
+
+    def __init__(self, shapes: Sequence[Tuple[int, int]], *, ns_fp32: bool = False, device=None):
+        import torch
+        get_lib()
+        self.torch = torch
+        self.shapes = [(int(r), int(c)) for r, c in shapes]
+        if not self.shapes:
+            raise ValueError("MuonH needs at least one matrix")
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.type != "cuda":
+            raise ValueError("MuonH runs on a ROCm GPU device only")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        buckets: Dict[Tuple[int, int], List[int]] = {}
+        for i, s in enumerate(self.shapes):
+            buckets.setdefault(s, []).append(i)
+        self.plan_order: List[int] = [i for idx in buckets.values() for i in idx]
+        self.plan_index = {caller: p for p, caller in enumerate(self.plan_order)}
+        self.plan = Plan([(r, c, len(idx)) for (r, c), idx in buckets.items()], ns_fp32=ns_fp32)
+        nbytes = max(self.plan.workspace_bytes, 256)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        if self.workspace.data_ptr() % 256:
+            raise MuonHError(MUONH_EWORKSPACE, "torch returned a workspace that is not 256-aligned")
+        self.R = torch.zeros(len(self.shapes), dtype=torch.float32, device=self.device)
+        self._ptr_cache: Dict[str, Tuple[Tuple[int, ...], object]] = {}
+
+    # -- marshalling ------------------------------------------------------
+    def _check(self, tensors, name: str):
+        torch = self.torch
+        if len(tensors) != len(self.shapes):
+            raise ValueError(f"{name}: expected {len(self.shapes)} tensors, got {len(tensors)}")
+        for i, t in enumerate(tensors):
+            if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+                raise TypeError(f"{name}[{i}] must be a float32 torch tensor")
+            if t.device != self.device:
+                raise ValueError(f"{name}[{i}] is on {t.device}, expected {self.device}")
+            if tuple(t.shape) != self.shapes[i] or not t.is_contiguous():
+                raise ValueError(f"{name}[{i}] must be a contiguous {self.shapes[i]} tensor")
+
+    def _ptr_array(self, name: str, tensors) -> int:
+        ptrs = tuple(int(tensors[c].data_ptr()) for c in self.plan_order)
+        cached = self._ptr_cache.get(name)
+        if cached is None or cached[0] != ptrs:
+            arr = self.torch.tensor(ptrs, dtype=self.torch.int64).to(self.device)
+            self._ptr_cache[name] = (ptrs, arr)
+        return int(self._ptr_cache[name][1].data_ptr())
+
+    def _stream(self) -> int:
+        return int(self.torch.cuda.current_stream(self.device).cuda_stream)
+
+    # -- API ----------------------------------------------------------------
+    def init(self, weights) -> "object":
+        """R[i] = ||W0[i]||_F (device float32, caller order)."""
+        self._check(weights, "weights")
+        r_plan = self.torch.empty_like(self.R)
+        check(get_lib().muonh_init(self.plan.handle, self._ptr_array("W", weights), r_plan.data_ptr(),
+                             self.workspace.data_ptr(), self.workspace.numel(), self._stream()))
+        inv = self.torch.tensor(self.plan_order, dtype=self.torch.int64, device=self.device)
+        self.R = self.torch.empty_like(r_plan).index_copy_(0, inv, r_plan)
+        self._R_plan = r_plan
+        return self.R
+
+    def set_radius(self, radius) -> None:
+        """Restore R (caller order), e.g. from a checkpoint."""
+        r = radius.to(device=self.device, dtype=self.torch.float32).contiguous()
+        if r.numel() != len(self.shapes):
+            raise ValueError("radius must have one entry per matrix")
+        self.R = r
+        inv = self.torch.tensor(self.plan_order, dtype=self.torch.int64, device=self.device)
+        self._R_plan = r.index_select(0, inv)
+
+    def step(self, weights, grads, moms, lr: float, beta: float = 0.95, ns_iters: int = 5) -> None:
+        """One MuonH step: moms and weights are updated in place."""
+        self._check(weights, "weights")
+        self._check(grads, "grads")
+        self._check(moms, "moms")
+        if not hasattr(self, "_R_plan"):
+            raise RuntimeError("call init() (or set_radius()) before step()")
+        check(get_lib().muonh_step(self.plan.handle, self._ptr_array("W", weights),
+                             self._ptr_array("G", grads), self._ptr_array("M", moms),
+                             self._R_plan.data_ptr(), float(lr), float(beta), int(ns_iters),
+                             self.workspace.data_ptr(), self.workspace.numel(), self._stream()))
+
+    def step_timed(self, weights, grads, moms, lr: float, beta: float, ns_iters: int,
+                   events) -> None:
+        """step() plus hipEventRecord of `events` (torch.cuda.Event list of
+        length 3*ns_iters+3, already recorded once) at the phase boundaries."""
+        self._check(weights, "weights")
+        self._check(grads, "grads")
+        self._check(moms, "moms")
+        if not hasattr(self, "_R_plan"):
+            raise RuntimeError("call init() (or set_radius()) before step_timed()")
+        arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+        check(get_lib().muonh_step_timed(self.plan.handle, self._ptr_array("W", weights),
+                                   self._ptr_array("G", grads), self._ptr_array("M", moms),
+                                   self._R_plan.data_ptr(), float(lr), float(beta), int(ns_iters),
+                                   self.workspace.data_ptr(), self.workspace.numel(),
+                                   self._stream(), arr, len(events)))
+
+    def read_update(self, index: int):
+        """The update O of matrix `index` from the last step (fp32, rows x cols)."""
+        r, c = self.shapes[index]
+        out = self.torch.empty((r, c), dtype=self.torch.float32, device=self.device)
+        check(get_lib().muonh_read_update(self.plan.handle, self.plan_index[index], out.data_ptr(),
+                                    self.workspace.data_ptr(), self.workspace.numel(),
+                                    self._stream()))
+        return out
+
+
+__all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
+           "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
+           "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32"]

@@ -1,0 +1,473 @@
+// Host side of the MuonH C ABI (include/muonh.h): plan creation, argument
+// validation, workspace layout and the fixed launch sequence of one step.
+//
+// Step sequence (all grouped launches over every matrix of the plan):
+//   momentum (M <- beta M + G, partial ||M||^2)  -> finalize ||M||
+//   normcast (X0 = M/(||M||+eps) into X and X^T, bf16 or fp32, zero-padded)
+//   ns_iters x { Gram A = X X^T ; Poly B = bA + cAA ; Apply X <- aX + BX }
+//   update (partial ||W - lr O||^2) -> finalize -> project (W <- R W'/||W'||)
+// The projection onto the fixed sphere follows the digest page "Puro-2B
+// trains for $6.9K, attention sinks hit 99%, LoopArena tops at 24.69%",
+// section "The load-bearing tricks aren't in the abstract"; the absence of a
+// weight-decay term follows the model card "Puro", section "Training".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/muonh.h"
+#include "muonh_internal.h"
+
+using namespace muonh;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MUONH_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+struct GroupPlan {
+  int rows, cols, count, first;
+  bool trans;
+  int s, l, sp, lp;
+  int64_t n;            // rows * cols
+  int64_t off;          // workspace byte offset of the group's first matrix block
+  int64_t mat_bytes;    // bytes per matrix block
+  int64_t offX, offXt[2], offA, offB;
+  int bpm;              // streaming blocks per matrix
+};
+
+// Elements one streaming block handles (before the per-matrix partial cap).
+constexpr int64_t kElemsPerBlock = 16384;
+
+}  // namespace
+
+struct muonh_plan {
+  std::vector<GroupPlan> groups;
+  int64_t n_mats = 0;
+  int64_t n_params = 0;
+  uint32_t flags = 0;
+  bool fp32 = false;
+  int esize = 2;
+  int64_t off_partials = 0, off_norm_m = 0, off_norm_w = 0;
+  size_t ws_bytes = 0;
+};
+
+namespace {
+
+bool check_ws(const muonh_plan* p, const void* ws, size_t bytes, int* err) {
+  if (!ws) {
+    *err = fail(MUONH_EWORKSPACE, "workspace is NULL");
+    return false;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) {
+    *err = fail(MUONH_EWORKSPACE, "workspace must be 256-byte aligned");
+    return false;
+  }
+  if (bytes < p->ws_bytes) {
+    *err = fail(MUONH_EWORKSPACE, "workspace has %zu bytes, the plan needs %zu", bytes, p->ws_bytes);
+    return false;
+  }
+  return true;
+}
+
+// Streaming (bpm blocks per matrix) or tile (64x64 tiles of the padded
+// domain) launch descriptors, in batches of at most kMaxEwGroups groups.
+std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final_xt) {
+  std::vector<EwArgs> out;
+  const size_t ng = p->groups.size();
+  for (size_t g0 = 0; g0 < ng; g0 += kMaxEwGroups) {
+    EwArgs a;
+    std::memset(&a, 0, sizeof a);
+    int64_t blocks = 0;
+    const size_t g1 = std::min(ng, g0 + kMaxEwGroups);
+    for (size_t gi = g0; gi < g1; ++gi) {
+      const GroupPlan& G = p->groups[gi];
+      EwGroup& e = a.g[gi - g0];
+      e.rows = G.rows;
+      e.cols = G.cols;
+      e.count = G.count;
+      e.first = G.first;
+      e.bpm = G.bpm;
+      e.n = G.n;
+      e.ns_base = ws + G.off;
+      e.mat_bytes = G.mat_bytes;
+      const int rp = G.trans ? G.lp : G.sp;
+      const int cp = G.trans ? G.sp : G.lp;
+      e.rp = rp;
+      e.cp = cp;
+      // D holds the matrix's own orientation: X for wide matrices, X^T for
+      // tall ones; E the other layout.
+      const int64_t xt = G.offXt[final_xt];
+      e.offD = G.trans ? xt : G.offX;
+      e.offE = G.trans ? G.offX : xt;
+      e.tiles_per_mat = (rp / 64) * (cp / 64);
+      e.block_begin = (int)blocks;
+      blocks += (int64_t)G.count * (tiles ? e.tiles_per_mat : G.bpm);
+    }
+    a.ngroups = (int)(g1 - g0);
+    a.nblocks = (int)blocks;
+    out.push_back(a);
+  }
+  return out;
+}
+
+// GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
+std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters) {
+  const int T = gemm_tile(p->fp32);
+  std::vector<GemmGroup> all;
+  for (const GroupPlan& G : p->groups) {
+    GemmGroup q;
+    std::memset(&q, 0, sizeof q);
+    q.base = ws + G.off;
+    q.mat_bytes = G.mat_bytes;
+    q.count = G.count;
+    q.offE = q.offO1 = q.offO2 = -1;
+    const int ts = G.sp / T, tl = G.lp / T;
+    if (mode == kGram) {
+      q.offP = q.offQ = G.offX;
+      q.ldp = q.ldq = G.lp;
+      q.K = G.lp;
+      q.tm = q.tn = ts;
+      q.tiles_per_mat = ts * (ts + 1) / 2;
+      q.offO1 = G.offA;
+      q.ldo1 = G.sp;
+    } else if (mode == kPoly) {
+      q.offP = q.offQ = G.offA;
+      q.ldp = q.ldq = G.sp;
+      q.K = G.sp;
+      q.tm = q.tn = ts;
+      q.tiles_per_mat = ts * (ts + 1) / 2;
+      q.offE = G.offA;
+      q.lde = G.sp;
+      q.offO1 = G.offB;
+      q.ldo1 = G.sp;
+    } else {
+      const bool last = it == iters - 1;
+      const int xin = (iters - it) & 1, xout = (iters - 1 - it) & 1;
+      q.offP = G.offB;
+      q.ldp = G.sp;
+      q.offQ = G.offXt[xin];
+      q.ldq = G.sp;
+      q.K = G.sp;
+      q.tm = ts;
+      q.tn = tl;
+      q.tiles_per_mat = ts * tl;
+      q.offE = G.offX;
+      q.lde = G.lp;
+      if (!(last && G.trans)) {
+        q.offO1 = G.offX;
+        q.ldo1 = G.lp;
+      }
+      if (!(last && !G.trans)) {
+        q.offO2 = G.offXt[xout];
+        q.ldo2 = G.sp;
+      }
+    }
+    all.push_back(q);
+  }
+  std::stable_sort(all.begin(), all.end(),
+                   [](const GemmGroup& x, const GemmGroup& y) { return x.K > y.K; });
+  std::vector<GemmArgs> out;
+  for (size_t g0 = 0; g0 < all.size(); g0 += kMaxGemmGroups) {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    int64_t tiles = 0;
+    const size_t g1 = std::min(all.size(), g0 + kMaxGemmGroups);
+    for (size_t gi = g0; gi < g1; ++gi) {
+      a.g[gi - g0] = all[gi];
+      a.g[gi - g0].tile_begin = (int)tiles;
+      tiles += (int64_t)all[gi].count * all[gi].tiles_per_mat;
+    }
+    a.ngroups = (int)(g1 - g0);
+    a.ntiles = (int)tiles;
+    if (mode == kPoly) {
+      a.c0 = kNsB;
+      a.c1 = kNsC;
+    } else if (mode == kApply) {
+      a.c0 = kNsA;
+      a.c1 = 1.f;
+    } else {
+      a.c0 = 0.f;
+      a.c1 = 1.f;
+    }
+    out.push_back(a);
+  }
+  return out;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t muonh_abi_version(void) { return MUONH_ABI_VERSION; }
+
+const char* muonh_status_string(int status) {
+  switch (status) {
+    case MUONH_OK: return "ok";
+    case MUONH_EINVAL: return "invalid argument";
+    case MUONH_ESHAPE: return "invalid shape or index";
+    case MUONH_EWORKSPACE: return "invalid workspace";
+    case MUONH_EHIP: return "HIP runtime error";
+    case MUONH_ENOMEM: return "out of host memory";
+    default: return "unknown status";
+  }
+}
+
+const char* muonh_last_error(void) { return g_last_error.c_str(); }
+
+int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t n_groups,
+                      uint32_t flags) {
+  if (!out) return fail(MUONH_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!groups) return fail(MUONH_EINVAL, "groups is NULL");
+  if (n_groups < 1 || n_groups > MUONH_MAX_GROUPS)
+    return fail(MUONH_EINVAL, "n_groups=%d out of [1, %d]", n_groups, MUONH_MAX_GROUPS);
+  if (flags & ~uint32_t(MUONH_NS_FP32)) return fail(MUONH_EINVAL, "unknown flags 0x%x", flags);
+
+  muonh_plan* p = new (std::nothrow) muonh_plan;
+  if (!p) return fail(MUONH_ENOMEM, "plan allocation failed");
+  p->flags = flags;
+  p->fp32 = (flags & MUONH_NS_FP32) != 0;
+  p->esize = p->fp32 ? 4 : 2;
+
+  int64_t n_mats = 0;
+  for (int32_t i = 0; i < n_groups; ++i) {
+    const muonh_group_desc& d = groups[i];
+    if (d.rows < 1 || d.rows > MUONH_MAX_DIM || d.cols < 1 || d.cols > MUONH_MAX_DIM) {
+      delete p;
+      return fail(MUONH_ESHAPE, "group %d: shape %dx%d out of [1, %d]", i, d.rows, d.cols,
+                  MUONH_MAX_DIM);
+    }
+    if (d.count < 1) {
+      delete p;
+      return fail(MUONH_ESHAPE, "group %d: count=%d must be >= 1", i, d.count);
+    }
+    n_mats += d.count;
+    if (n_mats > MUONH_MAX_MATRICES) {
+      delete p;
+      return fail(MUONH_ESHAPE, "more than %d matrices", MUONH_MAX_MATRICES);
+    }
+  }
+  try {
+    p->groups.resize(n_groups);
+  } catch (...) {
+    delete p;
+    return fail(MUONH_ENOMEM, "plan allocation failed");
+  }
+
+  // Workspace: norm partials, two per-matrix norm arrays, then per group the
+  // matrix blocks [X | X^T (two copies) | A | B].
+  int64_t off = 0;
+  p->off_partials = off;
+  off = round_up(off + n_mats * kMaxPartials * (int64_t)sizeof(double), 256);
+  p->off_norm_m = off;
+  off = round_up(off + n_mats * (int64_t)sizeof(double), 256);
+  p->off_norm_w = off;
+  off = round_up(off + n_mats * (int64_t)sizeof(double), 256);
+
+  int first = 0;
+  int64_t params = 0;
+  for (int32_t i = 0; i < n_groups; ++i) {
+    const muonh_group_desc& d = groups[i];
+    GroupPlan& G = p->groups[i];
+    G.rows = d.rows;
+    G.cols = d.cols;
+    G.count = d.count;
+    G.first = first;
+    first += d.count;
+    G.trans = d.rows > d.cols;
+    G.s = std::min(d.rows, d.cols);
+    G.l = std::max(d.rows, d.cols);
+    G.sp = (int)round_up(G.s, kPad);
+    G.lp = (int)round_up(G.l, kPad);
+    G.n = (int64_t)d.rows * d.cols;
+    params += G.n * d.count;
+    const int64_t e = p->esize;
+    const int64_t xs = round_up((int64_t)G.sp * G.lp * e, 256);
+    const int64_t ss = round_up((int64_t)G.sp * G.sp * e, 256);
+    G.offX = 0;
+    G.offXt[0] = xs;
+    G.offXt[1] = 2 * xs;
+    G.offA = 3 * xs;
+    G.offB = 3 * xs + ss;
+    G.mat_bytes = 3 * xs + 2 * ss;
+    G.off = off;
+    off += G.mat_bytes * d.count;
+    int64_t bpm = (G.n + kElemsPerBlock - 1) / kElemsPerBlock;
+    G.bpm = (int)std::max<int64_t>(1, std::min<int64_t>(bpm, kMaxPartials));
+  }
+  p->n_mats = n_mats;
+  p->n_params = params;
+  p->ws_bytes = (size_t)round_up(off, 256);
+  *out = p;
+  return MUONH_OK;
+}
+
+void muonh_plan_destroy(muonh_plan* plan) { delete plan; }
+
+int64_t muonh_plan_num_matrices(const muonh_plan* plan) { return plan ? plan->n_mats : 0; }
+
+int64_t muonh_plan_num_params(const muonh_plan* plan) { return plan ? plan->n_params : 0; }
+
+size_t muonh_workspace_bytes(const muonh_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MUONH_EINVAL, "plan is NULL");
+  if (!W || !R) return fail(MUONH_EINVAL, "W and R must be device arrays");
+  int err = 0;
+  if (!check_ws(plan, workspace, workspace_bytes, &err)) return err;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
+  double* norms = reinterpret_cast<double*>(ws + plan->off_norm_w);
+  hipError_t e;
+  for (const EwArgs& a : make_ew(plan, ws, false, 0)) {
+    if ((e = launch_sumsq(a, W, partials, s)) != hipSuccess) return hip_fail(e, "init sumsq");
+    if ((e = launch_finalize(a, partials, norms, R, s)) != hipSuccess)
+      return hip_fail(e, "init finalize");
+  }
+  return MUONH_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
+              const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
+              size_t workspace_bytes, void* stream, void* const* events, int32_t n_events) {
+  if (!plan) return fail(MUONH_EINVAL, "plan is NULL");
+  if (!W || !G || !M || !R) return fail(MUONH_EINVAL, "W, G, M and R must be device arrays");
+  if (!std::isfinite(lr) || lr < 0.f) return fail(MUONH_EINVAL, "lr=%g must be finite and >= 0", lr);
+  if (!std::isfinite(beta) || beta < 0.f || beta >= 1.f)
+    return fail(MUONH_EINVAL, "beta=%g must be in [0, 1)", beta);
+  if (ns_iters < 0 || ns_iters > MUONH_MAX_NS_ITERS)
+    return fail(MUONH_EINVAL, "ns_iters=%d out of [0, %d]", ns_iters, MUONH_MAX_NS_ITERS);
+  if (events) {
+    if (n_events != 3 * ns_iters + 3)
+      return fail(MUONH_EINVAL, "n_events=%d, expected 3*ns_iters+3 = %d", n_events,
+                  3 * ns_iters + 3);
+    for (int i = 0; i < n_events; ++i)
+      if (!events[i]) return fail(MUONH_EINVAL, "events[%d] is NULL", i);
+  }
+  int err = 0;
+  if (!check_ws(plan, workspace, workspace_bytes, &err)) return err;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
+  double* norm_m = reinterpret_cast<double*>(ws + plan->off_norm_m);
+  double* norm_w = reinterpret_cast<double*>(ws + plan->off_norm_w);
+  const int x0 = ns_iters & 1;  // X^T copy that receives X0^T; the last apply lands in copy 0
+  hipError_t e;
+  int ev = 0;
+  auto mark = [&]() -> hipError_t {
+    if (!events) return hipSuccess;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(events[ev++]), s);
+  };
+
+  const std::vector<EwArgs> stream_args = make_ew(plan, ws, false, 0);
+  const std::vector<EwArgs> tile_args = make_ew(plan, ws, true, x0);
+
+  if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
+  for (const EwArgs& a : stream_args) {
+    if ((e = launch_momentum(a, G, M, beta, partials, s)) != hipSuccess)
+      return hip_fail(e, "momentum");
+    if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "momentum finalize");
+  }
+  for (const EwArgs& a : tile_args)
+    if ((e = launch_normcast(a, plan->fp32, M, norm_m, s)) != hipSuccess)
+      return hip_fail(e, "normcast");
+  if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
+
+  for (int it = 0; it < ns_iters; ++it) {
+    for (const GemmArgs& a : make_gemm(plan, ws, kGram, it, ns_iters))
+      if ((e = launch_gemm(kGram, plan->fp32, a, s)) != hipSuccess) return hip_fail(e, "ns gram");
+    if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
+    for (const GemmArgs& a : make_gemm(plan, ws, kPoly, it, ns_iters))
+      if ((e = launch_gemm(kPoly, plan->fp32, a, s)) != hipSuccess) return hip_fail(e, "ns poly");
+    if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
+    for (const GemmArgs& a : make_gemm(plan, ws, kApply, it, ns_iters))
+      if ((e = launch_gemm(kApply, plan->fp32, a, s)) != hipSuccess)
+        return hip_fail(e, "ns apply");
+    if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
+  }
+
+  for (const EwArgs& a : stream_args) {
+    if ((e = launch_update_norm(a, plan->fp32, W, lr, partials, s)) != hipSuccess)
+      return hip_fail(e, "update norm");
+    if ((e = launch_finalize(a, partials, norm_w, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "update finalize");
+    if ((e = launch_project(a, plan->fp32, W, R, norm_w, lr, s)) != hipSuccess)
+      return hip_fail(e, "project");
+  }
+  if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
+  return MUONH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int muonh_step(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
+               const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return step_impl(plan, W, G, M, R, lr, beta, ns_iters, workspace, workspace_bytes, stream,
+                   nullptr, 0);
+}
+
+int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const* G,
+                     float* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+                     void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                     int32_t n_events) {
+  if (!events) return fail(MUONH_EINVAL, "events is NULL");
+  return step_impl(plan, W, G, M, R, lr, beta, ns_iters, workspace, workspace_bytes, stream,
+                   events, n_events);
+}
+
+int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MUONH_EINVAL, "plan is NULL");
+  if (!dst) return fail(MUONH_EINVAL, "dst is NULL");
+  if (index < 0 || index >= plan->n_mats)
+    return fail(MUONH_ESHAPE, "index %lld out of [0, %lld)", (long long)index,
+                (long long)plan->n_mats);
+  int err = 0;
+  if (!check_ws(plan, workspace, workspace_bytes, &err)) return err;
+  const GroupPlan* G = nullptr;
+  for (const GroupPlan& g : plan->groups)
+    if (index >= g.first && index < g.first + g.count) G = &g;
+  const char* blk = static_cast<const char*>(workspace) + G->off + (index - G->first) * G->mat_bytes;
+  const char* D = blk + (G->trans ? G->offXt[0] : G->offX);
+  const int ld = G->trans ? G->sp : G->lp;
+  hipError_t e = launch_read_update(plan->fp32, D, ld, G->rows, G->cols, dst,
+                                    reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read update");
+  return MUONH_OK;
+}
+
+}  // extern "C"

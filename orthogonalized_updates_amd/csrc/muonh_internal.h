@@ -1,0 +1,108 @@
+// Internal interfaces between the host side of the MuonH library (plan,
+// validation, launch sequence) and its HIP kernels. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muonh {
+
+// Newton-Schulz quintic coefficients and the normalisation epsilon
+// (see include/muonh.h for the step they belong to).
+constexpr float kNsA = 3.4445f;
+constexpr float kNsB = -4.7750f;
+constexpr float kNsC = 2.0315f;
+constexpr double kNsEps = 1e-7;
+
+// Every Newton-Schulz operand is zero-padded to a multiple of this on both
+// sides, so that the MFMA kernels never need bounds checks. Zero rows and
+// columns stay exactly zero through every iteration.
+constexpr int kPad = 256;
+
+// Max number of per-matrix partial sums of a norm reduction.
+constexpr int kMaxPartials = 256;
+
+// ---------------------------------------------------------------------------
+// Elementwise / reduction kernels (elementwise.hip)
+// ---------------------------------------------------------------------------
+constexpr int kMaxEwGroups = 16;
+
+struct EwGroup {
+  int rows, cols;       // matrix shape (row-major fp32)
+  int count, first;     // number of matrices, global index of the first one
+  int bpm;              // blocks per matrix for the streaming kernels
+  int block_begin;      // first block of this group in the launch
+  int64_t n;            // rows * cols
+  // Newton-Schulz buffers of matrix m live at ns_base + m * mat_bytes.
+  char* ns_base;
+  int64_t mat_bytes;
+  // Layouts in the matrix's own orientation: D is rows x cols with leading
+  // dimension cp (holds X0 for wide matrices, X0^T for tall ones, and the
+  // final update O in both cases); E is its transpose, cols x rows with
+  // leading dimension rp.
+  int64_t offD, offE;
+  int rp, cp;           // padded rows / cols
+  int tiles_per_mat;    // 64x64 tiles of the padded rp x cp domain
+};
+
+struct EwArgs {
+  EwGroup g[kMaxEwGroups];
+  int ngroups;
+  int nblocks;
+};
+
+// Norm partials: partials[mat * kMaxPartials + chunk] (double).
+hipError_t launch_sumsq(const EwArgs& a, float* const* W, double* partials, hipStream_t s);
+hipError_t launch_momentum(const EwArgs& a, const float* const* G, float* const* M, float beta,
+                           double* partials, hipStream_t s);
+// norms[mat] = sqrt(sum of partials) for the matrices of the batch `a`;
+// if R != nullptr also R[mat] = (float)norms[mat].
+hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norms, float* R,
+                           hipStream_t s);
+// X0 = M / (norm + eps) written to D (same orientation) and E (transposed).
+hipError_t launch_normcast(const EwArgs& a, bool fp32, const float* const* M, const double* norms,
+                           hipStream_t s);
+hipError_t launch_update_norm(const EwArgs& a, bool fp32, float* const* W, float lr,
+                              double* partials, hipStream_t s);
+hipError_t launch_project(const EwArgs& a, bool fp32, float* const* W, const float* R,
+                          const double* norms, float lr, hipStream_t s);
+// dst (rows x cols fp32) <- D of one matrix.
+hipError_t launch_read_update(bool fp32, const char* D, int ldD, int rows, int cols, float* dst,
+                              hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz MFMA GEMM kernels (ns_gemm.hip)
+//   C[i][j] = sum_k P[i][k] * Q[j][k]  (both operands K-contiguous rows)
+// ---------------------------------------------------------------------------
+constexpr int kMaxGemmGroups = 16;
+
+enum GemmMode : int {
+  kGram = 0,   // O1 = P P^T              (symmetric; upper tiles, mirrored)
+  kPoly = 1,   // O1 = c0*E + c1*(P P^T)  (symmetric; upper tiles, mirrored)
+  kApply = 2,  // v = c0*E + P Q^T; O1[i][j] = v, O2[j][i] = v (either optional)
+};
+
+struct GemmGroup {
+  const char* base;     // first matrix's Newton-Schulz block
+  int64_t mat_bytes;    // stride between matrices
+  int64_t offP, offQ, offE, offO1, offO2;  // byte offsets in a block (-1: absent)
+  int ldp, ldq, lde, ldo1, ldo2;           // leading dimensions, in elements
+  int K;                // contraction length (multiple of kPad)
+  int tm, tn;           // tile grid (symmetric modes: tm == tn, upper triangle)
+  int tiles_per_mat;
+  int tile_begin;
+  int count;
+};
+
+struct GemmArgs {
+  GemmGroup g[kMaxGemmGroups];
+  int ngroups;
+  int ntiles;
+  float c0, c1;
+};
+
+// Tile edge (square tiles) used by the launchers for the given mode/type.
+int gemm_tile(bool fp32);
+hipError_t launch_gemm(GemmMode mode, bool fp32, const GemmArgs& a, hipStream_t s);
+
+}  // namespace muonh

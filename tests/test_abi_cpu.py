@@ -1,0 +1,141 @@
+"""Host-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and its plan and validation logic behaves as documented.
+No call here reaches a HIP runtime function (every case is rejected, or is a
+host-only plan query, before any device work is enqueued)."""
+from __future__ import annotations
+
+import ctypes
+import re
+
+import pytest
+
+import orthogonalized_updates_amd as mh
+
+
+def header_functions():
+    text = mh.HEADER_PATH.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(muonh_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("muonh_plan_create", "muonh_plan_destroy", "muonh_workspace_bytes", "muonh_init",
+              "muonh_step", "muonh_read_update", "muonh_last_error", "muonh_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(mh.LIB_PATH))
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, f"symbols declared in muonh.h but not exported: {missing}"
+
+
+def test_abi_version():
+    assert mh.lib.muonh_abi_version() == 1
+
+
+def _create(groups, flags=0):
+    arr = (mh.GroupDesc * max(len(groups), 1))(*[mh.GroupDesc(*g) for g in groups])
+    h = ctypes.c_void_p()
+    st = mh.lib.muonh_plan_create(ctypes.byref(h), arr, len(groups), flags)
+    return st, h
+
+
+@pytest.mark.parametrize("groups,flags,code", [
+    ([], 0, mh.MUONH_EINVAL),                      # no groups (empty input)
+    ([(4, 4, 1)], 0x10, mh.MUONH_EINVAL),          # unknown flag
+    ([(0, 4, 1)], 0, mh.MUONH_ESHAPE),             # zero rows
+    ([(4, -1, 1)], 0, mh.MUONH_ESHAPE),            # negative cols
+    ([(4, 4, 0)], 0, mh.MUONH_ESHAPE),             # empty group
+    ([(65537, 4, 1)], 0, mh.MUONH_ESHAPE),         # beyond the max dimension
+])
+def test_plan_create_rejects(groups, flags, code):
+    st, h = _create(groups, flags)
+    assert st == code
+    assert h.value is None
+    assert mh.lib.muonh_last_error().decode()
+
+
+def test_plan_create_null_arguments():
+    assert mh.lib.muonh_plan_create(None, None, 1, 0) == mh.MUONH_EINVAL
+    h = ctypes.c_void_p()
+    assert mh.lib.muonh_plan_create(ctypes.byref(h), None, 1, 0) == mh.MUONH_EINVAL
+
+
+def test_plan_counts_and_workspace_growth():
+    p = mh.Plan([(2048, 2048, 56), (512, 2048, 56), (6144, 2048, 56), (2048, 6144, 28)])
+    assert p.num_matrices == 196
+    assert p.num_params == 1_350_565_888
+    # bf16 operands: X, two X^T copies, A and B per matrix, padded to 256
+    ws = p.workspace_bytes
+    ns = 56 * 2 * (3 * 2048 * 2048 + 2 * 2048 * 2048) + 56 * 2 * (3 * 512 * 2048 + 2 * 512 * 512) \
+        + 84 * 2 * (3 * 2048 * 6144 + 2 * 2048 * 2048)
+    assert ns <= ws <= ns + 196 * (256 * 8 + 16) + 4096
+    p32 = mh.Plan([(2048, 2048, 56), (512, 2048, 56), (6144, 2048, 56), (2048, 6144, 28)], ns_fp32=True)
+    assert p32.workspace_bytes > 1.9 * ns
+
+
+def test_plan_padding_of_ragged_shapes():
+    p = mh.Plan([(1, 1, 1)])
+    # one 256x256 block per operand buffer (X, 2 X^T, A, B) in bf16
+    assert p.workspace_bytes >= 5 * 256 * 256 * 2
+    assert p.num_params == 1
+
+
+class _FakeDev:
+    """Non-null addresses that the library must never dereference: every call
+    below fails argument validation first."""
+    ptr = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x100000)
+    misaligned = ctypes.c_void_p(0x100010)
+
+
+@pytest.mark.parametrize("lr,beta,iters,code", [
+    (float("nan"), 0.95, 5, mh.MUONH_EINVAL),
+    (-0.1, 0.95, 5, mh.MUONH_EINVAL),
+    (float("inf"), 0.95, 5, mh.MUONH_EINVAL),
+    (0.02, 1.0, 5, mh.MUONH_EINVAL),
+    (0.02, -0.5, 5, mh.MUONH_EINVAL),
+    (0.02, float("nan"), 5, mh.MUONH_EINVAL),
+    (0.02, 0.95, -1, mh.MUONH_EINVAL),
+    (0.02, 0.95, 33, mh.MUONH_EINVAL),
+])
+def test_step_rejects_bad_scalars(lr, beta, iters, code):
+    p = mh.Plan([(8, 8, 1)])
+    f = _FakeDev
+    st = mh.lib.muonh_step(p.handle, f.ptr, f.ptr, f.ptr, f.ptr, lr, beta, iters, f.ws,
+                           p.workspace_bytes, None)
+    assert st == code
+
+
+def test_step_rejects_null_and_workspace_problems():
+    p = mh.Plan([(8, 8, 1)])
+    f = _FakeDev
+    n = p.workspace_bytes
+    assert mh.lib.muonh_step(None, f.ptr, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 5, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step(p.handle, None, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 5, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step(p.handle, f.ptr, f.ptr, f.ptr, None, 0.02, 0.9, 5, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step(p.handle, f.ptr, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 5, None, n, None) == mh.MUONH_EWORKSPACE
+    assert mh.lib.muonh_step(p.handle, f.ptr, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 5, f.misaligned, n, None) == mh.MUONH_EWORKSPACE
+    assert mh.lib.muonh_step(p.handle, f.ptr, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 5, f.ws, n - 1, None) == mh.MUONH_EWORKSPACE
+    assert "needs" in mh.lib.muonh_last_error().decode()
+
+
+def test_init_and_read_update_validation():
+    p = mh.Plan([(8, 8, 2)])
+    f = _FakeDev
+    n = p.workspace_bytes
+    assert mh.lib.muonh_init(p.handle, None, f.ptr, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_init(p.handle, f.ptr, None, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_init(p.handle, f.ptr, f.ptr, f.ws, 0, None) == mh.MUONH_EWORKSPACE
+    assert mh.lib.muonh_read_update(p.handle, 2, f.ptr, f.ws, n, None) == mh.MUONH_ESHAPE
+    assert mh.lib.muonh_read_update(p.handle, -1, f.ptr, f.ws, n, None) == mh.MUONH_ESHAPE
+    assert mh.lib.muonh_read_update(p.handle, 0, None, f.ws, n, None) == mh.MUONH_EINVAL
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert mh.lib.muonh_status_string(code)
+    assert mh.lib.muonh_status_string(7) == b"unknown status"

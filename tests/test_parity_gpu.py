@@ -1,0 +1,364 @@
+"""GPU parity: the HIP MuonH step (through the C ABI) against the fp64 oracle.
+
+Parity is teacher-forced per step: before each GPU step the pre-step fp32
+(W, M) are copied to the host, the oracle runs the same step from them with
+the same G, and the GPU's results after the step are compared:
+  * update O      : relative Frobenius error <= 2e-2 (bf16 MFMA Newton-Schulz)
+                    and <= 1e-5 (fp32 mode). Where bf16 storage alone already
+                    costs more than 2e-2 (tiny matrices with a few singular
+                    values: the floor of tests/bf16_floor.py), a bf16 result
+                    must instead be within 1.3x of that floor;
+  * momentum M    : relative Frobenius error <= 1e-6 (fp32 fma vs fp64);
+  * weights W     : within 2e-6 (relative Frobenius) of the oracle's projection
+                    of the GPU's own O (this isolates the elementwise phases
+                    from the Newton-Schulz rounding), and within the first-order
+                    bound of the oracle's full step: W = R W'/||W'|| with
+                    W' = W - lr O moves by at most R lr ||dO|| / ||W'|| when O
+                    moves by dO, so ||dW||/R <= 1.5 lr ||dO|| / ||W'|| + 1e-6;
+  * sphere        : | ||W||_F / R - 1 | <= 1e-5 for every matrix.
+The tolerances for O and the sphere are the ones the method's specification
+states; the others follow from fp32 rounding of a fused multiply-add per
+element (M) and of the two-level fp32/fp64 norm (W).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+from bf16_floor import floor as bf16_floor
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TOL_O = {False: 2e-2, True: 1e-5}
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def make_opt(shapes, fp32):
+    import orthogonalized_updates_amd as mh
+    return mh.MuonH(shapes, ns_fp32=fp32)
+
+
+def check_step(opt, W, M, G, W_pre, M_pre, R_gpu, lr, beta, k, fp32, indices, label):
+    """Compare the GPU step just taken with the oracle, for matrices `indices`."""
+    worst = {"O": 0.0, "M": 0.0, "Wproj": 0.0, "Wfull": 0.0, "sphere": 0.0}
+    for i in indices:
+        o_gpu = opt.read_update(i).cpu().numpy()
+        w_gpu = W[i].cpu().numpy()
+        m_gpu = M[i].cpu().numpy()
+        g = G[i].cpu().numpy() if hasattr(G[i], "cpu") else G[i]
+        r = float(R_gpu[i])
+        w_o, m_o, o_o = oracle.muonh_step(W_pre[i], g, M_pre[i], r, lr, beta, k)
+        e_o = rel(o_gpu, o_o)
+        e_m = rel(m_gpu, m_o)
+        e_wp = rel(w_gpu, oracle.hyperball_project(W_pre[i], o_gpu, r, lr))
+        e_wf = rel(w_gpu, w_o)
+        trial = np.linalg.norm(W_pre[i].astype(np.float64) - lr * o_o)
+        bound_wf = 1.5 * lr * np.linalg.norm(o_gpu - o_o) / max(trial, 1e-30) + 1e-6
+        e_s = abs(np.linalg.norm(w_gpu.astype(np.float64)) / r - 1.0) if r > 0 else 0.0
+        for key, v in (("O", e_o), ("M", e_m), ("Wproj", e_wp), ("Wfull", e_wf), ("sphere", e_s)):
+            worst[key] = max(worst[key], v)
+        tol_o = TOL_O[fp32]
+        if not fp32 and e_o > tol_o:
+            fl = bf16_floor(oracle.momentum_update(M_pre[i], g, beta), k, o_o)
+            tol_o = max(tol_o, 1.3 * fl)
+            say(f"{label} mat {i}: O err {e_o:.3e} above 2e-2; bf16 floor {fl:.3e}")
+        assert e_o <= tol_o, f"{label} mat {i}: O rel err {e_o:.3e} > {tol_o:.3e}"
+        assert e_m <= 1e-6, f"{label} mat {i}: M rel err {e_m:.3e}"
+        assert e_wp <= 2e-6, f"{label} mat {i}: W vs projection of GPU O {e_wp:.3e}"
+        assert e_wf <= bound_wf, f"{label} mat {i}: W vs oracle step {e_wf:.3e} > {bound_wf:.3e}"
+        assert e_s <= 1e-5, f"{label} mat {i}: ||W||/R - 1 = {e_s:.3e}"
+    return worst
+
+
+def run_host_workload(shapes, *, steps, k, fp32, lr=0.02, beta=0.95, wid=50, w_std=0.02,
+                      g_std=0.01, heavy_tail=False, check_every=1, indices=None, label=""):
+    """Seeded host inputs, GPU steps, oracle comparison every `check_every` steps."""
+    need_gpu()
+    wl = workloads.Workload(wid=wid, name=label, shapes=tuple(shapes), steps=steps, ns_iters=(k,),
+                            lr=lr, beta=beta, w_std=w_std, g_std=g_std, heavy_tail=heavy_tail)
+    dev = torch.device("cuda")
+    opt = make_opt(shapes, fp32)
+    W = [torch.from_numpy(workloads.host_weight(wl, i)).to(dev) for i in range(len(shapes))]
+    M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+    say(f"[{label}] init {len(shapes)} matrices fp32={fp32} k={k}")
+    R = opt.init(W)
+    torch.cuda.synchronize()
+    R_host = R.cpu().numpy()
+    for i in range(len(shapes)):
+        r_o = oracle.init_radius(W[i].cpu().numpy())
+        assert abs(R_host[i] - r_o) <= 1e-6 * max(r_o, 1e-30), f"R[{i}] {R_host[i]} vs {r_o}"
+    idx = list(range(len(shapes))) if indices is None else indices
+    worst_all = {}
+    for step in range(steps):
+        G_host = [workloads.host_grad(wl, i, step) for i in range(len(shapes))]
+        G = [torch.from_numpy(g).to(dev) for g in G_host]
+        check = (step % check_every == 0) or step == steps - 1
+        if check:
+            W_pre = {i: W[i].cpu().numpy() for i in idx}
+            M_pre = {i: M[i].cpu().numpy() for i in idx}
+        say(f"[{label}] step {step}")
+        opt.step(W, G, M, lr, beta, k)
+        torch.cuda.synchronize()
+        if check:
+            worst = check_step(opt, W, M, G_host, W_pre, M_pre, R_host, lr, beta, k, fp32, idx,
+                               f"{label} step {step}")
+            for key, v in worst.items():
+                worst_all[key] = max(worst_all.get(key, 0.0), v)
+        # the sphere invariant on every matrix, every step
+        for i in range(len(shapes)):
+            if R_host[i] > 0:
+                n = float(torch.linalg.vector_norm(W[i].double()))
+                assert abs(n / R_host[i] - 1.0) <= 1e-5
+    say(f"[{label}] worst errors: " + ", ".join(f"{k_}={v:.2e}" for k_, v in worst_all.items()))
+    return worst_all
+
+
+# ---------------------------------------------------------------------------
+# Small workload (one 128x256 matrix, 10 steps) and ragged multi-group sets
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fp32", [True, False])
+def test_single_128x256(fp32):
+    wl = workloads.WORKLOADS["single_128x256"]
+    run_host_workload(wl.shapes, steps=wl.steps, k=5, fp32=fp32, wid=wl.wid, label="single_128x256")
+
+
+RAGGED = [(1, 1), (3, 5), (5, 3), (1, 64), (64, 1), (300, 200), (257, 129), (130, 700),
+          (300, 200), (511, 513)]
+
+
+@pytest.mark.parametrize("fp32", [True, False])
+@pytest.mark.parametrize("k", [0, 1, 5])
+def test_ragged_groups(fp32, k):
+    run_host_workload(RAGGED, steps=3, k=k, fp32=fp32, wid=51, label=f"ragged k={k}")
+
+
+def test_eight_iterations_bf16():
+    run_host_workload([(384, 640), (640, 384)], steps=2, k=8, fp32=False, wid=52, label="k8")
+
+
+def test_heavy_tailed_grads():
+    run_host_workload([(512, 1536), (1536, 512)] * 3, steps=3, k=5, fp32=False, wid=53,
+                      heavy_tail=True, label="heavy-tail")
+
+
+@pytest.mark.parametrize("fp32", [True, False])
+def test_single_2048(fp32):
+    wl = workloads.WORKLOADS["single_2048"]
+    steps = wl.steps if not fp32 else 3
+    run_host_workload(wl.shapes, steps=steps, k=5, fp32=fp32, wid=wl.wid, check_every=4,
+                      label=f"single_2048 fp32={fp32}")
+
+
+# ---------------------------------------------------------------------------
+# Degenerate cases
+# ---------------------------------------------------------------------------
+
+def _setup(shapes, fp32=False, w=None):
+    need_gpu()
+    dev = torch.device("cuda")
+    opt = make_opt(shapes, fp32)
+    if w is None:
+        W = [torch.from_numpy(workloads.host_custom(s, 0.02, (60, i))).to(dev) for i, s in enumerate(shapes)]
+    else:
+        W = [t.to(dev) for t in w]
+    M = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+    return opt, W, M
+
+
+def test_zero_weights_stay_zero():
+    shapes = [(64, 96)]
+    opt, W, M = _setup(shapes, w=[torch.zeros(64, 96)])
+    R = opt.init(W)
+    G = [torch.from_numpy(workloads.host_custom((64, 96), 0.01, (61, 0))).cuda()]
+    opt.step(W, G, M, 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    assert float(R[0]) == 0.0
+    # R = 0: W' = -lr*O is nonzero, and the projection scales it by R/||W'|| = 0
+    assert torch.count_nonzero(W[0]) == 0
+
+
+def test_zero_gradient_zero_momentum_keeps_w():
+    shapes = [(200, 120), (120, 200)]
+    opt, W, M = _setup(shapes)
+    opt.init(W)
+    W0 = [w.clone() for w in W]
+    G = [torch.zeros(s, device="cuda") for s in shapes]
+    opt.step(W, G, M, 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.count_nonzero(M[i]) == 0
+        assert torch.count_nonzero(opt.read_update(i)) == 0
+        # W is rescaled by R/||W|| = 1 up to float rounding of the norm
+        assert float((W[i] - W0[i]).abs().max()) <= 4e-7 * float(W0[i].abs().max())
+
+
+@pytest.mark.parametrize("fp32", [True, False])
+def test_zero_iterations_is_normalised_momentum(fp32):
+    shapes = [(96, 160), (160, 96)]
+    opt, W, M = _setup(shapes, fp32)
+    opt.init(W)
+    G = [torch.from_numpy(workloads.host_custom(s, 0.01, (62, i))).cuda() for i, s in enumerate(shapes)]
+    opt.step(W, G, M, 0.02, 0.0, 0)
+    torch.cuda.synchronize()
+    for i in range(2):
+        m = M[i].cpu().numpy().astype(np.float64)
+        expected = m / (np.linalg.norm(m) + 1e-7)
+        assert rel(opt.read_update(i).cpu().numpy(), expected) <= (1e-6 if fp32 else 4e-3)
+        np.testing.assert_array_equal(M[i].cpu().numpy(), G[i].cpu().numpy())  # beta = 0
+
+
+def test_zero_lr_keeps_w():
+    shapes = [(128, 128)]
+    opt, W, M = _setup(shapes)
+    opt.init(W)
+    W0 = W[0].clone()
+    G = [torch.from_numpy(workloads.host_custom((128, 128), 0.01, (63, 0))).cuda()]
+    opt.step(W, G, M, 0.0, 0.9, 5)
+    torch.cuda.synchronize()
+    assert float((W[0] - W0).abs().max()) <= 4e-7 * float(W0.abs().max())
+
+
+def test_misaligned_pointers_take_the_scalar_path():
+    need_gpu()
+    shapes = [(33, 47), (47, 33)]
+    dev = torch.device("cuda")
+    bufs = {}
+
+    def view(name, i, s, fill):
+        b = torch.zeros(s[0] * s[1] + 1, dtype=torch.float32, device=dev)
+        v = b[1:].view(s)  # 4-byte offset: not 16-byte aligned
+        v.copy_(fill)
+        bufs[(name, i)] = b
+        return v
+
+    W = [view("W", i, s, torch.from_numpy(workloads.host_custom(s, 0.02, (64, i)))) for i, s in enumerate(shapes)]
+    M = [view("M", i, s, torch.zeros(s)) for i, s in enumerate(shapes)]
+    G_host = [workloads.host_custom(s, 0.01, (65, i)) for i, s in enumerate(shapes)]
+    G = [view("G", i, s, torch.from_numpy(g)) for i, (s, g) in enumerate(zip(shapes, G_host))]
+    assert all(t.data_ptr() % 16 for t in W + M + G)
+    opt = make_opt(shapes, True)
+    R = opt.init(W).cpu().numpy()
+    W_pre = {i: W[i].cpu().numpy() for i in range(2)}
+    M_pre = {i: M[i].cpu().numpy() for i in range(2)}
+    opt.step(W, G, M, 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    check_step(opt, W, M, G_host, W_pre, M_pre, R, 0.02, 0.95, 5, True, [0, 1], "misaligned")
+
+
+# ---------------------------------------------------------------------------
+# Determinism, batch invariance, orientation
+# ---------------------------------------------------------------------------
+
+def test_bitwise_determinism_and_batch_invariance():
+    need_gpu()
+    shapes = [(256, 512), (512, 256), (256, 512), (100, 300)]
+    dev = torch.device("cuda")
+    W_init = [torch.from_numpy(workloads.host_custom(s, 0.02, (66, i))) for i, s in enumerate(shapes)]
+    G_host = [torch.from_numpy(workloads.host_custom(s, 0.01, (67, i))) for i, s in enumerate(shapes)]
+
+    def run(sel):
+        opt = make_opt([shapes[i] for i in sel], False)
+        W = [W_init[i].to(dev) for i in sel]
+        M = [torch.zeros(shapes[i], device=dev) for i in sel]
+        G = [G_host[i].to(dev) for i in sel]
+        opt.init(W)
+        for _ in range(2):
+            opt.step(W, G, M, 0.02, 0.95, 5)
+        torch.cuda.synchronize()
+        return [w.cpu() for w in W], [opt.read_update(j).cpu() for j in range(len(sel))]
+
+    w_a, o_a = run([0, 1, 2, 3])
+    w_b, o_b = run([0, 1, 2, 3])
+    for x, y in zip(w_a + o_a, w_b + o_b):
+        assert torch.equal(x, y)
+    w_c, o_c = run([2])   # matrix 2 alone equals matrix 2 inside the batch
+    assert torch.equal(w_c[0], w_a[2]) and torch.equal(o_c[0], o_a[2])
+
+
+@pytest.mark.parametrize("fp32", [True, False])
+def test_tall_matrix_equals_transposed_wide(fp32):
+    need_gpu()
+    dev = torch.device("cuda")
+    m = workloads.host_custom((192, 448), 0.01, (68, 0))
+    w = workloads.host_custom((192, 448), 0.02, (68, 1))
+    opt = make_opt([(192, 448), (448, 192)], fp32)
+    W = [torch.from_numpy(w).to(dev), torch.from_numpy(np.ascontiguousarray(w.T)).to(dev)]
+    M = [torch.zeros((192, 448), device=dev), torch.zeros((448, 192), device=dev)]
+    G = [torch.from_numpy(m).to(dev), torch.from_numpy(np.ascontiguousarray(m.T)).to(dev)]
+    opt.init(W)
+    opt.step(W, G, M, 0.02, 0.95, 5)
+    torch.cuda.synchronize()
+    o_wide = opt.read_update(0).cpu().numpy()
+    o_tall = opt.read_update(1).cpu().numpy()
+    assert rel(o_tall, o_wide.T) <= (1e-6 if fp32 else 1e-2)
+    assert rel(W[1].cpu().numpy(), W[0].cpu().numpy().T) <= (1e-6 if fp32 else 1e-3)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads in the benchmark's launch configuration, sampled
+# ---------------------------------------------------------------------------
+
+def run_device_workload(name, *, steps, k, sample, label):
+    need_gpu()
+    wl = workloads.WORKLOADS[name]
+    dev = torch.device("cuda")
+    opt = make_opt(wl.shapes, False)
+    say(f"[{label}] generating {wl.n_matrices} matrices ({wl.n_params} params) on the device")
+    W = [workloads.device_weight_(wl, i, torch.empty(s, device=dev)) for i, s in enumerate(wl.shapes)]
+    M = [torch.zeros(s, device=dev) for s in wl.shapes]
+    G = [torch.empty(s, device=dev) for s in wl.shapes]
+    R = opt.init(W)
+    torch.cuda.synchronize()
+    R_host = R.cpu().numpy()
+    for i in sample:
+        r_o = oracle.init_radius(W[i].cpu().numpy())
+        assert abs(R_host[i] - r_o) <= 1e-6 * r_o
+    for step in range(steps):
+        for i, s in enumerate(wl.shapes):
+            workloads.device_grad_(wl, i, step, G[i])
+        W_pre = {i: W[i].cpu().numpy() for i in sample}
+        M_pre = {i: M[i].cpu().numpy() for i in sample}
+        G_host = {i: G[i].cpu().numpy() for i in sample}
+        say(f"[{label}] step {step}")
+        opt.step(W, G, M, wl.lr, wl.beta, k)
+        torch.cuda.synchronize()
+        worst = check_step(opt, W, M, G_host, W_pre, M_pre, R_host, wl.lr, wl.beta, k, False,
+                           sample, f"{label} step {step}")
+        say(f"[{label}] step {step} worst: " + ", ".join(f"{a}={b:.2e}" for a, b in worst.items()))
+        norms = torch.stack([torch.linalg.vector_norm(w.double()) for w in W]).cpu().numpy()
+        assert np.max(np.abs(norms / R_host - 1.0)) <= 1e-5
+
+
+def test_qwen3_2b_full_size_sampled():
+    # layers 0 and 27: q, k, v, o, gate, up, down
+    sample = list(range(0, 7)) + list(range(27 * 7, 28 * 7))
+    run_device_workload("qwen3_2b", steps=2, k=5, sample=sample, label="qwen3_2b")
+
+
+def test_occupancy_full_size_sampled():
+    run_device_workload("occupancy_512x1536", steps=2, k=5, sample=[0, 1, 255, 256, 300, 511],
+                        label="occupancy")
