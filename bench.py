@@ -109,6 +109,23 @@ def cpu_baseline(wl, k, budget_s):
     }
 
 
+def calibrate_copy() -> int:
+    """A plain device copy of known size: each launch reads and writes 1 GiB.
+
+    Run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, its counters give the
+    factor between the counters and true HBM bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": 3}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +136,11 @@ def main() -> int:
     ap.add_argument("--ns-fp32", action="store_true", help="fp32 Newton-Schulz (debug mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -35,32 +35,34 @@ def compile_flags() -> list:
     ]
 
 
-def build(verbose: bool = False, jobs: int = 3) -> Path:
+def build(verbose: bool = False, jobs: int = 3, extra_flags=(), out: Path = LIB,
+          objdir: Path = PKG / "_build") -> Path:
     """Compile every HIP source for gfx950 and link libmuonh.so (always rebuilds)."""
     cc = hipcc()
-    objdir = PKG / "_build"
-    objdir.mkdir(exist_ok=True)
+    objdir = Path(objdir)
+    objdir.mkdir(parents=True, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
         obj = objdir / (Path(src).stem + ".o")
         objs.append(obj)
-        cmd = [cc, *compile_flags(), "-c", str(CSRC / src), "-o", str(obj)]
+        cmd = [cc, *compile_flags(), *extra_flags, "-c", str(CSRC / src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _drain(procs)
     _drain(procs)
-    tmp = LIB.with_suffix(".so.tmp")
+    out = Path(out)
+    tmp = out.with_suffix(".so.tmp")
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
     if verbose:
         print(" ".join(cmd), flush=True)
-    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if out.returncode != 0:
-        raise RuntimeError(f"link failed:\n{out.stdout}")
-    os.replace(tmp, LIB)
-    return LIB
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}")
+    os.replace(tmp, out)
+    return out
 
 
 def _drain(procs: list) -> None:

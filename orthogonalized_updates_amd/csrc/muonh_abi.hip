@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -133,6 +134,14 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final
   return out;
 }
 
+bool xcd_map_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("MUONH_XCD_MAP");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 // GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
 std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters) {
   const int T = gemm_tile(p->fp32);
@@ -202,6 +211,22 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     }
     a.ngroups = (int)(g1 - g0);
     a.ntiles = (int)tiles;
+    a.xcd_map = (!p->fp32 && xcd_map_enabled()) ? 1 : 0;
+    if (a.xcd_map) {
+      // slots per XCD: the longest of the 8 per-XCD lists
+      int64_t longest = 0;
+      for (int x = 0; x < 8; ++x) {
+        int64_t len = 0;
+        for (int gi = 0; gi < a.ngroups; ++gi) {
+          const int64_t tot = (int64_t)a.g[gi].count * a.g[gi].tiles_per_mat;
+          len += ((x + 1) * tot >> 3) - (x * tot >> 3);
+        }
+        longest = std::max(longest, len);
+      }
+      a.grid = (int)(8 * longest);
+    } else {
+      a.grid = a.ntiles;
+    }
     if (mode == kPoly) {
       a.c0 = kNsB;
       a.c1 = kNsC;

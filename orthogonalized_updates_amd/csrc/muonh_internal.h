@@ -98,6 +98,8 @@ struct GemmArgs {
   GemmGroup g[kMaxGemmGroups];
   int ngroups;
   int ntiles;
+  int grid;      // blocks launched (>= ntiles when the XCD mapping pads)
+  int xcd_map;   // 1: deal each group's tiles to the 8 XCDs in contiguous eighths
   float c0, c1;
 };
 

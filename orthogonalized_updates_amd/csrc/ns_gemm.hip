@@ -132,7 +132,7 @@ __device__ __forceinline__ void st_4(T* p, float v0, float v1, float v2, float v
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int MODE>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gemm(GemmArgs args) {
+__global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm(GemmArgs args) {
   constexpr int NTHR = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
@@ -249,19 +249,362 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gemm(GemmArgs args) {
   }
 }
 
-constexpr int kTile = 128;
-constexpr int kWGM = 2, kWGN = 2;
+// ---------------------------------------------------------------------------
+// bf16 pipeline: 256x256 tiles, 8 waves (2 x 4, wave tile 128x64), operands
+// streamed straight from global memory into a 4-stage LDS ring of 32-wide
+// K-slabs (global_load_lds_dwordx4: no staging registers), prefetching three
+// slabs ahead of the MFMAs so that L2-miss latency is covered. Each stage is
+// its own __shared__ object so the compiler can tell the in-flight DMA
+// writes of later stages apart from the reads of the current one.
+// ---------------------------------------------------------------------------
+namespace p3 {
+
+constexpr int kBM = 256, kBN = 256;
+constexpr int kRow = 64;                             // bytes per slab row (32 bf16)
+constexpr int kSlabA = kBM * kRow, kSlabB = kBN * kRow;
+constexpr int kStages = 4;
+
+// Wave grid WGM x WGN over the 256x256 tile; each wave owns MT x NT blocks
+// of 32x32.
+template <int WGM, int WGN>
+struct Cfg {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kWTM = kBM / WGM, kWTN = kBN / WGN;
+  static constexpr int kMT = kWTM / 32, kNT = kWTN / 32;
+  // global_load_lds instructions per wave per stage (1 KB each).
+  static constexpr int kLdsPerWave = (kSlabA + kSlabB) / 1024 / kWaves;
+};
+
+// Chunk (16 B) c of slab row r sits at r*64 + ((c ^ ((r >> 1) & 3)) << 4):
+// the 8 rows one ds_read_b128 phase touches land on 8 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRow + ((chunk ^ ((row >> 1) & 3)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt/lgkmcnt left at max.
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the LDS ring. __syncthreads() would also wait for
+// every outstanding global load (its release fence covers the LDS DMA writes
+// of the stages still in flight); here each wave has already waited for the
+// loads it needs, and its LDS reads of the buffer about to be refilled were
+// consumed by MFMAs before this point (lgkmcnt(0) makes that explicit). The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Issue this wave's share of one stage. Instruction j (0..31) fills 1 KB:
+// rows [16*j, 16*j+16) of A (j < 16) or of B (j >= 16). Lane l fills LDS
+// bytes l*16..l*16+15 of that block: row 16*j + l/4, position l%4, which
+// must hold chunk (l%4) ^ swizzle(row) of that row.
+template <int PER_WAVE>
+__device__ __forceinline__ void issue_stage(const char* P, const char* Q, int64_t ldp_b,
+                                            int64_t ldq_b, int64_t k0_b, char* ldsA, char* ldsB,
+                                            int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int j = wave * PER_WAVE + i;
+    const bool isA = j < kBM / 16;
+    const int jj = isA ? j : j - kBM / 16;
+    const int row = jj * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const char* g = (isA ? P + row * ldp_b : Q + row * ldq_b) + k0_b + (c << 4);
+    char* l = (isA ? ldsA : ldsB) + jj * 1024;
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+  }
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void mma_stage(const char* la, const char* lb, int wm0, int wn0,
+                                          int lane, f32x16 (&acc)[MT][NT]) {
+  const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = ks * 2 + g;
+    bf16x8 av[MT], bv[NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+      av[mi] = *reinterpret_cast<const bf16x8*>(la + swz(wm0 + mi * 32 + r, c));
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni)
+      bv[ni] = *reinterpret_cast<const bf16x8*>(lb + swz(wn0 + ni * 32 + r, c));
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+}  // namespace p3
+
+// Maps a block to (group, local tile). With kXcdMap the 8 XCDs (blocks are
+// dealt to them round-robin by block index) each take a contiguous eighth of
+// every group's tile list, so concurrently resident tiles on one XCD belong to
+// the same few matrices and share operand rows in that XCD's L2.
+__device__ __forceinline__ bool map_tile(const GemmArgs& args, int b, int& gi, int& local) {
+  if (args.xcd_map) {
+    const int xcd = b & 7;
+    int slot = b >> 3;
+    for (int i = 0; i < args.ngroups; ++i) {
+      const int64_t tot = (int64_t)args.g[i].count * args.g[i].tiles_per_mat;
+      const int lo = (int)((xcd * tot) >> 3), hi = (int)(((xcd + 1) * tot) >> 3);
+      if (slot < hi - lo) {
+        gi = i;
+        local = lo + slot;
+        return true;
+      }
+      slot -= hi - lo;
+    }
+    return false;
+  }
+  gi = 0;
+  for (int i = 1; i < args.ngroups; ++i)
+    if (b >= args.g[i].tile_begin) gi = i;
+  local = b - args.g[gi].tile_begin;
+  return true;
+}
+
+// Tile coordinates of local tile t of a matrix. Symmetric modes walk the
+// upper triangle row by row; the apply groups rows in bands of 4 tile rows
+// (4 x 8 = 32 consecutive tiles share 4 B row-blocks and 8 X^T row-blocks).
+template <bool kSym>
+__device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, int& bj) {
+  if (kSym) {
+    int rowlen = g.tm;
+    bi = 0;
+    while (t >= rowlen) {
+      t -= rowlen;
+      ++bi;
+      --rowlen;
+    }
+    bj = bi + t;
+  } else {
+    constexpr int kBand = 4;
+    const int gsz = kBand * g.tn;
+    const int band = t / gsz;
+    const int first = band * kBand;
+    const int gm = g.tm - first < kBand ? g.tm - first : kBand;
+    const int rr = t - band * gsz;
+    bi = first + rr % gm;
+    bj = rr / gm;
+  }
+}
+
+template <int MODE, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf16(GemmArgs args) {
+  using namespace p3;
+  using C = Cfg<WGM, WGN>;
+  constexpr int kWGN = WGN, kWTM = C::kWTM, kWTN = C::kWTN, kMT = C::kMT, kNT = C::kNT;
+  constexpr int kLdsPerWave = C::kLdsPerWave;
+  constexpr bool kSym = (MODE != kApply);
+  __shared__ __attribute__((aligned(1024))) char s0[kSlabA + kSlabB];
+  __shared__ __attribute__((aligned(1024))) char s1[kSlabA + kSlabB];
+  __shared__ __attribute__((aligned(1024))) char s2[kSlabA + kSlabB];
+  __shared__ __attribute__((aligned(1024))) char s3[kSlabA + kSlabB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / kWGN, wn = wave - (wave / kWGN) * kWGN;
+
+  int gi, local;
+  if (!map_tile(args, blockIdx.x, gi, local)) return;
+  const GemmGroup& g = args.g[gi];
+  const int mat = local / g.tiles_per_mat;
+  int bi, bj;
+  tile_coords<kSym>(g, local - mat * g.tiles_per_mat, bi, bj);
+
+  const char* blk = g.base + (int64_t)mat * g.mat_bytes;
+  const int64_t ldp_b = (int64_t)g.ldp * 2, ldq_b = (int64_t)g.ldq * 2;
+  const char* P = blk + g.offP + (int64_t)bi * kBM * ldp_b;
+  const char* Q = blk + g.offQ + (int64_t)bj * kBN * ldq_b;
+
+  f32x16 acc[kMT][kNT];
+#pragma unroll
+  for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNT; ++ni) acc[mi][ni] = f32x16{};
+
+  const int nk = g.K / 32;  // multiple of 8 (K is a multiple of kPad)
+  const int wm0 = wm * kWTM, wn0 = wn * kWTN;
+  issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, 0 * kRow, s0, s0 + kSlabA, wave, lane);
+  issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, 1 * kRow, s1, s1 + kSlabA, wave, lane);
+  issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, 2 * kRow, s2, s2 + kSlabA, wave, lane);
+
+  // Stage kt lives in buffer kt % 4. Before computing it, this wave waits
+  // for its own loads of stage kt (the loads of up to two later stages may
+  // stay in flight), then the barrier publishes every wave's loads and also
+  // guarantees that nobody still reads buffer (kt + 3) % 4, which is refilled.
+#define MUONH_STAGE(BUF, NXT)                                                        \
+  {                                                                                  \
+    const int ahead = nk - 1 - kt;                                                   \
+    if (ahead >= 2) wait_vmcnt<2 * kLdsPerWave>();                                   \
+    else if (ahead == 1) wait_vmcnt<kLdsPerWave>();                                  \
+    else wait_vmcnt<0>();                                                            \
+    ring_barrier();                                                                  \
+    if (kt + 3 < nk)                                                                 \
+      issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, (int64_t)(kt + 3) * kRow, NXT,     \
+                               NXT + kSlabA, wave, lane);                            \
+    mma_stage<kMT, kNT>(BUF, BUF + kSlabA, wm0, wn0, lane, acc);                     \
+    ++kt;                                                                            \
+  }
+  for (int kt = 0; kt < nk;) {
+    MUONH_STAGE(s0, s3)
+    MUONH_STAGE(s1, s0)
+    MUONH_STAGE(s2, s1)
+    MUONH_STAGE(s3, s2)
+  }
+#undef MUONH_STAGE
+
+  // ---- epilogue. Accumulator element q of a 32x32 block sits at row
+  // 8*(q/4) + 4*(lane/32) + q%4, column lane%32: each lane holds 4
+  // consecutive rows of one column. The fp32 term c0*E (apply: E = X;
+  // polynomial: E = A) is read from the transpose of the Q operand (X^T, or
+  // A itself, which is symmetric), where those 4 values are contiguous.
+  // Outputs leave through the now idle LDS ring in two 256x256 bf16 passes
+  // (row-major, then transposed) so that every global store is a coalesced
+  // 16-byte store.
+  const float c0 = args.c0, c1 = args.c1;
+  const __bf16* Et = reinterpret_cast<const __bf16*>(blk + g.offQ);  // Q buffer, absolute rows
+  bf16x4 v4[kMT][kNT][4];
+#pragma unroll
+  for (int mi = 0; mi < kMT; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < kNT; ++ni) {
+      const int col = bj * kBN + wn0 + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int row0 = bi * kBM + wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5);
+        float e[4] = {0.f, 0.f, 0.f, 0.f};
+        if (MODE != kGram) {
+          const bf16x4 ev = *reinterpret_cast<const bf16x4*>(Et + (int64_t)col * g.ldq + row0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = (float)ev[q];
+        }
+        bf16x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a = acc[mi][ni][rg * 4 + q];
+          float v;
+          if (MODE == kGram) v = a;
+          else if (MODE == kPoly) v = fmaf(c1, a, c0 * e[q]);
+          else v = fmaf(c0, e[q], a);
+          o[q] = (__bf16)v;
+        }
+        v4[mi][ni][rg] = o;
+      }
+    }
+  }
+
+  // The 4 ring buffers (32 KB each) hold 64 rows of 512 B of the staging tile.
+  auto ring = [&](int q) -> char* { return q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3; };
+  __bf16* O1 = g.offO1 < 0 ? nullptr : reinterpret_cast<__bf16*>(const_cast<char*>(blk) + g.offO1);
+  __bf16* O2 = g.offO2 < 0 ? nullptr : reinterpret_cast<__bf16*>(const_cast<char*>(blk) + g.offO2);
+  __bf16* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;  // transposed destination
+  const int ldT = kSym ? g.ldo1 : g.ldo2;
+
+  // Pass 1, row-major into O1: LDS tile [row][col], 16-byte chunk c of row r
+  // stored at position c ^ (r & 31).
+  if (O1) {
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNT; ++ni) {
+        const int col = wn0 + ni * 32 + (lane & 31);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5) + q;
+            char* base = ring(row >> 6) + (row & 63) * 512;
+            const int off = ((((col >> 3) ^ (row & 31)) << 4) | ((col & 7) << 1));
+            *reinterpret_cast<__bf16*>(base + off) = v4[mi][ni][rg][q];
+          }
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = tid + i * C::kThreads;  // 0 .. 8191
+      const int row = id >> 5, c = id & 31;
+      const u32x4 d = *reinterpret_cast<const u32x4*>(ring(row >> 6) + (row & 63) * 512 +
+                                                      ((c ^ (row & 31)) << 4));
+      *reinterpret_cast<u32x4*>(O1 + (int64_t)(bi * kBM + row) * g.ldo1 + bj * kBN + c * 8) = d;
+    }
+  }
+  // Pass 2, transposed into OT: LDS tile [col][row], 16-byte chunk c of LDS
+  // row j stored at position c ^ (j & 31).
+  if (OT) {
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNT; ++ni) {
+        const int col = wn0 + ni * 32 + (lane & 31);
+        char* base = ring(col >> 6) + (col & 63) * 512;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int row0 = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5);
+          const int off = ((((row0 >> 3) ^ (col & 31)) << 4) | ((row0 & 7) << 1));
+          *reinterpret_cast<bf16x4*>(base + off) = v4[mi][ni][rg];
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = tid + i * C::kThreads;
+      const int j = id >> 5, c = id & 31;
+      const u32x4 d = *reinterpret_cast<const u32x4*>(ring(j >> 6) + (j & 63) * 512 +
+                                                      ((c ^ (j & 31)) << 4));
+      *reinterpret_cast<u32x4*>(OT + (int64_t)(bj * kBN + j) * ldT + bi * kBM + c * 8) = d;
+    }
+  }
+}
+
+// bf16: 256x256 tiles, 8 waves (2 x 4), wave tile 128x64, 128 KB LDS ring:
+// one workgroup (2 waves per SIMD) per CU. fp32 debug: 128x128, 4 waves.
+template <typename T>
+struct TileCfg;
+template <>
+struct TileCfg<__bf16> {
+  static constexpr int kTile = 256, kWGM = 2, kWGN = 4;
+};
+template <>
+struct TileCfg<float> {
+  static constexpr int kTile = 128, kWGM = 2, kWGN = 2;
+};
 
 template <typename T, int MODE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_ns_gemm<T, kTile, kTile, kWGM, kWGN, MODE>), dim3(a.ntiles),
-                     dim3(kWGM * kWGN * 64), 0, s, a);
+  if constexpr (std::is_same<T, __bf16>::value) {
+#ifndef MUONH_WGM
+#define MUONH_WGM 2
+#define MUONH_WGN 4
+#endif
+    hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, MUONH_WGM, MUONH_WGN>), dim3(a.grid),
+                       dim3(MUONH_WGM * MUONH_WGN * 64), 0, s, a);
+  } else {
+    using C = TileCfg<T>;
+    hipLaunchKernelGGL((k_ns_gemm<T, C::kTile, C::kTile, C::kWGM, C::kWGN, MODE>), dim3(a.ntiles),
+                       dim3(C::kWGM * C::kWGN * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_tile(bool /*fp32*/) { return kTile; }
+int gemm_tile(bool fp32) { return fp32 ? TileCfg<float>::kTile : TileCfg<__bf16>::kTile; }
 
 hipError_t launch_gemm(GemmMode mode, bool fp32, const GemmArgs& a, hipStream_t s) {
   if (a.ntiles <= 0) return hipSuccess;
