@@ -260,9 +260,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm(Gem
 namespace p3 {
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kRow = 64;                             // bytes per slab row (32 bf16)
+constexpr int kRow = 128;                            // bytes per slab row (64 bf16)
 constexpr int kSlabA = kBM * kRow, kSlabB = kBN * kRow;
-constexpr int kStages = 4;
+constexpr int kKS = kRow / 32;                       // 16-wide MFMA k steps per slab
 
 // Wave grid WGM x WGN over the 256x256 tile; each wave owns MT x NT blocks
 // of 32x32.
@@ -276,10 +276,13 @@ struct Cfg {
   static constexpr int kLdsPerWave = (kSlabA + kSlabB) / 1024 / kWaves;
 };
 
-// Chunk (16 B) c of slab row r sits at r*64 + ((c ^ ((r >> 1) & 3)) << 4):
-// the 8 rows one ds_read_b128 phase touches land on 8 distinct bank groups.
+// Chunk (16 B) c of slab row r sits at r*128 + ((c ^ ((r >> 1) & 7)) << 4).
+// A ds_read_b128 is served 16 lanes at a time from 64 four-byte banks; the
+// 16 consecutive rows one pass touches then fall on 16 distinct 16-byte bank
+// groups ((r & 1) picks half of the 256-byte bank window, the swizzled chunk
+// a slot within it).
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRow + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * kRow + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -292,10 +295,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Workgroup barrier for the LDS ring. __syncthreads() would also wait for
 // every outstanding global load (its release fence covers the LDS DMA writes
-// of the stages still in flight); here each wave has already waited for the
-// loads it needs, and its LDS reads of the buffer about to be refilled were
-// consumed by MFMAs before this point (lgkmcnt(0) makes that explicit). The
-// empty asm statements keep the compiler from moving memory accesses across.
+// still in flight); here each wave has already waited for the loads it needs,
+// and lgkmcnt(0) retires its LDS reads of the buffer about to be refilled.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -303,47 +306,85 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Issue this wave's share of one stage. Instruction j (0..31) fills 1 KB:
-// rows [16*j, 16*j+16) of A (j < 16) or of B (j >= 16). Lane l fills LDS
-// bytes l*16..l*16+15 of that block: row 16*j + l/4, position l%4, which
-// must hold chunk (l%4) ^ swizzle(row) of that row.
-template <int PER_WAVE>
-__device__ __forceinline__ void issue_stage(const char* P, const char* Q, int64_t ldp_b,
-                                            int64_t ldq_b, int64_t k0_b, char* ldsA, char* ldsB,
-                                            int wave, int lane) {
+// Phase barrier of the ping-pong schedule: like ring_barrier, plus
+// scheduling barriers so that no instruction (MFMAs included) migrates from
+// one phase into the next.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage is 64 global_load_lds instructions of 1 KB (8 rows x 128 B, full
+// cache lines): waves 0-3 issue rows of A, waves 4-7 rows of B, 8 each.
+// Instruction i of wave w covers rows 8*jj .. 8*jj+7, jj = 8*(w % 4) + i, of
+// its operand; lane l fills LDS bytes l*16..l*16+15 of that 1 KB block: row
+// 8*jj + l/8, position l%8, which must hold chunk (l%8) ^ swizzle(row). The
+// swizzle (row >> 1) & 7 = (4*(jj & 1) + l/16) & 7 depends on jj only
+// through its parity, so a lane needs two 32-bit offsets (voff[jj & 1]); the
+// rest of the address is wave-uniform.
+struct StageSrc {
+  const char* base;  // operand rows of this wave's share, wave-uniform
+  int64_t ld_b;      // operand row pitch in bytes
+  char* lds;         // this wave's 8 KB of the slab, in the buffer at offset 0
+  int voff[2];
+};
+
+__device__ __forceinline__ StageSrc stage_src(const char* P, const char* Q, int64_t ldp_b,
+                                              int64_t ldq_b, int wave, int lane) {
+  StageSrc t;
+  const bool isA = wave < 4;
+  const int jj0 = (wave & 3) * 8;
+  t.ld_b = isA ? ldp_b : ldq_b;
+  t.base = (isA ? P : Q) + (int64_t)(jj0 * 8) * t.ld_b;
+  t.lds = nullptr;
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int j = wave * PER_WAVE + i;
-    const bool isA = j < kBM / 16;
-    const int jj = isA ? j : j - kBM / 16;
-    const int row = jj * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
-    const char* g = (isA ? P + row * ldp_b : Q + row * ldq_b) + k0_b + (c << 4);
-    char* l = (isA ? ldsA : ldsB) + jj * 1024;
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+  for (int par = 0; par < 2; ++par)
+    t.voff[par] = (int)((lane >> 3) * t.ld_b) + (((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) << 4);
+  return t;
+}
+
+// Issue this wave's 8 loads of the stage at K offset k0_b into slab buffer
+// `buf` (A at +0, B at +kSlabA).
+__device__ __forceinline__ void issue_stage(const StageSrc& t, int wave, int64_t k0_b, char* buf) {
+  char* l = buf + (wave < 4 ? 0 : kSlabA) + (wave & 3) * 8 * 1024;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const char* g = t.base + (int64_t)(i * 8) * t.ld_b + k0_b;
+    __builtin_amdgcn_global_load_lds(g + t.voff[i & 1], (lds_ptr)(l + i * 1024), 16, 0, 0);
   }
 }
 
 template <int MT, int NT>
-__device__ __forceinline__ void mma_stage(const char* la, const char* lb, int wm0, int wn0,
-                                          int lane, f32x16 (&acc)[MT][NT]) {
-  const int r = lane & 31, g = lane >> 5;
+struct Frags {
+  bf16x8 a[MT], b[NT];
+};
+
+// Operand fragments of 16-wide k step ks of a slab. Fragment rows are
+// (multiple of 32) + lane%32, so the swizzle depends only on the lane: lane
+// offset loff[ks] = (lane%32)*128 + (((2ks + lane/32) ^ (((lane%32) >> 1) & 7)) << 4)
+// serves every fragment of both operands; the row block is a uniform term.
+template <int MT, int NT>
+__device__ __forceinline__ void load_frags(const char* la, const char* lb, int wm0, int wn0,
+                                           int loff, Frags<MT, NT>& f) {
+  const char* pa = la + wm0 * kRow + loff;
+  const char* pb = lb + wn0 * kRow + loff;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int c = ks * 2 + g;
-    bf16x8 av[MT], bv[NT];
+  for (int mi = 0; mi < MT; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * kRow);
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-      av[mi] = *reinterpret_cast<const bf16x8*>(la + swz(wm0 + mi * 32 + r, c));
+  for (int ni = 0; ni < NT; ++ni) f.b[ni] = *reinterpret_cast<const bf16x8*>(pb + ni * 32 * kRow);
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void mfma_frags(const Frags<MT, NT>& f, f32x16 (&acc)[MT][NT]) {
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni)
-      bv[ni] = *reinterpret_cast<const bf16x8*>(lb + swz(wn0 + ni * 32 + r, c));
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
-  }
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
 }
 
 }  // namespace p3
@@ -401,6 +442,101 @@ __device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, 
   }
 }
 
+// 4x4 transpose of bf16 values within each quad of lanes. Lane k of a quad
+// holds 4 consecutive rows of column k (d0 = rows 0|1, d1 = rows 2|3, low
+// half first); afterwards it holds columns 0..3 of row k. Two rounds of DPP
+// quad permutes: 2x2 transposes of 16-bit halves between lanes k and k^1,
+// then an exchange of dwords between lanes k and k^2.
+__device__ __forceinline__ void quad_transpose(uint32_t& d0, uint32_t& d1, int lane) {
+  const int k = lane & 3;
+  const uint32_t x0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  const uint32_t x1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xB1, 0xF, 0xF, false);
+  if ((k & 1) == 0) {
+    d0 = (d0 & 0xFFFFu) | (x0 << 16);
+    d1 = (d1 & 0xFFFFu) | (x1 << 16);
+  } else {
+    d0 = (x0 >> 16) | (d0 & 0xFFFF0000u);
+    d1 = (x1 >> 16) | (d1 & 0xFFFF0000u);
+  }
+  const uint32_t send = (k & 2) ? d0 : d1;
+  const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  if (k & 2) d0 = recv;
+  else d1 = recv;
+}
+
+// Main loop of one group of the ping-pong schedule (see k_ns_gemm_bf16).
+// Both groups execute the same sequence of barriers; G selects the role.
+// With E_TERM, the fp32 term seed*E (apply: E = X, seed = a; polynomial:
+// E = A, seed = b/c) is added to the accumulators on the way: element
+// (i, j) of E is element (j, i) of the Q operand (X^T, or A itself, which
+// is symmetric), so the E tile streams through the LDS ring as part of Q's
+// slabs with k in [256*bi, 256*bi + 256). When a wave loads a chunk of that
+// K range, it also reads, for the 32 accumulator rows the chunk covers, its
+// 4 consecutive k values per column (one 8-byte LDS read per 4 elements).
+template <int G, int MT, int NT, bool E_TERM>
+__device__ __forceinline__ void pingpong(const p3::StageSrc& src, int wave, int nk, char* s0,
+                                         char* s1, int wm0, int wn0, const int (&loff)[p3::kKS],
+                                         int lane, int bi, float seed, f32x16 (&acc)[MT][NT]) {
+  using namespace p3;
+  Frags<MT, NT> fa, fb;  // the two k steps of one chunk
+  // Chunk ch of stage kt covers k in [64*kt + 32*ch, +32): accumulator rows
+  // (of this tile) r = 64*kt + 32*ch - 256*bi when that lies in [0, 256).
+  auto take_e = [&](const char* buf, int kt, int ch) {
+    const int r = 64 * kt + 32 * ch - 256 * bi - wm0;  // row block in this wave's 128 rows
+    if (r < 0 || r >= MT * 32) return;
+    const char* lb = buf + kSlabA;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      if (r != mi * 32) continue;
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          // k within the slab: 32*ch + 8*rg + 4*(lane/32); Q row: wn0 + ni*32 + lane%32
+          const int kk = 32 * ch + 8 * rg + 4 * (lane >> 5);
+          const int qrow = wn0 + ni * 32 + (lane & 31);
+          const bf16x4 ev =
+              *reinterpret_cast<const bf16x4*>(lb + p3::swz(qrow, kk >> 3) + ((kk & 7) << 1));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[mi][ni][rg * 4 + q] = fmaf(seed, (float)ev[q], acc[mi][ni][rg * 4 + q]);
+        }
+    }
+  };
+  auto load = [&](const char* buf, int ch, int kt) {
+    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[2 * ch], fa);
+    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[2 * ch + 1], fb);
+    if (E_TERM) take_e(buf, kt, ch);
+  };
+  auto mul = [&]() {
+    mfma_frags<MT, NT>(fa, acc);
+    mfma_frags<MT, NT>(fb, acc);
+  };
+  // phase 0: group 0 loads chunk 0 of stage 0
+  if (G == 0) load(s0, 0, 0);
+  phase_barrier();
+  auto stage = [&](int kt, char* buf, char* nxt) {
+    if (G == 0) mul(); else load(buf, 0, kt);                   // 4s+1
+    phase_barrier();
+    if (G == 0) load(buf, 1, kt); else mul();                   // 4s+2
+    phase_barrier();
+    if (G == 0) mul(); else load(buf, 1, kt);                   // 4s+3
+    wait_vmcnt<0>();
+    phase_barrier();
+    if (kt + 2 < nk) issue_stage(src, wave, (int64_t)(kt + 2) * kRow, buf);  // 4s+4
+    if (G == 0) {
+      if (kt + 1 < nk) load(nxt, 0, kt + 1);
+    } else {
+      mul();
+    }
+    phase_barrier();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    stage(kt, s0, s1);
+    stage(kt + 1, s1, s0);
+  }
+}
+
 template <int MODE, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf16(GemmArgs args) {
   using namespace p3;
@@ -410,11 +546,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   constexpr bool kSym = (MODE != kApply);
   __shared__ __attribute__((aligned(1024))) char s0[kSlabA + kSlabB];
   __shared__ __attribute__((aligned(1024))) char s1[kSlabA + kSlabB];
-  __shared__ __attribute__((aligned(1024))) char s2[kSlabA + kSlabB];
-  __shared__ __attribute__((aligned(1024))) char s3[kSlabA + kSlabB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across a wave; readfirstlane lets the compiler
+  // know, so that branches on it are scalar branches.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWGN, wn = wave - (wave / kWGN) * kWGN;
 
   int gi, local;
@@ -435,102 +571,89 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 #pragma unroll
     for (int ni = 0; ni < kNT; ++ni) acc[mi][ni] = f32x16{};
 
-  const int nk = g.K / 32;  // multiple of 8 (K is a multiple of kPad)
+  const int nk = g.K / 64;  // slabs; even, since K is a multiple of kPad
   const int wm0 = wm * kWTM, wn0 = wn * kWTN;
-  issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, 0 * kRow, s0, s0 + kSlabA, wave, lane);
-  issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, 1 * kRow, s1, s1 + kSlabA, wave, lane);
-  issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, 2 * kRow, s2, s2 + kSlabA, wave, lane);
-
-  // Stage kt lives in buffer kt % 4. Before computing it, this wave waits
-  // for its own loads of stage kt (the loads of up to two later stages may
-  // stay in flight), then the barrier publishes every wave's loads and also
-  // guarantees that nobody still reads buffer (kt + 3) % 4, which is refilled.
-#define MUONH_STAGE(BUF, NXT)                                                        \
-  {                                                                                  \
-    const int ahead = nk - 1 - kt;                                                   \
-    if (ahead >= 2) wait_vmcnt<2 * kLdsPerWave>();                                   \
-    else if (ahead == 1) wait_vmcnt<kLdsPerWave>();                                  \
-    else wait_vmcnt<0>();                                                            \
-    ring_barrier();                                                                  \
-    if (kt + 3 < nk)                                                                 \
-      issue_stage<kLdsPerWave>(P, Q, ldp_b, ldq_b, (int64_t)(kt + 3) * kRow, NXT,     \
-                               NXT + kSlabA, wave, lane);                            \
-    mma_stage<kMT, kNT>(BUF, BUF + kSlabA, wm0, wn0, lane, acc);                     \
-    ++kt;                                                                            \
+  // Ping-pong schedule. Stage s (a 64-wide K slab, full 128-byte rows) lives
+  // in buffer s % 2 and is consumed in two chunks of two 16-wide k steps.
+  // Waves 0-3 (group 0) and 4-7 (group 1) -- one of each per SIMD -- take
+  // turns: in every phase one group issues a cluster of 16 MFMAs while the
+  // other loads its next chunk's fragments from LDS, so each SIMD's matrix
+  // core always has a wave feeding it. Phases are separated by barriers.
+  // Phase 0: g0 loads chunk 0 of stage 0. Then per stage s:
+  //   4s+1: g0 multiplies chunk 0, g1 loads chunk 0
+  //   4s+2: g0 loads chunk 1, g1 multiplies chunk 0
+  //   4s+3: g0 multiplies chunk 1, g1 loads chunk 1; every wave then waits
+  //         for its loads of stage s+1, so the next barrier publishes it
+  //   4s+4: loads of stage s+2 into buffer s % 2 (last read in 4s+3);
+  //         g0 loads chunk 0 of stage s+1, g1 multiplies chunk 1.
+  // Stage s+2's loads thus have one stage of time to land.
+  int loff[kKS];
+  {
+    const int r = lane & 31, y = (lane >> 5) ^ ((r >> 1) & 7);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) loff[ks] = r * kRow + (((2 * ks) ^ y) << 4);
   }
-  for (int kt = 0; kt < nk;) {
-    MUONH_STAGE(s0, s3)
-    MUONH_STAGE(s1, s0)
-    MUONH_STAGE(s2, s1)
-    MUONH_STAGE(s3, s2)
-  }
-#undef MUONH_STAGE
+  const StageSrc src = stage_src(P, Q, ldp_b, ldq_b, wave, lane);
+  issue_stage(src, wave, 0, s0);
+  issue_stage(src, wave, kRow, s1);
+  wait_vmcnt<8>();
+  phase_barrier();
+  const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
+  if (wave < 4)
+    pingpong<0, kMT, kNT, MODE != kGram>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi, seed,
+                                         acc);
+  else
+    pingpong<1, kMT, kNT, MODE != kGram>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi, seed,
+                                         acc);
 
-  // ---- epilogue. Accumulator element q of a 32x32 block sits at row
-  // 8*(q/4) + 4*(lane/32) + q%4, column lane%32: each lane holds 4
-  // consecutive rows of one column. The fp32 term c0*E (apply: E = X;
-  // polynomial: E = A) is read from the transpose of the Q operand (X^T, or
-  // A itself, which is symmetric), where those 4 values are contiguous.
-  // Outputs leave through the now idle LDS ring in two 256x256 bf16 passes
-  // (row-major, then transposed) so that every global store is a coalesced
-  // 16-byte store.
-  const float c0 = args.c0, c1 = args.c1;
-  const __bf16* Et = reinterpret_cast<const __bf16*>(blk + g.offQ);  // Q buffer, absolute rows
+  // ---- epilogue. The E term is already in the accumulators (the
+  // polynomial's still needs its factor c). Outputs leave through the idle
+  // LDS ring in two 256x256 bf16 passes (row-major, then transposed) so that
+  // every global store is a coalesced 16-byte store.
+  const float scale = MODE == kPoly ? args.c1 : 1.f;
   bf16x4 v4[kMT][kNT][4];
 #pragma unroll
-  for (int mi = 0; mi < kMT; ++mi) {
+  for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < kNT; ++ni) {
-      const int col = bj * kBN + wn0 + ni * 32 + (lane & 31);
+    for (int ni = 0; ni < kNT; ++ni)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int row0 = bi * kBM + wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5);
-        float e[4] = {0.f, 0.f, 0.f, 0.f};
-        if (MODE != kGram) {
-          const bf16x4 ev = *reinterpret_cast<const bf16x4*>(Et + (int64_t)col * g.ldq + row0);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) e[q] = (float)ev[q];
-        }
         bf16x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a = acc[mi][ni][rg * 4 + q];
-          float v;
-          if (MODE == kGram) v = a;
-          else if (MODE == kPoly) v = fmaf(c1, a, c0 * e[q]);
-          else v = fmaf(c0, e[q], a);
-          o[q] = (__bf16)v;
-        }
+        for (int q = 0; q < 4; ++q) o[q] = (__bf16)(scale * acc[mi][ni][rg * 4 + q]);
         v4[mi][ni][rg] = o;
       }
-    }
-  }
 
-  // The 4 ring buffers (32 KB each) hold 64 rows of 512 B of the staging tile.
-  auto ring = [&](int q) -> char* { return q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3; };
+  // The two 64 KB ring buffers hold 128 rows of 512 B each of the staging
+  // tile; ring(q) is the 32 KB quarter holding rows [64q, 64q + 64).
+  auto ring = [&](int q) -> char* { return (q < 2 ? s0 : s1) + (q & 1) * 32768; };
   __bf16* O1 = g.offO1 < 0 ? nullptr : reinterpret_cast<__bf16*>(const_cast<char*>(blk) + g.offO1);
   __bf16* O2 = g.offO2 < 0 ? nullptr : reinterpret_cast<__bf16*>(const_cast<char*>(blk) + g.offO2);
   __bf16* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;  // transposed destination
   const int ldT = kSym ? g.ldo1 : g.ldo2;
 
   // Pass 1, row-major into O1: LDS tile [row][col], 16-byte chunk c of row r
-  // stored at position c ^ (r & 31).
+  // stored at position c ^ (r & 31). A quad transpose first gives each lane
+  // 4 consecutive columns of one row, so the LDS writes are 8-byte writes.
   if (O1) {
     __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
       for (int ni = 0; ni < kNT; ++ni) {
-        const int col = wn0 + ni * 32 + (lane & 31);
+        const int col = wn0 + ni * 32 + (lane & 28);  // first of the quad's 4 columns
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5) + q;
-            char* base = ring(row >> 6) + (row & 63) * 512;
-            const int off = ((((col >> 3) ^ (row & 31)) << 4) | ((col & 7) << 1));
-            *reinterpret_cast<__bf16*>(base + off) = v4[mi][ni][rg][q];
-          }
+          const int row = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5) + (lane & 3);
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          u32x2 d = __builtin_bit_cast(u32x2, v4[mi][ni][rg]);
+          uint32_t d0 = d.x, d1 = d.y;
+          quad_transpose(d0, d1, lane);
+          d.x = d0;
+          d.y = d1;
+          char* base = ring(row >> 6) + (row & 63) * 512;
+          const int off = ((((col >> 3) ^ (row & 31)) << 4) | ((col & 7) << 1));
+          *reinterpret_cast<u32x2*>(base + off) = d;
         }
       }
     __syncthreads();
