@@ -109,6 +109,27 @@ def cpu_baseline(wl, k, budget_s):
     }
 
 
+def committed_traffic(kernel_name: str, workload: str):
+    """HBM bytes per launch of `kernel_name` from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by its factor on a
+    plain copy of known size), or None when no summary exists for this
+    workload or the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"muonh_step_{workload}_hbm_counters.md")
+    src = os.path.join(ROOT, "orthogonalized_updates_amd", "csrc", "ns_gemm.hip")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        for line in open(path):
+            line = line.strip()
+            if line.startswith("{") and '"traffic_bytes_per_launch"' in line:
+                rec = json.loads(line)
+                if rec.get("kernel") == kernel_name and rec.get("ns_gemm_sha256_16") == sha:
+                    return int(rec["traffic_bytes_per_launch"])
+    except (OSError, ValueError):
+        return None
+    return None
+
+
 def calibrate_copy() -> int:
     """A plain device copy of known size: each launch reads and writes 1 GiB.
 
@@ -222,12 +243,14 @@ def main() -> int:
     pre_ms, post_ms = pre / nst, post / nst
     dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
 
-    kernel_names = {"gram": "k_ns_gemm<Gram>", "poly": "k_ns_gemm<Poly>", "apply": "k_ns_gemm<Apply>"}
+    kernel_names = {"gram": "k_ns_gemm_bf16<Gram>", "poly": "k_ns_gemm_bf16<Poly>",
+                    "apply": "k_ns_gemm_bf16<Apply>"}
     if dom is not None:
         avg_ms = phase[dom] / launches
         achieved = flops[dom] / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
+                    "traffic": None if args.ns_fp32 else committed_traffic(kernel_names[dom], wl.name),
                     "kernel": kernel_names[dom], "avg_launch_ms": round(avg_ms, 4),
                     "algorithmic_flop_per_launch": flops[dom]}
     else:

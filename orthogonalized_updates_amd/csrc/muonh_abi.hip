@@ -16,7 +16,6 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -134,14 +133,6 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final
   return out;
 }
 
-bool xcd_map_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("MUONH_XCD_MAP");
-    return !(e && e[0] == '0');
-  }();
-  return on;
-}
-
 // GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
 std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters) {
   const int T = gemm_tile(p->fp32);
@@ -211,7 +202,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     }
     a.ngroups = (int)(g1 - g0);
     a.ntiles = (int)tiles;
-    a.xcd_map = (!p->fp32 && xcd_map_enabled()) ? 1 : 0;
+    a.xcd_map = p->fp32 ? 0 : 1;
     if (a.xcd_map) {
       // slots per XCD: the longest of the 8 per-XCD lists
       int64_t longest = 0;

@@ -11,11 +11,16 @@
 // as K-contiguous rows. The apply step writes the new X in both layouts (X and
 // X^T) so that the next Gram and the next apply again read K-contiguous rows.
 //
-// Kernel shape: one workgroup per output tile (grouped across all matrices of
-// all shape groups in one launch), 4 waves in a 2x2 grid, 32x32 MFMA blocks,
-// operands staged through a double-buffered LDS ring of 128-byte K-slab rows
-// with an XOR swizzle of the 16-byte chunks, fp32 accumulation, fused
-// epilogues. bf16: v_mfma_f32_32x32x16_bf16; fp32 debug: v_mfma_f32_32x32x2f32.
+// Every launch covers one phase for all matrices of all shape groups: one
+// workgroup per output tile, tiles dealt to the 8 XCDs in contiguous runs.
+// bf16 (the product path): 256x256 tiles, 8 waves in two groups that take
+// turns between MFMA clusters (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
+// and LDS fragment loads, operands streamed into a 2-stage LDS ring of
+// 64-wide K slabs by LDS DMA (global_load_lds_dwordx4), the fp32 a*X or b*A
+// term folded into the accumulators from the operand stream, and epilogues
+// staged through LDS for coalesced stores of both output layouts.
+// fp32 debug: a simpler 128x128 kernel on v_mfma_f32_32x32x2f32 with
+// register-staged double buffering and direct epilogue stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -251,13 +256,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm(Gem
 
 // ---------------------------------------------------------------------------
 // bf16 pipeline: 256x256 tiles, 8 waves (2 x 4, wave tile 128x64), operands
-// streamed straight from global memory into a 4-stage LDS ring of 32-wide
-// K-slabs (global_load_lds_dwordx4: no staging registers), prefetching three
-// slabs ahead of the MFMAs so that L2-miss latency is covered. Each stage is
-// its own __shared__ object so the compiler can tell the in-flight DMA
-// writes of later stages apart from the reads of the current one.
+// streamed straight from global memory into a 2-stage LDS ring of 64-wide K
+// slabs (full 128-byte rows; global_load_lds_dwordx4, no staging
+// registers). Each stage buffer is its own __shared__ object so that the
+// compiler can tell the in-flight DMA writes of one buffer apart from the
+// reads of the other.
 // ---------------------------------------------------------------------------
-namespace p3 {
+namespace bf {
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kRow = 128;                            // bytes per slab row (64 bf16)
@@ -272,8 +277,7 @@ struct Cfg {
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kWTM = kBM / WGM, kWTN = kBN / WGN;
   static constexpr int kMT = kWTM / 32, kNT = kWTN / 32;
-  // global_load_lds instructions per wave per stage (1 KB each).
-  static constexpr int kLdsPerWave = (kSlabA + kSlabB) / 1024 / kWaves;
+  static_assert(kWaves == 8, "the ping-pong schedule and the DMA split assume 8 waves");
 };
 
 // Chunk (16 B) c of slab row r sits at r*128 + ((c ^ ((r >> 1) & 7)) << 4).
@@ -293,22 +297,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Workgroup barrier for the LDS ring. __syncthreads() would also wait for
-// every outstanding global load (its release fence covers the LDS DMA writes
-// still in flight); here each wave has already waited for the loads it needs,
-// and lgkmcnt(0) retires its LDS reads of the buffer about to be refilled.
-// The empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Phase barrier of the ping-pong schedule: like ring_barrier, plus
-// scheduling barriers so that no instruction (MFMAs included) migrates from
-// one phase into the next.
+// Phase barrier of the ping-pong schedule. __syncthreads() would also wait
+// for every outstanding global load (its release fence covers the LDS DMA
+// writes still in flight); here each wave has already waited for the loads
+// it needs, and lgkmcnt(0) retires its LDS reads (so a buffer may be
+// refilled after the barrier). The empty asm statements keep the compiler
+// from moving memory accesses across, and the scheduling barriers keep any
+// instruction (MFMAs included) from migrating from one phase to the next.
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
@@ -329,8 +324,7 @@ __device__ __forceinline__ void phase_barrier() {
 struct StageSrc {
   const char* base;  // operand rows of this wave's share, wave-uniform
   int64_t ld_b;      // operand row pitch in bytes
-  char* lds;         // this wave's 8 KB of the slab, in the buffer at offset 0
-  int voff[2];
+  int voff[2];       // per-lane offsets for even and odd instructions
 };
 
 __device__ __forceinline__ StageSrc stage_src(const char* P, const char* Q, int64_t ldp_b,
@@ -340,7 +334,6 @@ __device__ __forceinline__ StageSrc stage_src(const char* P, const char* Q, int6
   const int jj0 = (wave & 3) * 8;
   t.ld_b = isA ? ldp_b : ldq_b;
   t.base = (isA ? P : Q) + (int64_t)(jj0 * 8) * t.ld_b;
-  t.lds = nullptr;
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     t.voff[par] = (int)((lane >> 3) * t.ld_b) + (((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) << 4);
@@ -387,12 +380,13 @@ __device__ __forceinline__ void mfma_frags(const Frags<MT, NT>& f, f32x16 (&acc)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
 }
 
-}  // namespace p3
+}  // namespace bf
 
-// Maps a block to (group, local tile). With kXcdMap the 8 XCDs (blocks are
+// Maps a block to (group, local tile). With xcd_map the 8 XCDs (blocks are
 // dealt to them round-robin by block index) each take a contiguous eighth of
 // every group's tile list, so concurrently resident tiles on one XCD belong to
-// the same few matrices and share operand rows in that XCD's L2.
+// the same few matrices and share operand rows in that XCD's L2 (this halves
+// the L2-miss traffic of the apply on the 2B-shaped set).
 __device__ __forceinline__ bool map_tile(const GemmArgs& args, int b, int& gi, int& local) {
   if (args.xcd_map) {
     const int xcd = b & 7;
@@ -474,10 +468,10 @@ __device__ __forceinline__ void quad_transpose(uint32_t& d0, uint32_t& d1, int l
 // K range, it also reads, for the 32 accumulator rows the chunk covers, its
 // 4 consecutive k values per column (one 8-byte LDS read per 4 elements).
 template <int G, int MT, int NT, bool E_TERM>
-__device__ __forceinline__ void pingpong(const p3::StageSrc& src, int wave, int nk, char* s0,
-                                         char* s1, int wm0, int wn0, const int (&loff)[p3::kKS],
+__device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int nk, char* s0,
+                                         char* s1, int wm0, int wn0, const int (&loff)[bf::kKS],
                                          int lane, int bi, float seed, f32x16 (&acc)[MT][NT]) {
-  using namespace p3;
+  using namespace bf;
   Frags<MT, NT> fa, fb;  // the two k steps of one chunk
   // Chunk ch of stage kt covers k in [64*kt + 32*ch, +32): accumulator rows
   // (of this tile) r = 64*kt + 32*ch - 256*bi when that lies in [0, 256).
@@ -496,7 +490,7 @@ __device__ __forceinline__ void pingpong(const p3::StageSrc& src, int wave, int 
           const int kk = 32 * ch + 8 * rg + 4 * (lane >> 5);
           const int qrow = wn0 + ni * 32 + (lane & 31);
           const bf16x4 ev =
-              *reinterpret_cast<const bf16x4*>(lb + p3::swz(qrow, kk >> 3) + ((kk & 7) << 1));
+              *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, kk >> 3) + ((kk & 7) << 1));
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             acc[mi][ni][rg * 4 + q] = fmaf(seed, (float)ev[q], acc[mi][ni][rg * 4 + q]);
@@ -539,10 +533,9 @@ __device__ __forceinline__ void pingpong(const p3::StageSrc& src, int wave, int 
 
 template <int MODE, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf16(GemmArgs args) {
-  using namespace p3;
+  using namespace bf;
   using C = Cfg<WGM, WGN>;
   constexpr int kWGN = WGN, kWTM = C::kWTM, kWTN = C::kWTN, kMT = C::kMT, kNT = C::kNT;
-  constexpr int kLdsPerWave = C::kLdsPerWave;
   constexpr bool kSym = (MODE != kApply);
   __shared__ __attribute__((aligned(1024))) char s0[kSlabA + kSlabB];
   __shared__ __attribute__((aligned(1024))) char s1[kSlabA + kSlabB];
@@ -695,39 +688,24 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   }
 }
 
-// bf16: 256x256 tiles, 8 waves (2 x 4), wave tile 128x64, 128 KB LDS ring:
-// one workgroup (2 waves per SIMD) per CU. fp32 debug: 128x128, 4 waves.
-template <typename T>
-struct TileCfg;
-template <>
-struct TileCfg<__bf16> {
-  static constexpr int kTile = 256, kWGM = 2, kWGN = 4;
-};
-template <>
-struct TileCfg<float> {
-  static constexpr int kTile = 128, kWGM = 2, kWGN = 2;
-};
+// fp32 debug path: the generic 128x128 kernel with 4 waves (2 x 2).
+constexpr int kTile32 = 128;
 
 template <typename T, int MODE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   if constexpr (std::is_same<T, __bf16>::value) {
-#ifndef MUONH_WGM
-#define MUONH_WGM 2
-#define MUONH_WGN 4
-#endif
-    hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, MUONH_WGM, MUONH_WGN>), dim3(a.grid),
-                       dim3(MUONH_WGM * MUONH_WGN * 64), 0, s, a);
+    // bf16: 256x256 tiles, 8 waves in a 2 x 4 grid (wave tile 128 x 64).
+    hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4>), dim3(a.grid), dim3(512), 0, s, a);
   } else {
-    using C = TileCfg<T>;
-    hipLaunchKernelGGL((k_ns_gemm<T, C::kTile, C::kTile, C::kWGM, C::kWGN, MODE>), dim3(a.ntiles),
-                       dim3(C::kWGM * C::kWGN * 64), 0, s, a);
+    hipLaunchKernelGGL((k_ns_gemm<T, kTile32, kTile32, 2, 2, MODE>), dim3(a.ntiles), dim3(256), 0,
+                       s, a);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_tile(bool fp32) { return fp32 ? TileCfg<float>::kTile : TileCfg<__bf16>::kTile; }
+int gemm_tile(bool fp32) { return fp32 ? kTile32 : bf::kBM; }
 
 hipError_t launch_gemm(GemmMode mode, bool fp32, const GemmArgs& a, hipStream_t s) {
   if (a.ntiles <= 0) return hipSuccess;
