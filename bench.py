@@ -154,12 +154,17 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3_2b", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--ns-iters", type=int, default=None)
-    ap.add_argument("--ns-fp32", action="store_true", help="fp32 Newton-Schulz (debug mode)")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "split_bf16", "fp32"],
+                    help="Newton-Schulz operands: bf16 (default), split_bf16 (hi + lo bf16 "
+                         "pairs, 3 MFMAs per product) or fp32 (debug mode)")
+    ap.add_argument("--ns-fp32", action="store_true", help="same as --precision fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.ns_fp32:
+        args.precision = "fp32"
     if args.calibrate_copy:
         return calibrate_copy()
 
@@ -183,7 +188,7 @@ def main() -> int:
     k = args.ns_iters if args.ns_iters is not None else wl.ns_iters[0]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    opt = mh.MuonH(wl.shapes, ns_fp32=args.ns_fp32, device=dev)
+    opt = mh.MuonH(wl.shapes, precision=args.precision, device=dev)
 
     print(f"[bench] {wl.name}: {wl.n_matrices} matrices, {wl.n_params} params, k={k}, "
           f"workspace {opt.plan.workspace_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
@@ -237,8 +242,9 @@ def main() -> int:
     flops = ns_flops(wl.shapes, k)
     ns_ms = sum(phase.values()) / nst
     ns_tflops = (sum(flops.values()) * k) / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
-    peak_mfma = PEAK_FP32_MFMA_TFLOPS if args.ns_fp32 else PEAK_BF16_TFLOPS
-    ns_bytes = 4 if args.ns_fp32 else 2
+    fp32 = args.precision == "fp32"
+    peak_mfma = PEAK_FP32_MFMA_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    ns_bytes = 2 if args.precision == "bf16" else 4
     pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes)
     pre_ms, post_ms = pre / nst, post / nst
     dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
@@ -250,7 +256,8 @@ def main() -> int:
         achieved = flops[dom] / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
                     "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
-                    "traffic": None if args.ns_fp32 else committed_traffic(kernel_names[dom], wl.name),
+                    "traffic": (committed_traffic(kernel_names[dom], wl.name)
+                                if args.precision == "bf16" else None),
                     "kernel": kernel_names[dom], "avg_launch_ms": round(avg_ms, 4),
                     "algorithmic_flop_per_launch": flops[dom]}
     else:
@@ -269,11 +276,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if args.ns_fp32 else "bf16",
+        "dtype": "f32" if fp32 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.notes}", "matrices": wl.n_matrices,
                    "params": wl.n_params, "ns_iters": k, "lr": wl.lr, "beta": wl.beta,
-                   "master_weights": "fp32", "ns_operands": "fp32" if args.ns_fp32 else "bf16"},
+                   "master_weights": "fp32", "ns_operands": args.precision},
         "roofline": roofline,
         "phases": {
             "ns_ms": round(ns_ms, 4),

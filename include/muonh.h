@@ -35,7 +35,8 @@
  *     Pointers that are 16-byte aligned take the vector path; others work
  *     through a scalar path. W, G and M must not overlap.
  *   - The workspace is a DEVICE buffer of at least muonh_workspace_bytes(plan)
- *     bytes, 256-byte aligned, owned by the caller. It holds the bf16 (or fp32)
+ *     bytes, 256-byte aligned, owned by the caller. It holds the bf16 (split
+ *     bf16, fp32)
  *     Newton-Schulz operands and the norm partials. Its contents after a step
  *     hold that step's update O until the next call that uses it.
  *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
@@ -76,11 +77,19 @@ enum {
   MUONH_ENOMEM = -5      /* host allocation failed */
 };
 
-/* Plan flags. */
+/* Plan flags (at most one). Default: Newton-Schulz operands in bf16, bf16
+ * MFMA with fp32 accumulation; about 1e-2 relative error of O at 5
+ * iterations, about 2e-2 at 8. */
 enum {
-  /* Run Newton-Schulz in fp32 (fp32 MFMA) instead of bf16 MFMA with fp32
-   * accumulation. Debug/reference mode: about 16x slower, ~1e-6 accurate. */
-  MUONH_NS_FP32 = 1u
+  /* fp32 operands and fp32 MFMA. Debug/reference mode: about 1e-6 relative
+   * error, an order of magnitude slower. */
+  MUONH_NS_FP32 = 1u,
+  /* Split-bf16 operands: every stored value v is kept as hi = bf16(v) plus
+   * lo = bf16(v - hi), and each product takes hi*hi + hi*lo + lo*hi on bf16
+   * MFMA (fp32 accumulation). About 1e-4 relative error of O at 8
+   * iterations, for about 3x the Newton-Schulz time and twice its
+   * workspace. */
+  MUONH_NS_SPLIT_BF16 = 2u
 };
 
 /* Limits. */
@@ -94,9 +103,10 @@ int32_t muonh_abi_version(void);
 
 /*
  * Create a plan for `n_groups` shape groups. Host-only: no HIP call.
- * flags: 0 or MUONH_NS_FP32. On success *out owns a plan that must be
- * released with muonh_plan_destroy. Errors: MUONH_EINVAL (null out/groups,
- * n_groups out of [1, MUONH_MAX_GROUPS], unknown flag), MUONH_ESHAPE (a dim out
+ * flags: 0, MUONH_NS_FP32 or MUONH_NS_SPLIT_BF16. On success *out owns a plan
+ * that must be released with muonh_plan_destroy. Errors: MUONH_EINVAL (null
+ * out/groups, n_groups out of [1, MUONH_MAX_GROUPS], unknown or conflicting
+ * flags), MUONH_ESHAPE (a dim out
  * of [1, MUONH_MAX_DIM], count < 1, too many matrices), MUONH_ENOMEM.
  */
 int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t n_groups,

@@ -29,6 +29,10 @@ MUONH_EWORKSPACE = -3
 MUONH_EHIP = -4
 MUONH_ENOMEM = -5
 MUONH_NS_FP32 = 1
+MUONH_NS_SPLIT_BF16 = 2
+
+# Newton-Schulz operand precision -> plan flag
+PRECISIONS = {"bf16": 0, "split_bf16": MUONH_NS_SPLIT_BF16, "fp32": MUONH_NS_FP32}
 
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
 
@@ -98,17 +102,35 @@ def check(status: int) -> None:
                          or lib.muonh_status_string(status).decode())
 
 
-class Plan:
-    """Owns a muonh_plan for shape groups [(rows, cols, count), ...]."""
+def _precision(precision: str, ns_fp32: bool) -> str:
+    if ns_fp32:
+        if precision not in ("bf16", "fp32"):
+            raise ValueError("ns_fp32=True conflicts with precision=%r" % (precision,))
+        precision = "fp32"
+    if precision not in PRECISIONS:
+        raise ValueError("precision must be one of %s, got %r" % (sorted(PRECISIONS), precision))
+    return precision
 
-    def __init__(self, groups: Sequence[Tuple[int, int, int]], ns_fp32: bool = False):
+
+class Plan:
+    """Owns a muonh_plan for shape groups [(rows, cols, count), ...].
+
+    precision: Newton-Schulz operand precision, "bf16" (default),
+    "split_bf16" (hi + lo bf16 pairs, three bf16 products each) or "fp32";
+    ns_fp32=True is the same as precision="fp32".
+    """
+
+    def __init__(self, groups: Sequence[Tuple[int, int, int]], ns_fp32: bool = False,
+                 precision: str = "bf16"):
+        precision = _precision(precision, ns_fp32)
         arr = (GroupDesc * len(groups))(*[GroupDesc(int(r), int(c), int(n)) for r, c, n in groups])
         handle = ctypes.c_void_p()
         check(get_lib().muonh_plan_create(ctypes.byref(handle), arr, len(groups),
-                                    MUONH_NS_FP32 if ns_fp32 else 0))
+                                          PRECISIONS[precision]))
         self.handle = handle
         self.groups = [tuple(int(v) for v in g) for g in groups]
-        self.ns_fp32 = bool(ns_fp32)
+        self.precision = precision
+        self.ns_fp32 = precision == "fp32"
 
     @property
     def num_matrices(self) -> int:
@@ -137,7 +159,8 @@ class MuonH:
     caller's order.
     """
 
-    def __init__(self, shapes: Sequence[Tuple[int, int]], *, ns_fp32: bool = False, device=None):
+    def __init__(self, shapes: Sequence[Tuple[int, int]], *, ns_fp32: bool = False,
+                 precision: str = "bf16", device=None):
         import torch
         get_lib()
         self.torch = torch
@@ -155,7 +178,8 @@ class MuonH:
             buckets.setdefault(s, []).append(i)
         self.plan_order: List[int] = [i for idx in buckets.values() for i in idx]
         self.plan_index = {caller: p for p, caller in enumerate(self.plan_order)}
-        self.plan = Plan([(r, c, len(idx)) for (r, c), idx in buckets.items()], ns_fp32=ns_fp32)
+        self.plan = Plan([(r, c, len(idx)) for (r, c), idx in buckets.items()], ns_fp32=ns_fp32,
+                         precision=precision)
         nbytes = max(self.plan.workspace_bytes, 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         if self.workspace.data_ptr() % 256:

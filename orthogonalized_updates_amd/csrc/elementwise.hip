@@ -148,20 +148,69 @@ __global__ __launch_bounds__(kThreads) void k_finalize(EwArgs a, const double* p
 }
 
 // --------------------------------------------------------------------------
+// Newton-Schulz operand storage formats (see NsPrec): element `col` of a row
+// that starts at byte `row`.
+// --------------------------------------------------------------------------
+template <int F>
+struct Fmt;
+template <>
+struct Fmt<kBf16> {
+  __device__ static void store(char* row, int col, float v) {
+    reinterpret_cast<__bf16*>(row)[col] = (__bf16)v;
+  }
+  __device__ static float load(const char* row, int col) {
+    return (float)reinterpret_cast<const __bf16*>(row)[col];
+  }
+  // 4 consecutive elements, col a multiple of 4.
+  __device__ static float4 load4(const char* row, int col) {
+    const uint2 u = *reinterpret_cast<const uint2*>(row + col * 2);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+template <>
+struct Fmt<kSplitBf16> {
+  // 128-byte blocks of 32 hi then 32 lo values
+  __device__ static int64_t off(int col) { return (int64_t)(col >> 5) * 128 + ((col & 31) << 1); }
+  __device__ static void store(char* row, int col, float v) {
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    __bf16* p = reinterpret_cast<__bf16*>(row + off(col));
+    p[0] = h;
+    p[32] = l;
+  }
+  __device__ static float load(const char* row, int col) {
+    const __bf16* p = reinterpret_cast<const __bf16*>(row + off(col));
+    return (float)p[0] + (float)p[32];
+  }
+  __device__ static float4 load4(const char* row, int col) {
+    const float4 h = Fmt<kBf16>::load4(row + off(col), 0);
+    const float4 l = Fmt<kBf16>::load4(row + off(col) + 64, 0);
+    return make_float4(h.x + l.x, h.y + l.y, h.z + l.z, h.w + l.w);
+  }
+};
+template <>
+struct Fmt<kFp32> {
+  __device__ static void store(char* row, int col, float v) {
+    reinterpret_cast<float*>(row)[col] = v;
+  }
+  __device__ static float load(const char* row, int col) {
+    return reinterpret_cast<const float*>(row)[col];
+  }
+  __device__ static float4 load4(const char* row, int col) {
+    return *reinterpret_cast<const float4*>(row + col * 4);
+  }
+};
+
+// --------------------------------------------------------------------------
 // X0 = M / (||M|| + eps): one 64x64 tile of the padded rp x cp domain per
 // block; written straight to D and transposed (through LDS) to E. Entries
 // outside rows x cols are written as zero.
 // --------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ T to_ns(float v);
-template <>
-__device__ __forceinline__ float to_ns<float>(float v) { return v; }
-template <>
-__device__ __forceinline__ __bf16 to_ns<__bf16>(float v) { return (__bf16)v; }
-
-template <typename T>
+template <int F>
 __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* const* M,
                                                        const double* norms) {
+  constexpr int kEB = ns_elem_bytes((NsPrec)F);
   __shared__ float tile[64][65];
   const int gi = group_of_block(a, blockIdx.x);
   const EwGroup& g = a.g[gi];
@@ -173,8 +222,8 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
   const float scale = (float)(1.0 / (norms[mat] + kNsEps));
   const float* mp = M[mat];
   char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
-  T* D = reinterpret_cast<T*>(blk + g.offD);
-  T* E = reinterpret_cast<T*>(blk + g.offE);
+  char* D = blk + g.offD;
+  char* E = blk + g.offE;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {
@@ -183,13 +232,13 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
     float v = 0.f;
     if (r < g.rows && c < g.cols) v = mp[(int64_t)r * g.cols + c] * scale;
     tile[rr][tx] = v;
-    D[(int64_t)r * g.cp + c] = to_ns<T>(v);
+    Fmt<F>::store(D + (int64_t)r * g.cp * kEB, c, v);
   }
   __syncthreads();
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {
     const int cc = i * 4 + ty;
-    E[(int64_t)(c0 + cc) * g.rp + r0 + tx] = to_ns<T>(tile[tx][cc]);
+    Fmt<F>::store(E + (int64_t)(c0 + cc) * g.rp * kEB, r0 + tx, tile[tx][cc]);
   }
 }
 
@@ -197,31 +246,11 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
 // Trial update W' = W - lr*O (O read from D) and partial sums of squares of
 // W'; the projection recomputes W' identically and rescales it.
 // --------------------------------------------------------------------------
-template <typename T>
-struct Vec4;
-template <>
-struct Vec4<float> {
-  __device__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
-};
-template <>
-struct Vec4<__bf16> {
-  __device__ static float4 load(const __bf16* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    float4 r;
-    r.x = __uint_as_float(u.x << 16);
-    r.y = __uint_as_float(u.x & 0xffff0000u);
-    r.z = __uint_as_float(u.y << 16);
-    r.w = __uint_as_float(u.y & 0xffff0000u);
-    return r;
-  }
-};
-__device__ __forceinline__ float ns_to_f(float v) { return v; }
-__device__ __forceinline__ float ns_to_f(__bf16 v) { return (float)v; }
-
-template <typename T, bool kProject>
+template <int F, bool kProject>
 __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, float lr,
                                                      double* partials, const float* R,
                                                      const double* norms) {
+  constexpr int kEB = ns_elem_bytes((NsPrec)F);
   __shared__ double red[4];
   const int gi = group_of_block(a, blockIdx.x);
   const EwGroup& g = a.g[gi];
@@ -229,7 +258,8 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
   const int m = local / g.bpm, c = local - m * g.bpm;
   const int mat = g.first + m;
   float* w = W[mat];
-  const T* D = reinterpret_cast<const T*>(g.ns_base + (int64_t)m * g.mat_bytes + g.offD);
+  const char* D = g.ns_base + (int64_t)m * g.mat_bytes + g.offD;
+  const int64_t ldb = (int64_t)g.cp * kEB;
   int64_t lo, hi;
   chunk_range(g.n, g.bpm, c, lo, hi);
   const float nlr = -lr;
@@ -249,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     const int dr = step / cols, dc = step - (step / cols) * cols;
     for (int64_t e = e0; e < hi; e += step) {
       float4 wv = *reinterpret_cast<const float4*>(w + e);
-      const float4 ov = Vec4<T>::load(D + r * g.cp + col);
+      const float4 ov = Fmt<F>::load4(D + r * ldb, col);
       wv.x = fmaf(nlr, ov.x, wv.x);
       wv.y = fmaf(nlr, ov.y, wv.y);
       wv.z = fmaf(nlr, ov.z, wv.z);
@@ -271,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
       const int64_t r = e / cols;
       const int col = (int)(e - r * cols);
-      float v = fmaf(nlr, ns_to_f(D[r * g.cp + col]), w[e]);
+      float v = fmaf(nlr, Fmt<F>::load(D + r * ldb, col), w[e]);
       if (kProject) {
         w[e] = v * scale;
       } else {
@@ -285,15 +315,16 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_read_update(const T* D, int ldD, int rows, int cols,
-                                                          float* dst) {
+template <int F>
+__global__ __launch_bounds__(kThreads) void k_read_update(const char* D, int ldD, int rows,
+                                                          int cols, float* dst) {
+  constexpr int kEB = ns_elem_bytes((NsPrec)F);
   const int64_t n = (int64_t)rows * cols;
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n;
        e += (int64_t)gridDim.x * kThreads) {
     const int64_t r = e / cols;
     const int col = (int)(e - r * cols);
-    dst[e] = ns_to_f(D[r * ldD + col]);
+    dst[e] = Fmt<F>::load(D + r * ldD * kEB, col);
   }
 }
 
@@ -318,48 +349,45 @@ hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norm
   return hipGetLastError();
 }
 
-hipError_t launch_normcast(const EwArgs& a, bool fp32, const float* const* M, const double* norms,
-                           hipStream_t s) {
-  if (fp32)
-    hipLaunchKernelGGL(k_normcast<float>, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms);
-  else
-    hipLaunchKernelGGL(k_normcast<__bf16>, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms);
+#define MUONH_PREC_DISPATCH(PREC, KERNEL, ...)                       \
+  switch (PREC) {                                                    \
+    case kBf16: hipLaunchKernelGGL(KERNEL(kBf16), __VA_ARGS__); break; \
+    case kSplitBf16: hipLaunchKernelGGL(KERNEL(kSplitBf16), __VA_ARGS__); break; \
+    case kFp32: hipLaunchKernelGGL(KERNEL(kFp32), __VA_ARGS__); break; \
+  }
+
+#define K_NORMCAST(F) k_normcast<F>
+#define K_UPDATE(F) (k_update<F, false>)
+#define K_PROJECT(F) (k_update<F, true>)
+#define K_READ(F) k_read_update<F>
+
+hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
+                           const double* norms, hipStream_t s) {
+  MUONH_PREC_DISPATCH(prec, K_NORMCAST, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms)
   return hipGetLastError();
 }
 
-hipError_t launch_update_norm(const EwArgs& a, bool fp32, float* const* W, float lr,
+hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, float lr,
                               double* partials, hipStream_t s) {
-  if (fp32)
-    hipLaunchKernelGGL((k_update<float, false>), dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr,
-                       partials, nullptr, nullptr);
-  else
-    hipLaunchKernelGGL((k_update<__bf16, false>), dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr,
-                       partials, nullptr, nullptr);
+  MUONH_PREC_DISPATCH(prec, K_UPDATE, dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr, partials,
+                      nullptr, nullptr)
   return hipGetLastError();
 }
 
-hipError_t launch_project(const EwArgs& a, bool fp32, float* const* W, const float* R,
+hipError_t launch_project(const EwArgs& a, NsPrec prec, float* const* W, const float* R,
                           const double* norms, float lr, hipStream_t s) {
-  if (fp32)
-    hipLaunchKernelGGL((k_update<float, true>), dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr,
-                       nullptr, R, norms);
-  else
-    hipLaunchKernelGGL((k_update<__bf16, true>), dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr,
-                       nullptr, R, norms);
+  MUONH_PREC_DISPATCH(prec, K_PROJECT, dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr, nullptr,
+                      R, norms)
   return hipGetLastError();
 }
 
-hipError_t launch_read_update(bool fp32, const char* D, int ldD, int rows, int cols, float* dst,
+hipError_t launch_read_update(NsPrec prec, const char* D, int ldD, int rows, int cols, float* dst,
                               hipStream_t s) {
   const int64_t n = (int64_t)rows * cols;
   int64_t blocks = (n + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
-  if (fp32)
-    hipLaunchKernelGGL(k_read_update<float>, dim3((int)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const float*>(D), ldD, rows, cols, dst);
-  else
-    hipLaunchKernelGGL(k_read_update<__bf16>, dim3((int)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const __bf16*>(D), ldD, rows, cols, dst);
+  MUONH_PREC_DISPATCH(prec, K_READ, dim3((int)blocks), dim3(kThreads), 0, s, D, ldD, rows, cols,
+                      dst)
   return hipGetLastError();
 }
 

@@ -68,8 +68,8 @@ struct muonh_plan {
   int64_t n_mats = 0;
   int64_t n_params = 0;
   uint32_t flags = 0;
-  bool fp32 = false;
-  int esize = 2;
+  NsPrec prec = kBf16;
+  int esize = 2;  // workspace bytes per logical Newton-Schulz element
   int64_t off_partials = 0, off_norm_m = 0, off_norm_w = 0;
   size_t ws_bytes = 0;
 };
@@ -135,7 +135,7 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final
 
 // GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
 std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters) {
-  const int T = gemm_tile(p->fp32);
+  const int T = gemm_tile(p->prec);
   std::vector<GemmGroup> all;
   for (const GroupPlan& G : p->groups) {
     GemmGroup q;
@@ -202,7 +202,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     }
     a.ngroups = (int)(g1 - g0);
     a.ntiles = (int)tiles;
-    a.xcd_map = p->fp32 ? 0 : 1;
+    a.xcd_map = p->prec == kFp32 ? 0 : 1;
     if (a.xcd_map) {
       // slots per XCD: the longest of the 8 per-XCD lists
       int64_t longest = 0;
@@ -260,13 +260,16 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   if (!groups) return fail(MUONH_EINVAL, "groups is NULL");
   if (n_groups < 1 || n_groups > MUONH_MAX_GROUPS)
     return fail(MUONH_EINVAL, "n_groups=%d out of [1, %d]", n_groups, MUONH_MAX_GROUPS);
-  if (flags & ~uint32_t(MUONH_NS_FP32)) return fail(MUONH_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~uint32_t(MUONH_NS_FP32 | MUONH_NS_SPLIT_BF16))
+    return fail(MUONH_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & MUONH_NS_FP32) && (flags & MUONH_NS_SPLIT_BF16))
+    return fail(MUONH_EINVAL, "MUONH_NS_FP32 and MUONH_NS_SPLIT_BF16 exclude each other");
 
   muonh_plan* p = new (std::nothrow) muonh_plan;
   if (!p) return fail(MUONH_ENOMEM, "plan allocation failed");
   p->flags = flags;
-  p->fp32 = (flags & MUONH_NS_FP32) != 0;
-  p->esize = p->fp32 ? 4 : 2;
+  p->prec = (flags & MUONH_NS_FP32) ? kFp32 : (flags & MUONH_NS_SPLIT_BF16) ? kSplitBf16 : kBf16;
+  p->esize = ns_elem_bytes(p->prec);
 
   int64_t n_mats = 0;
   for (int32_t i = 0; i < n_groups; ++i) {
@@ -416,29 +419,29 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
       return hip_fail(e, "momentum finalize");
   }
   for (const EwArgs& a : tile_args)
-    if ((e = launch_normcast(a, plan->fp32, M, norm_m, s)) != hipSuccess)
+    if ((e = launch_normcast(a, plan->prec, M, norm_m, s)) != hipSuccess)
       return hip_fail(e, "normcast");
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
 
   for (int it = 0; it < ns_iters; ++it) {
     for (const GemmArgs& a : make_gemm(plan, ws, kGram, it, ns_iters))
-      if ((e = launch_gemm(kGram, plan->fp32, a, s)) != hipSuccess) return hip_fail(e, "ns gram");
+      if ((e = launch_gemm(kGram, plan->prec, a, s)) != hipSuccess) return hip_fail(e, "ns gram");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
     for (const GemmArgs& a : make_gemm(plan, ws, kPoly, it, ns_iters))
-      if ((e = launch_gemm(kPoly, plan->fp32, a, s)) != hipSuccess) return hip_fail(e, "ns poly");
+      if ((e = launch_gemm(kPoly, plan->prec, a, s)) != hipSuccess) return hip_fail(e, "ns poly");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
     for (const GemmArgs& a : make_gemm(plan, ws, kApply, it, ns_iters))
-      if ((e = launch_gemm(kApply, plan->fp32, a, s)) != hipSuccess)
+      if ((e = launch_gemm(kApply, plan->prec, a, s)) != hipSuccess)
         return hip_fail(e, "ns apply");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
   }
 
   for (const EwArgs& a : stream_args) {
-    if ((e = launch_update_norm(a, plan->fp32, W, lr, partials, s)) != hipSuccess)
+    if ((e = launch_update_norm(a, plan->prec, W, lr, partials, s)) != hipSuccess)
       return hip_fail(e, "update norm");
     if ((e = launch_finalize(a, partials, norm_w, nullptr, s)) != hipSuccess)
       return hip_fail(e, "update finalize");
-    if ((e = launch_project(a, plan->fp32, W, R, norm_w, lr, s)) != hipSuccess)
+    if ((e = launch_project(a, plan->prec, W, R, norm_w, lr, s)) != hipSuccess)
       return hip_fail(e, "project");
   }
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
@@ -480,7 +483,7 @@ int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const v
   const char* blk = static_cast<const char*>(workspace) + G->off + (index - G->first) * G->mat_bytes;
   const char* D = blk + (G->trans ? G->offXt[0] : G->offX);
   const int ld = G->trans ? G->sp : G->lp;
-  hipError_t e = launch_read_update(plan->fp32, D, ld, G->rows, G->cols, dst,
+  hipError_t e = launch_read_update(plan->prec, D, ld, G->rows, G->cols, dst,
                                     reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "read update");
   return MUONH_OK;

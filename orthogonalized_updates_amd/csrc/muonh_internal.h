@@ -22,6 +22,16 @@ constexpr int kPad = 256;
 // Max number of per-matrix partial sums of a norm reduction.
 constexpr int kMaxPartials = 256;
 
+// Storage format of the Newton-Schulz operands (X, X^T, A, B):
+//   kBf16      bf16, rows dense;
+//   kSplitBf16 each value v as hi = bf16(v) and lo = bf16(v - hi); a row is a
+//              sequence of 128-byte blocks of 32 hi then 32 lo values;
+//   kFp32      fp32 (debug mode).
+// Leading dimensions are always in logical elements; bytes per logical
+// element: 2, 4 and 4.
+enum NsPrec : int { kBf16 = 0, kSplitBf16 = 1, kFp32 = 2 };
+constexpr int ns_elem_bytes(NsPrec p) { return p == kBf16 ? 2 : 4; }
+
 // ---------------------------------------------------------------------------
 // Elementwise / reduction kernels (elementwise.hip)
 // ---------------------------------------------------------------------------
@@ -60,14 +70,14 @@ hipError_t launch_momentum(const EwArgs& a, const float* const* G, float* const*
 hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norms, float* R,
                            hipStream_t s);
 // X0 = M / (norm + eps) written to D (same orientation) and E (transposed).
-hipError_t launch_normcast(const EwArgs& a, bool fp32, const float* const* M, const double* norms,
-                           hipStream_t s);
-hipError_t launch_update_norm(const EwArgs& a, bool fp32, float* const* W, float lr,
+hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
+                           const double* norms, hipStream_t s);
+hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, float lr,
                               double* partials, hipStream_t s);
-hipError_t launch_project(const EwArgs& a, bool fp32, float* const* W, const float* R,
+hipError_t launch_project(const EwArgs& a, NsPrec prec, float* const* W, const float* R,
                           const double* norms, float lr, hipStream_t s);
 // dst (rows x cols fp32) <- D of one matrix.
-hipError_t launch_read_update(bool fp32, const char* D, int ldD, int rows, int cols, float* dst,
+hipError_t launch_read_update(NsPrec prec, const char* D, int ldD, int rows, int cols, float* dst,
                               hipStream_t s);
 
 // ---------------------------------------------------------------------------
@@ -103,8 +113,8 @@ struct GemmArgs {
   float c0, c1;
 };
 
-// Tile edge (square tiles) used by the launchers for the given mode/type.
-int gemm_tile(bool fp32);
-hipError_t launch_gemm(GemmMode mode, bool fp32, const GemmArgs& a, hipStream_t s);
+// Tile edge (square tiles) used by the launchers for the given precision.
+int gemm_tile(NsPrec prec);
+hipError_t launch_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a, hipStream_t s);
 
 }  // namespace muonh

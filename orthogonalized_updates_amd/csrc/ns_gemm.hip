@@ -460,51 +460,80 @@ __device__ __forceinline__ void quad_transpose(uint32_t& d0, uint32_t& d1, int l
 
 // Main loop of one group of the ping-pong schedule (see k_ns_gemm_bf16).
 // Both groups execute the same sequence of barriers; G selects the role.
+//
+// Plain bf16: a slab is 64 logical k; chunk ch holds k steps 2ch and 2ch+1
+// (fragments fa, fb); each 32x32 block takes 2 MFMAs per chunk.
+// SPLIT (split-bf16 operands, each 128-byte slab row = 32 hi + 32 lo values
+// of 32 logical k): chunk ch is k step ch, fa its hi and fb its lo
+// fragments; each block takes hi*hi + hi*lo + lo*hi (3 MFMAs per chunk).
+//
 // With E_TERM, the fp32 term seed*E (apply: E = X, seed = a; polynomial:
 // E = A, seed = b/c) is added to the accumulators on the way: element
 // (i, j) of E is element (j, i) of the Q operand (X^T, or A itself, which
 // is symmetric), so the E tile streams through the LDS ring as part of Q's
 // slabs with k in [256*bi, 256*bi + 256). When a wave loads a chunk of that
-// K range, it also reads, for the 32 accumulator rows the chunk covers, its
-// 4 consecutive k values per column (one 8-byte LDS read per 4 elements).
-template <int G, int MT, int NT, bool E_TERM>
+// K range, it also reads, for the accumulator rows the chunk covers, its 4
+// consecutive k values per column (one 8-byte LDS read per 4 elements, two
+// with SPLIT: E = hi + lo).
+template <int G, int MT, int NT, bool E_TERM, bool SPLIT>
 __device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int nk, char* s0,
                                          char* s1, int wm0, int wn0, const int (&loff)[bf::kKS],
                                          int lane, int bi, float seed, f32x16 (&acc)[MT][NT]) {
   using namespace bf;
-  Frags<MT, NT> fa, fb;  // the two k steps of one chunk
-  // Chunk ch of stage kt covers k in [64*kt + 32*ch, +32): accumulator rows
-  // (of this tile) r = 64*kt + 32*ch - 256*bi when that lies in [0, 256).
+  constexpr int kW = SPLIT ? 16 : 32;   // logical k per chunk
+  constexpr int kSW = SPLIT ? 32 : 64;  // logical k per slab
+  Frags<MT, NT> fa, fb;
   auto take_e = [&](const char* buf, int kt, int ch) {
-    const int r = 64 * kt + 32 * ch - 256 * bi - wm0;  // row block in this wave's 128 rows
+    // first accumulator row (relative to wm0) whose E value sits in this chunk
+    const int r = kt * kSW + ch * kW - 256 * bi - wm0;
     if (r < 0 || r >= MT * 32) return;
     const char* lb = buf + kSlabA;
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      if (r != mi * 32) continue;
+    for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
+      for (int rg = 0; rg < 4; ++rg) {
+        const int row = mi * 32 + 8 * rg;  // rows row + 4*(lane/32) + q, q < 4
+        if (row < r || row >= r + kW) continue;
+        const int kk = ch * kW + (row - r) + 4 * (lane >> 5);  // logical k within the slab
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          // k within the slab: 32*ch + 8*rg + 4*(lane/32); Q row: wn0 + ni*32 + lane%32
-          const int kk = 32 * ch + 8 * rg + 4 * (lane >> 5);
+        for (int ni = 0; ni < NT; ++ni) {
           const int qrow = wn0 + ni * 32 + (lane & 31);
-          const bf16x4 ev =
+          const bf16x4 hv =
               *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, kk >> 3) + ((kk & 7) << 1));
+          float e[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = (float)hv[q];
+          if (SPLIT) {
+            const bf16x4 lv =
+                *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, 4 + (kk >> 3)) + ((kk & 7) << 1));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) e[q] += (float)lv[q];
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[mi][ni][rg * 4 + q] = fmaf(seed, (float)ev[q], acc[mi][ni][rg * 4 + q]);
+            acc[mi][ni][rg * 4 + q] = fmaf(seed, e[q], acc[mi][ni][rg * 4 + q]);
         }
-    }
+      }
   };
   auto load = [&](const char* buf, int ch, int kt) {
-    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[2 * ch], fa);
-    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[2 * ch + 1], fb);
+    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[SPLIT ? ch : 2 * ch], fa);
+    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[SPLIT ? ch + 2 : 2 * ch + 1], fb);
     if (E_TERM) take_e(buf, kt, ch);
   };
   auto mul = [&]() {
-    mfma_frags<MT, NT>(fa, acc);
-    mfma_frags<MT, NT>(fb, acc);
+    if (SPLIT) {
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb.a[mi], fa.b[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa.a[mi], fb.b[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa.a[mi], fa.b[ni], acc[mi][ni], 0, 0, 0);
+        }
+    } else {
+      mfma_frags<MT, NT>(fa, acc);
+      mfma_frags<MT, NT>(fb, acc);
+    }
   };
   // phase 0: group 0 loads chunk 0 of stage 0
   if (G == 0) load(s0, 0, 0);
@@ -531,7 +560,7 @@ __device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int 
   }
 }
 
-template <int MODE, int WGM, int WGN>
+template <int MODE, int WGM, int WGN, bool SPLIT>
 __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf16(GemmArgs args) {
   using namespace bf;
   using C = Cfg<WGM, WGN>;
@@ -554,7 +583,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   tile_coords<kSym>(g, local - mat * g.tiles_per_mat, bi, bj);
 
   const char* blk = g.base + (int64_t)mat * g.mat_bytes;
-  const int64_t ldp_b = (int64_t)g.ldp * 2, ldq_b = (int64_t)g.ldq * 2;
+  // Row pitch in bytes: 2 per logical element, 4 with split operands.
+  constexpr int kEB = SPLIT ? 4 : 2;
+  const int64_t ldp_b = (int64_t)g.ldp * kEB, ldq_b = (int64_t)g.ldq * kEB;
   const char* P = blk + g.offP + (int64_t)bi * kBM * ldp_b;
   const char* Q = blk + g.offQ + (int64_t)bj * kBN * ldq_b;
 
@@ -564,7 +595,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 #pragma unroll
     for (int ni = 0; ni < kNT; ++ni) acc[mi][ni] = f32x16{};
 
-  const int nk = g.K / 64;  // slabs; even, since K is a multiple of kPad
+  const int nk = g.K / (SPLIT ? 32 : 64);  // slabs; even, since K is a multiple of kPad
   const int wm0 = wm * kWTM, wn0 = wn * kWTN;
   // Ping-pong schedule. Stage s (a 64-wide K slab, full 128-byte rows) lives
   // in buffer s % 2 and is consumed in two chunks of two 16-wide k steps.
@@ -593,42 +624,55 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   phase_barrier();
   const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
   if (wave < 4)
-    pingpong<0, kMT, kNT, MODE != kGram>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi, seed,
-                                         acc);
+    pingpong<0, kMT, kNT, MODE != kGram, SPLIT>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi,
+                                                seed, acc);
   else
-    pingpong<1, kMT, kNT, MODE != kGram>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi, seed,
-                                         acc);
+    pingpong<1, kMT, kNT, MODE != kGram, SPLIT>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi,
+                                                seed, acc);
 
   // ---- epilogue. The E term is already in the accumulators (the
   // polynomial's still needs its factor c). Outputs leave through the idle
-  // LDS ring in two 256x256 bf16 passes (row-major, then transposed) so that
-  // every global store is a coalesced 16-byte store.
+  // LDS ring, one 256x256 bf16 pass per layout (row-major, then transposed;
+  // with SPLIT one pass for the hi and one for the lo parts of each) so
+  // that every global store is a coalesced 16-byte store.
   const float scale = MODE == kPoly ? args.c1 : 1.f;
-  bf16x4 v4[kMT][kNT][4];
+  bf16x4 vh[kMT][kNT][4], vl[kMT][kNT][4];
 #pragma unroll
   for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kNT; ++ni)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 o;
+        bf16x4 h, l;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = (__bf16)(scale * acc[mi][ni][rg * 4 + q]);
-        v4[mi][ni][rg] = o;
+        for (int q = 0; q < 4; ++q) {
+          const float v = scale * acc[mi][ni][rg * 4 + q];
+          h[q] = (__bf16)v;
+          if (SPLIT) l[q] = (__bf16)(v - (float)h[q]);
+        }
+        vh[mi][ni][rg] = h;
+        if (SPLIT) vl[mi][ni][rg] = l;
       }
 
   // The two 64 KB ring buffers hold 128 rows of 512 B each of the staging
   // tile; ring(q) is the 32 KB quarter holding rows [64q, 64q + 64).
   auto ring = [&](int q) -> char* { return (q < 2 ? s0 : s1) + (q & 1) * 32768; };
-  __bf16* O1 = g.offO1 < 0 ? nullptr : reinterpret_cast<__bf16*>(const_cast<char*>(blk) + g.offO1);
-  __bf16* O2 = g.offO2 < 0 ? nullptr : reinterpret_cast<__bf16*>(const_cast<char*>(blk) + g.offO2);
-  __bf16* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;  // transposed destination
-  const int ldT = kSym ? g.ldo1 : g.ldo2;
+  char* O1 = g.offO1 < 0 ? nullptr : const_cast<char*>(blk) + g.offO1;
+  char* O2 = g.offO2 < 0 ? nullptr : const_cast<char*>(blk) + g.offO2;
+  char* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;  // transposed destination
+  const int64_t ld1_b = (int64_t)g.ldo1 * kEB, ldT_b = (int64_t)(kSym ? g.ldo1 : g.ldo2) * kEB;
+  // Byte offset, within a row, of the 16-byte chunk holding logical columns
+  // col .. col+7 (col a multiple of 8): plain rows are dense bf16; split rows
+  // are 128-byte blocks of 32 hi then 32 lo values.
+  auto col_off = [&](int col, bool lo) -> int64_t {
+    if (!SPLIT) return (int64_t)col * 2;
+    return (int64_t)(col >> 5) * 128 + ((col & 31) << 1) + (lo ? 64 : 0);
+  };
 
-  // Pass 1, row-major into O1: LDS tile [row][col], 16-byte chunk c of row r
+  // Row-major pass into O1: LDS tile [row][col], 16-byte chunk c of row r
   // stored at position c ^ (r & 31). A quad transpose first gives each lane
   // 4 consecutive columns of one row, so the LDS writes are 8-byte writes.
-  if (O1) {
+  auto pass_rows = [&](const bf16x4 (&v)[kMT][kNT][4], bool lo) {
     __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
@@ -639,7 +683,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
         for (int rg = 0; rg < 4; ++rg) {
           const int row = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5) + (lane & 3);
           typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-          u32x2 d = __builtin_bit_cast(u32x2, v4[mi][ni][rg]);
+          u32x2 d = __builtin_bit_cast(u32x2, v[mi][ni][rg]);
           uint32_t d0 = d.x, d1 = d.y;
           quad_transpose(d0, d1, lane);
           d.x = d0;
@@ -656,12 +700,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
       const int row = id >> 5, c = id & 31;
       const u32x4 d = *reinterpret_cast<const u32x4*>(ring(row >> 6) + (row & 63) * 512 +
                                                       ((c ^ (row & 31)) << 4));
-      *reinterpret_cast<u32x4*>(O1 + (int64_t)(bi * kBM + row) * g.ldo1 + bj * kBN + c * 8) = d;
+      *reinterpret_cast<u32x4*>(O1 + (int64_t)(bi * kBM + row) * ld1_b +
+                                col_off(bj * kBN + c * 8, lo)) = d;
     }
-  }
-  // Pass 2, transposed into OT: LDS tile [col][row], 16-byte chunk c of LDS
+  };
+  // Transposed pass into OT: LDS tile [col][row], 16-byte chunk c of LDS
   // row j stored at position c ^ (j & 31).
-  if (OT) {
+  auto pass_cols = [&](const bf16x4 (&v)[kMT][kNT][4], bool lo) {
     __syncthreads();
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
@@ -673,7 +718,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
         for (int rg = 0; rg < 4; ++rg) {
           const int row0 = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5);
           const int off = ((((row0 >> 3) ^ (col & 31)) << 4) | ((row0 & 7) << 1));
-          *reinterpret_cast<bf16x4*>(base + off) = v4[mi][ni][rg];
+          *reinterpret_cast<bf16x4*>(base + off) = v[mi][ni][rg];
         }
       }
     __syncthreads();
@@ -683,8 +728,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
       const int j = id >> 5, c = id & 31;
       const u32x4 d = *reinterpret_cast<const u32x4*>(ring(j >> 6) + (j & 63) * 512 +
                                                       ((c ^ (j & 31)) << 4));
-      *reinterpret_cast<u32x4*>(OT + (int64_t)(bj * kBN + j) * ldT + bi * kBM + c * 8) = d;
+      *reinterpret_cast<u32x4*>(OT + (int64_t)(bj * kBN + j) * ldT_b +
+                                col_off(bi * kBM + c * 8, lo)) = d;
     }
+  };
+  if (O1) {
+    pass_rows(vh, false);
+    if (SPLIT) pass_rows(vl, true);
+  }
+  if (OT) {
+    pass_cols(vh, false);
+    if (SPLIT) pass_cols(vl, true);
   }
 }
 
@@ -692,10 +746,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 constexpr int kTile32 = 128;
 
 template <typename T, int MODE>
-hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_t(const GemmArgs& a, hipStream_t s, bool split) {
   if constexpr (std::is_same<T, __bf16>::value) {
     // bf16: 256x256 tiles, 8 waves in a 2 x 4 grid (wave tile 128 x 64).
-    hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4>), dim3(a.grid), dim3(512), 0, s, a);
+    if (split)
+      hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4, true>), dim3(a.grid), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4, false>), dim3(a.grid), dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL((k_ns_gemm<T, kTile32, kTile32, 2, 2, MODE>), dim3(a.ntiles), dim3(256), 0,
                        s, a);
@@ -705,21 +762,22 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int gemm_tile(bool fp32) { return fp32 ? kTile32 : bf::kBM; }
+int gemm_tile(NsPrec prec) { return prec == kFp32 ? kTile32 : bf::kBM; }
 
-hipError_t launch_gemm(GemmMode mode, bool fp32, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a, hipStream_t s) {
   if (a.ntiles <= 0) return hipSuccess;
-  if (fp32) {
+  const bool split = prec == kSplitBf16;
+  if (prec == kFp32) {
     switch (mode) {
-      case kGram: return launch_t<float, kGram>(a, s);
-      case kPoly: return launch_t<float, kPoly>(a, s);
-      case kApply: return launch_t<float, kApply>(a, s);
+      case kGram: return launch_t<float, kGram>(a, s, false);
+      case kPoly: return launch_t<float, kPoly>(a, s, false);
+      case kApply: return launch_t<float, kApply>(a, s, false);
     }
   } else {
     switch (mode) {
-      case kGram: return launch_t<__bf16, kGram>(a, s);
-      case kPoly: return launch_t<__bf16, kPoly>(a, s);
-      case kApply: return launch_t<__bf16, kApply>(a, s);
+      case kGram: return launch_t<__bf16, kGram>(a, s, split);
+      case kPoly: return launch_t<__bf16, kPoly>(a, s, split);
+      case kApply: return launch_t<__bf16, kApply>(a, s, split);
     }
   }
   return hipErrorInvalidValue;

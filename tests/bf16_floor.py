@@ -7,6 +7,10 @@ floor that bf16 storage alone imposes on the iteration for a given input; a
 bf16 GPU result cannot be expected to beat it. For most shapes the floor is
 well under the 2e-2 parity bound; for tiny matrices (a handful of singular
 values, so no averaging) it can exceed it.
+
+fmt="split_bf16" emulates the split storage instead: a stored value v is
+hi + lo with hi = bf16(v) and lo = bf16(v - hi) (the difference taken in
+fp32), and a product of two split operands omits lo*lo.
 """
 from __future__ import annotations
 
@@ -25,21 +29,54 @@ def round_bf16(x) -> np.ndarray:
     return np.where(np.isnan(f), np.nan, out)
 
 
-def ns_bf16(m, k: int) -> np.ndarray:
+def split_bf16(x):
+    """float -> (hi, lo) bf16 pair as float64 arrays, lo = bf16(fp32(x) - hi)."""
+    f = np.asarray(x, dtype=np.float32)
+    hi = round_bf16(f)
+    lo = round_bf16((f - hi.astype(np.float32)).astype(np.float32))
+    return hi, lo
+
+
+def _ns_emulated(m, k: int, fmt: str) -> np.ndarray:
+    if fmt == "bf16":
+        def store(v):
+            r = round_bf16(v)
+            return r, r, None
+
+        def mul(p, q):
+            return p[0] @ q[0]
+    elif fmt == "split_bf16":
+        def store(v):
+            hi, lo = split_bf16(v)
+            return hi + lo, hi, lo
+
+        def mul(p, q):
+            return p[1] @ q[1] + p[1] @ q[2] + p[2] @ q[1]
+    else:
+        raise ValueError(fmt)
     x = np.asarray(m, dtype=np.float64)
     t = x.shape[0] > x.shape[1]
     if t:
         x = x.T
-    x = round_bf16(x / (np.linalg.norm(x) + EPS))
+    x = store(x / (np.linalg.norm(x) + EPS))
     for _ in range(int(k)):
-        a = round_bf16(x @ x.T)
-        b = round_bf16(B_ * a + C_ * (a @ a))
-        x = round_bf16(A_ * x + b @ x)
-    return x.T if t else x
+        xt = tuple(None if v is None else v.T for v in x)
+        a = store(mul(x, xt))
+        b = store(B_ * a[0] + C_ * mul(a, a))
+        x = store(A_ * x[0] + mul(b, x))
+    return x[0].T if t else x[0]
 
 
-def floor(m, k: int, reference) -> float:
-    """Relative Frobenius error of the bf16-emulated iteration vs `reference`."""
-    e = ns_bf16(m, k)
+def ns_bf16(m, k: int) -> np.ndarray:
+    return _ns_emulated(m, k, "bf16")
+
+
+def ns_split_bf16(m, k: int) -> np.ndarray:
+    return _ns_emulated(m, k, "split_bf16")
+
+
+def floor(m, k: int, reference, fmt: str = "bf16") -> float:
+    """Relative Frobenius error of the emulated iteration vs `reference`."""
+    e = _ns_emulated(m, k, fmt)
     nr = np.linalg.norm(reference)
     return float(np.linalg.norm(e - reference) / (nr if nr > 0 else 1.0))

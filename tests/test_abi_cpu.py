@@ -46,6 +46,7 @@ def _create(groups, flags=0):
 @pytest.mark.parametrize("groups,flags,code", [
     ([], 0, mh.MUONH_EINVAL),                      # no groups (empty input)
     ([(4, 4, 1)], 0x10, mh.MUONH_EINVAL),          # unknown flag
+    ([(4, 4, 1)], mh.MUONH_NS_FP32 | mh.MUONH_NS_SPLIT_BF16, mh.MUONH_EINVAL),  # two precisions
     ([(0, 4, 1)], 0, mh.MUONH_ESHAPE),             # zero rows
     ([(4, -1, 1)], 0, mh.MUONH_ESHAPE),            # negative cols
     ([(4, 4, 0)], 0, mh.MUONH_ESHAPE),             # empty group
@@ -73,8 +74,20 @@ def test_plan_counts_and_workspace_growth():
     ns = 56 * 2 * (3 * 2048 * 2048 + 2 * 2048 * 2048) + 56 * 2 * (3 * 512 * 2048 + 2 * 512 * 512) \
         + 84 * 2 * (3 * 2048 * 6144 + 2 * 2048 * 2048)
     assert ns <= ws <= ns + 196 * (256 * 8 + 16) + 4096
-    p32 = mh.Plan([(2048, 2048, 56), (512, 2048, 56), (6144, 2048, 56), (2048, 6144, 28)], ns_fp32=True)
+    shapes = [(2048, 2048, 56), (512, 2048, 56), (6144, 2048, 56), (2048, 6144, 28)]
+    p32 = mh.Plan(shapes, ns_fp32=True)
     assert p32.workspace_bytes > 1.9 * ns
+    # split bf16: a hi and a lo value per element, so twice the operand bytes
+    psp = mh.Plan(shapes, precision="split_bf16")
+    assert 2 * ns <= psp.workspace_bytes <= 2 * ns + 196 * (256 * 8 + 16) + 4096
+    assert psp.precision == "split_bf16" and p32.precision == "fp32" and p.precision == "bf16"
+
+
+def test_binding_rejects_unknown_precision():
+    with pytest.raises(ValueError):
+        mh.Plan([(4, 4, 1)], precision="fp16")
+    with pytest.raises(ValueError):
+        mh.Plan([(4, 4, 1)], ns_fp32=True, precision="split_bf16")
 
 
 def test_plan_padding_of_ragged_shapes():

@@ -415,6 +415,34 @@ def test_bf16_rounding_is_nearest_even():
     assert np.isnan(round_bf16(np.float32("nan")))
 
 
+def test_split_bf16_pair_carries_sixteen_bits():
+    # hi + lo represents an fp32 value to within about 2^-17 of its magnitude
+    # (hi has 8 significant bits, lo the next 8 and a rounding bit), and lo is
+    # exactly the rounded remainder of hi.
+    from bf16_floor import round_bf16, split_bf16
+    x = rand((4096,), (21, 0), 1.0).astype(np.float32).astype(np.float64)
+    hi, lo = split_bf16(x)
+    np.testing.assert_array_equal(hi, round_bf16(x))
+    assert np.all(np.abs(x - (hi + lo)) <= 2.0 ** -16 * np.abs(x))
+    assert np.max(np.abs(x - (hi + lo)) / np.abs(x)) > 2.0 ** -20   # not exact: 8 more bits only
+    v = np.float64(1.0 + 2.0 ** -7 + 2.0 ** -15)   # hi = 1 + 2^-7, lo = 2^-15 exactly
+    h, l = split_bf16(v)
+    assert h == 1.0 + 2.0 ** -7 and l == 2.0 ** -15
+
+
+@pytest.mark.parametrize("shape,k", [((128, 256), 5), ((384, 640), 8)])
+def test_split_bf16_floor_is_far_below_bf16(shape, k):
+    # The split emulation (hi + lo operands, lo*lo omitted) lands near
+    # 2^-8 of the bf16 floor: 2e-5 to 6e-5 on these shapes.
+    from bf16_floor import floor
+    m = rand(shape, (22, shape[0]), 0.01)
+    ref = oracle.newton_schulz(m, k)
+    f16 = floor(m, k, ref)
+    fsp = floor(m, k, ref, "split_bf16")
+    assert fsp < 1e-4
+    assert fsp < f16 / 100
+
+
 @pytest.mark.parametrize("shape,k,limit", [((128, 256), 5, 1.4e-2), ((512, 1536), 5, 1.4e-2),
                                            ((384, 640), 8, 2.3e-2), ((1024, 3072), 8, 2.0e-2)])
 def test_bf16_floor_by_shape(shape, k, limit):
