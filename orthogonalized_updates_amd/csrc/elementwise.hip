@@ -148,57 +148,71 @@ __global__ __launch_bounds__(kThreads) void k_finalize(EwArgs a, const double* p
 }
 
 // --------------------------------------------------------------------------
-// Newton-Schulz operand storage formats (see NsPrec): element `col` of a row
-// that starts at byte `row`.
+// Newton-Schulz operand storage formats (see NsPrec): element (r, c) of a
+// matrix with ld logical columns (rows and ld multiples of 256).
+//   bf16:  panel-major, panels of 256 rows x 32 values (64-byte panel rows),
+//          panel (r/256, c/32) at ((r/256) * (ld/32) + c/32) * 16 KB;
+//   split: the same with 16 values per panel row: 16 hi (bf16(v)) then the
+//          16 matching lo (bf16(v - hi));
+//   fp32:  row-major, row pitch ld (the fp32 debug kernel's layout).
 // --------------------------------------------------------------------------
 template <int F>
 struct Fmt;
 template <>
 struct Fmt<kBf16> {
-  __device__ static void store(char* row, int col, float v) {
-    reinterpret_cast<__bf16*>(row)[col] = (__bf16)v;
+  __device__ static int64_t off(int64_t r, int c, int ld) {
+    return ((((r >> 8) * (ld >> 5)) + (c >> 5)) << 14) + ((r & 255) << 6) + ((c & 31) << 1);
   }
-  __device__ static float load(const char* row, int col) {
-    return (float)reinterpret_cast<const __bf16*>(row)[col];
+  __device__ static void store(char* base, int64_t r, int c, int ld, float v) {
+    *reinterpret_cast<__bf16*>(base + off(r, c, ld)) = (__bf16)v;
   }
-  // 4 consecutive elements, col a multiple of 4.
-  __device__ static float4 load4(const char* row, int col) {
-    const uint2 u = *reinterpret_cast<const uint2*>(row + col * 2);
+  __device__ static float load(const char* base, int64_t r, int c, int ld) {
+    return (float)*reinterpret_cast<const __bf16*>(base + off(r, c, ld));
+  }
+  // 4 consecutive elements of a row, c a multiple of 4 (one 8-byte load).
+  __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
+    const uint2 u = *reinterpret_cast<const uint2*>(base + off(r, c, ld));
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
   }
 };
 template <>
 struct Fmt<kSplitBf16> {
-  // 128-byte blocks of 32 hi then 32 lo values
-  __device__ static int64_t off(int col) { return (int64_t)(col >> 5) * 128 + ((col & 31) << 1); }
-  __device__ static void store(char* row, int col, float v) {
+  __device__ static int64_t off(int64_t r, int c, int ld) {  // of the hi value; lo at +32
+    return ((((r >> 8) * (ld >> 4)) + (c >> 4)) << 14) + ((r & 255) << 6) + ((c & 15) << 1);
+  }
+  __device__ static void store(char* base, int64_t r, int c, int ld, float v) {
     const __bf16 h = (__bf16)v;
     const __bf16 l = (__bf16)(v - (float)h);
-    __bf16* p = reinterpret_cast<__bf16*>(row + off(col));
+    __bf16* p = reinterpret_cast<__bf16*>(base + off(r, c, ld));
     p[0] = h;
-    p[32] = l;
+    p[16] = l;
   }
-  __device__ static float load(const char* row, int col) {
-    const __bf16* p = reinterpret_cast<const __bf16*>(row + off(col));
-    return (float)p[0] + (float)p[32];
+  __device__ static float load(const char* base, int64_t r, int c, int ld) {
+    const __bf16* p = reinterpret_cast<const __bf16*>(base + off(r, c, ld));
+    return (float)p[0] + (float)p[16];
   }
-  __device__ static float4 load4(const char* row, int col) {
-    const float4 h = Fmt<kBf16>::load4(row + off(col), 0);
-    const float4 l = Fmt<kBf16>::load4(row + off(col) + 64, 0);
-    return make_float4(h.x + l.x, h.y + l.y, h.z + l.z, h.w + l.w);
+  __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
+    const char* p = base + off(r, c, ld);
+    const uint2 h = *reinterpret_cast<const uint2*>(p);
+    const uint2 l = *reinterpret_cast<const uint2*>(p + 32);
+    return make_float4(__uint_as_float(h.x << 16) + __uint_as_float(l.x << 16),
+                       __uint_as_float(h.x & 0xffff0000u) + __uint_as_float(l.x & 0xffff0000u),
+                       __uint_as_float(h.y << 16) + __uint_as_float(l.y << 16),
+                       __uint_as_float(h.y & 0xffff0000u) + __uint_as_float(l.y & 0xffff0000u));
   }
 };
 template <>
 struct Fmt<kFp32> {
-  __device__ static void store(char* row, int col, float v) {
-    reinterpret_cast<float*>(row)[col] = v;
+  __device__ static int64_t off(int64_t r, int c, int ld) { return (r * ld + c) * 4; }
+  __device__ static void store(char* base, int64_t r, int c, int ld, float v) {
+    *reinterpret_cast<float*>(base + off(r, c, ld)) = v;
   }
-  __device__ static float load(const char* row, int col) {
-    return reinterpret_cast<const float*>(row)[col];
+  __device__ static float load(const char* base, int64_t r, int c, int ld) {
+    return *reinterpret_cast<const float*>(base + off(r, c, ld));
   }
-  __device__ static float4 load4(const char* row, int col) {
-    return *reinterpret_cast<const float4*>(row + col * 4);
+  __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
+    return *reinterpret_cast<const float4*>(base + off(r, c, ld));
   }
 };
 
@@ -210,7 +224,6 @@ struct Fmt<kFp32> {
 template <int F>
 __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* const* M,
                                                        const double* norms) {
-  constexpr int kEB = ns_elem_bytes((NsPrec)F);
   __shared__ float tile[64][65];
   const int gi = group_of_block(a, blockIdx.x);
   const EwGroup& g = a.g[gi];
@@ -232,13 +245,13 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
     float v = 0.f;
     if (r < g.rows && c < g.cols) v = mp[(int64_t)r * g.cols + c] * scale;
     tile[rr][tx] = v;
-    Fmt<F>::store(D + (int64_t)r * g.cp * kEB, c, v);
+    Fmt<F>::store(D, r, c, g.cp, v);
   }
   __syncthreads();
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {
     const int cc = i * 4 + ty;
-    Fmt<F>::store(E + (int64_t)(c0 + cc) * g.rp * kEB, r0 + tx, tile[tx][cc]);
+    Fmt<F>::store(E, c0 + cc, r0 + tx, g.rp, tile[tx][cc]);
   }
 }
 
@@ -250,7 +263,6 @@ template <int F, bool kProject>
 __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, float lr,
                                                      double* partials, const float* R,
                                                      const double* norms) {
-  constexpr int kEB = ns_elem_bytes((NsPrec)F);
   __shared__ double red[4];
   const int gi = group_of_block(a, blockIdx.x);
   const EwGroup& g = a.g[gi];
@@ -259,7 +271,6 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
   const int mat = g.first + m;
   float* w = W[mat];
   const char* D = g.ns_base + (int64_t)m * g.mat_bytes + g.offD;
-  const int64_t ldb = (int64_t)g.cp * kEB;
   int64_t lo, hi;
   chunk_range(g.n, g.bpm, c, lo, hi);
   const float nlr = -lr;
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     const int dr = step / cols, dc = step - (step / cols) * cols;
     for (int64_t e = e0; e < hi; e += step) {
       float4 wv = *reinterpret_cast<const float4*>(w + e);
-      const float4 ov = Fmt<F>::load4(D + r * ldb, col);
+      const float4 ov = Fmt<F>::load4(D, r, col, g.cp);
       wv.x = fmaf(nlr, ov.x, wv.x);
       wv.y = fmaf(nlr, ov.y, wv.y);
       wv.z = fmaf(nlr, ov.z, wv.z);
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
       const int64_t r = e / cols;
       const int col = (int)(e - r * cols);
-      float v = fmaf(nlr, Fmt<F>::load(D + r * ldb, col), w[e]);
+      float v = fmaf(nlr, Fmt<F>::load(D, r, col, g.cp), w[e]);
       if (kProject) {
         w[e] = v * scale;
       } else {
@@ -318,13 +329,12 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
 template <int F>
 __global__ __launch_bounds__(kThreads) void k_read_update(const char* D, int ldD, int rows,
                                                           int cols, float* dst) {
-  constexpr int kEB = ns_elem_bytes((NsPrec)F);
   const int64_t n = (int64_t)rows * cols;
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n;
        e += (int64_t)gridDim.x * kThreads) {
     const int64_t r = e / cols;
     const int col = (int)(e - r * cols);
-    dst[e] = Fmt<F>::load(D + r * ldD * kEB, col);
+    dst[e] = Fmt<F>::load(D, r, col, ldD);
   }
 }
 

@@ -8,17 +8,18 @@
 //   B = b A + c A A            (A symmetric, so A A = A A^T: same kernel shape)
 //   X <- a X + B X             (B X = B (X^T)^T: operands are B rows, X^T rows)
 // so every product is C[i][j] = sum_k P[i][k] Q[j][k] with both operands read
-// as K-contiguous rows. The apply step writes the new X in both layouts (X and
-// X^T) so that the next Gram and the next apply again read K-contiguous rows.
+// along K. The apply step writes the new X in both layouts (X and X^T) so that
+// the next Gram and the next apply again read their operands along K.
 //
 // Every launch covers one phase for all matrices of all shape groups: one
 // workgroup per output tile, tiles dealt to the 8 XCDs in contiguous runs.
-// bf16 (the product path): 256x256 tiles, 8 waves in two groups that take
-// turns between MFMA clusters (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
-// and LDS fragment loads, operands streamed into a 2-stage LDS ring of
-// 64-wide K slabs by LDS DMA (global_load_lds_dwordx4), the fp32 a*X or b*A
-// term folded into the accumulators from the operand stream, and epilogues
-// staged through LDS for coalesced stores of both output layouts.
+// bf16 (the product path): operands stored panel-major (256 rows x 64 bytes
+// per panel), 256x256 tiles, 8 waves in two groups that take turns between
+// MFMA clusters (v_mfma_f32_32x32x16_bf16, fp32 accumulation) and LDS
+// fragment loads plus LDS DMA refills (global_load_lds_dwordx4) of a 4-stage
+// ring of 32 KB stages, the fp32 a*X or b*A term folded into the accumulators
+// from the operand stream, and epilogues staged through LDS for coalesced
+// stores of both output layouts.
 // fp32 debug: a simpler 128x128 kernel on v_mfma_f32_32x32x2f32 with
 // register-staged double buffering and direct epilogue stores.
 #include <hip/hip_runtime.h>
@@ -255,19 +256,31 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm(Gem
 }
 
 // ---------------------------------------------------------------------------
-// bf16 pipeline: 256x256 tiles, 8 waves (2 x 4, wave tile 128x64), operands
-// streamed straight from global memory into a 2-stage LDS ring of 64-wide K
-// slabs (full 128-byte rows; global_load_lds_dwordx4, no staging
-// registers). Each stage buffer is its own __shared__ object so that the
-// compiler can tell the in-flight DMA writes of one buffer apart from the
-// reads of the other.
+// bf16 and split-bf16 pipeline.
+//
+// Operands are stored panel-major: a matrix of R x K logical elements (both
+// multiples of 256) is a grid of (R/256) x (K/kPK) panels of 256 rows x 64
+// bytes, panel (rb, kb) at (rb * (K/kPK) + kb) * 16 KB, panel row r at r*64.
+// A 64-byte panel row holds kPK = 32 bf16 values, or in split mode 16 hi
+// values followed by the 16 matching lo values (kPK = 16). One K-stage of a
+// 256x256 tile is thus one contiguous 16 KB panel per operand: stages move
+// into LDS in whole cache lines however small they are, and a 4-stage ring of
+// 32 KB stages leaves each refill 4-5 phases to land.
+//
+// 8 waves (2 x 4, wave tile 128 x 64) form two groups of 4, one wave of each
+// per SIMD. They take turns phase by phase: one group issues its MFMA cluster
+// for a stage while the other reads the next stage's fragments from LDS and
+// then issues a quarter of the ring refill (LDS DMA, global_load_lds_dwordx4,
+// 4 instructions per wave). MFMA waves issue no memory instructions, so a DMA
+// queue that backs up never holds back the matrix cores.
 // ---------------------------------------------------------------------------
 namespace bf {
 
 constexpr int kBM = 256, kBN = 256;
-constexpr int kRow = 128;                            // bytes per slab row (64 bf16)
-constexpr int kSlabA = kBM * kRow, kSlabB = kBN * kRow;
-constexpr int kKS = kRow / 32;                       // 16-wide MFMA k steps per slab
+constexpr int kPRow = 64;               // bytes per panel row
+constexpr int kPanel = 256 * kPRow;     // 16 KB: one operand's share of a stage
+constexpr int kStage = 2 * kPanel;      // A panel, then B panel
+constexpr int kNBuf = 4;                // stages in the LDS ring
 
 // Wave grid WGM x WGN over the 256x256 tile; each wave owns MT x NT blocks
 // of 32x32.
@@ -280,74 +293,76 @@ struct Cfg {
   static_assert(kWaves == 8, "the ping-pong schedule and the DMA split assume 8 waves");
 };
 
-// Chunk (16 B) c of slab row r sits at r*128 + ((c ^ ((r >> 1) & 7)) << 4).
-// A ds_read_b128 is served 16 lanes at a time from 64 four-byte banks; the
-// 16 consecutive rows one pass touches then fall on 16 distinct 16-byte bank
-// groups ((r & 1) picks half of the 256-byte bank window, the swizzled chunk
-// a slot within it).
+// Chunk (16 B) c of panel row r sits at r*64 + ((c ^ ((r >> 2) & 3)) << 4).
+// A ds_read_b128 is served 16 lanes at a time from 64 four-byte banks (256
+// bytes); the 16 consecutive rows one pass reads (one chunk each) then fall
+// on 16 distinct 16-byte slots: r & 3 picks the 64-byte quarter of the bank
+// window, the swizzled chunk a slot within it.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRow + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * kPRow + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt/lgkmcnt left at max.
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Phase barrier of the ping-pong schedule. __syncthreads() would also wait
-// for every outstanding global load (its release fence covers the LDS DMA
-// writes still in flight); here each wave has already waited for the loads
-// it needs, and lgkmcnt(0) retires its LDS reads (so a buffer may be
-// refilled after the barrier). The empty asm statements keep the compiler
-// from moving memory accesses across, and the scheduling barriers keep any
-// instruction (MFMAs included) from migrating from one phase to the next.
+// Phase barrier of the ping-pong schedule: wait until at most VM of this
+// wave's vector memory operations are outstanding (63: no wait) and its LDS
+// reads have retired (so a buffer may be refilled after the barrier), then
+// s_barrier. __syncthreads() would also drain every DMA still in flight. The
+// empty asm statements keep the compiler from moving memory accesses across,
+// the scheduling barriers keep any instruction (MFMAs included) from
+// migrating between phases.
+template <int VM = 63>
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));  // vmcnt(VM) lgkmcnt(0)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One stage is 64 global_load_lds instructions of 1 KB (8 rows x 128 B, full
-// cache lines): waves 0-3 issue rows of A, waves 4-7 rows of B, 8 each.
-// Instruction i of wave w covers rows 8*jj .. 8*jj+7, jj = 8*(w % 4) + i, of
-// its operand; lane l fills LDS bytes l*16..l*16+15 of that 1 KB block: row
-// 8*jj + l/8, position l%8, which must hold chunk (l%8) ^ swizzle(row). The
-// swizzle (row >> 1) & 7 = (4*(jj & 1) + l/16) & 7 depends on jj only
-// through its parity, so a lane needs two 32-bit offsets (voff[jj & 1]); the
-// rest of the address is wave-uniform.
-struct StageSrc {
-  const char* base;  // operand rows of this wave's share, wave-uniform
-  int64_t ld_b;      // operand row pitch in bytes
-  int voff[2];       // per-lane offsets for even and odd instructions
-};
-
-__device__ __forceinline__ StageSrc stage_src(const char* P, const char* Q, int64_t ldp_b,
-                                              int64_t ldq_b, int wave, int lane) {
-  StageSrc t;
-  const bool isA = wave < 4;
-  const int jj0 = (wave & 3) * 8;
-  t.ld_b = isA ? ldp_b : ldq_b;
-  t.base = (isA ? P : Q) + (int64_t)(jj0 * 8) * t.ld_b;
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-    t.voff[par] = (int)((lane >> 3) * t.ld_b) + (((lane & 7) ^ ((4 * par + (lane >> 4)) & 7)) << 4);
-  return t;
+// phase_barrier with vmcnt(4n), n in {0, 1, 2} (wave-uniform).
+__device__ __forceinline__ void phase_barrier_n(int n) {
+  if (n >= 2) phase_barrier<8>();
+  else if (n == 1) phase_barrier<4>();
+  else phase_barrier<0>();
 }
 
-// Issue this wave's 8 loads of the stage at K offset k0_b into slab buffer
-// `buf` (A at +0, B at +kSlabA).
-__device__ __forceinline__ void issue_stage(const StageSrc& t, int wave, int64_t k0_b, char* buf) {
-  char* l = buf + (wave < 4 ? 0 : kSlabA) + (wave & 3) * 8 * 1024;
+// One wave's share of a refill: 64 rows (4 KB) of one operand panel, as 4
+// DMA instructions of 16 rows (1 KB, contiguous in the panel). Group 1
+// (waves 4-7) refills the A panels, group 0 the B panels; wave w takes rows
+// 64*(w%4) .. +63. Lane l fills LDS bytes 16l .. 16l+15 of an instruction's
+// 1 KB block: panel row l/4 of the instruction's 16, position l%4, which must
+// hold chunk (l%4) ^ ((row >> 2) & 3); for every instruction of every wave
+// (row >> 2) & 3 = (l >> 4) & 3, so the per-lane source offset is fixed.
+struct DmaSrc {
+  const char* g;  // per-lane source address of instruction 0, stage 0
+  uint32_t lds;   // LDS offset of this wave's share within a stage buffer
+};
+
+__device__ __forceinline__ DmaSrc dma_src(const char* P, const char* Q, int wave, int lane) {
+  const bool isA = wave >= 4;
+  DmaSrc d;
+  d.g = (isA ? P : Q) + (wave & 3) * 4096 + (lane >> 2) * kPRow +
+        (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  d.lds = (uint32_t)((isA ? 0 : kPanel) + (wave & 3) * 4096);
+  return d;
+}
+
+// Issue this wave's share of stage kt into the ring buffer at LDS offset
+// `buf`. Written as inline asm: the compiler then does not track these LDS
+// writes (its own tracking put full vmcnt waits in front of reads of other
+// buffers); the schedule's explicit vmcnt waits and barriers order them. The
+// instruction has no register results, so nothing in flight can land in a
+// register the compiler has reused.
+__device__ __forceinline__ void issue_share(const DmaSrc& d, int kt, uint32_t buf) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const char* g = t.base + (int64_t)(i * 8) * t.ld_b + k0_b;
-    __builtin_amdgcn_global_load_lds(g + t.voff[i & 1], (lds_ptr)(l + i * 1024), 16, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    const char* g = d.g + (int64_t)kt * kPanel + i * 1024;
+    const uint32_t m0 = buf + d.lds + i * 1024;
+    // M0 (the LDS destination) is an input operand; the s_nop covers the
+    // wait state an LDS DMA needs after M0 is written.
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
   }
 }
 
@@ -356,19 +371,19 @@ struct Frags {
   bf16x8 a[MT], b[NT];
 };
 
-// Operand fragments of 16-wide k step ks of a slab. Fragment rows are
-// (multiple of 32) + lane%32, so the swizzle depends only on the lane: lane
-// offset loff[ks] = (lane%32)*128 + (((2ks + lane/32) ^ (((lane%32) >> 1) & 7)) << 4)
-// serves every fragment of both operands; the row block is a uniform term.
+// Operand fragments of one k half of a stage. Fragment rows are (multiple
+// of 32) + lane%32, so the swizzle depends only on the lane: the lane offset
+// loff = (lane%32)*64 + ((c ^ ((lane%32 >> 2) & 3)) << 4), with chunk
+// c = 2h + lane/32, serves every fragment of both operands.
 template <int MT, int NT>
 __device__ __forceinline__ void load_frags(const char* la, const char* lb, int wm0, int wn0,
                                            int loff, Frags<MT, NT>& f) {
-  const char* pa = la + wm0 * kRow + loff;
-  const char* pb = lb + wn0 * kRow + loff;
+  const char* pa = la + wm0 * kPRow + loff;
+  const char* pb = lb + wn0 * kPRow + loff;
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * kRow);
+  for (int mi = 0; mi < MT; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * kPRow);
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni) f.b[ni] = *reinterpret_cast<const bf16x8*>(pb + ni * 32 * kRow);
+  for (int ni = 0; ni < NT; ++ni) f.b[ni] = *reinterpret_cast<const bf16x8*>(pb + ni * 32 * kPRow);
 }
 
 template <int MT, int NT>
@@ -461,40 +476,39 @@ __device__ __forceinline__ void quad_transpose(uint32_t& d0, uint32_t& d1, int l
 // Main loop of one group of the ping-pong schedule (see k_ns_gemm_bf16).
 // Both groups execute the same sequence of barriers; G selects the role.
 //
-// Plain bf16: a slab is 64 logical k; chunk ch holds k steps 2ch and 2ch+1
-// (fragments fa, fb); each 32x32 block takes 2 MFMAs per chunk.
-// SPLIT (split-bf16 operands, each 128-byte slab row = 32 hi + 32 lo values
-// of 32 logical k): chunk ch is k step ch, fa its hi and fb its lo
-// fragments; each block takes hi*hi + hi*lo + lo*hi (3 MFMAs per chunk).
+// A stage is one panel per operand: 32 logical k for bf16 (two 16-wide k
+// steps: fragments fa and fb, 2 MFMAs per 32x32 block), 16 for split bf16
+// (one k step: fa holds the hi, fb the lo parts; 3 MFMAs per block,
+// hi*hi + hi*lo + lo*hi, the small terms first).
 //
 // With E_TERM, the fp32 term seed*E (apply: E = X, seed = a; polynomial:
 // E = A, seed = b/c) is added to the accumulators on the way: element
 // (i, j) of E is element (j, i) of the Q operand (X^T, or A itself, which
 // is symmetric), so the E tile streams through the LDS ring as part of Q's
-// slabs with k in [256*bi, 256*bi + 256). When a wave loads a chunk of that
-// K range, it also reads, for the accumulator rows the chunk covers, its 4
+// panels with k in [256*bi, 256*bi + 256). When a wave loads a stage of that
+// K range, it also reads, for the accumulator rows the stage covers, their 4
 // consecutive k values per column (one 8-byte LDS read per 4 elements, two
-// with SPLIT: E = hi + lo).
+// with split operands: E = hi + lo).
 template <int G, int MT, int NT, bool E_TERM, bool SPLIT>
-__device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int nk, char* s0,
-                                         char* s1, int wm0, int wn0, const int (&loff)[bf::kKS],
-                                         int lane, int bi, float seed, f32x16 (&acc)[MT][NT]) {
+__device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, int nk, const char* ring,
+                                         uint32_t ring_lds, int wm0, int wn0,
+                                         const int (&loff)[2], int lane, int bi, float seed,
+                                         f32x16 (&acc)[MT][NT]) {
   using namespace bf;
-  constexpr int kW = SPLIT ? 16 : 32;   // logical k per chunk
-  constexpr int kSW = SPLIT ? 32 : 64;  // logical k per slab
+  constexpr int kW = SPLIT ? 16 : 32;  // logical k per stage
   Frags<MT, NT> fa, fb;
-  auto take_e = [&](const char* buf, int kt, int ch) {
-    // first accumulator row (relative to wm0) whose E value sits in this chunk
-    const int r = kt * kSW + ch * kW - 256 * bi - wm0;
+  auto take_e = [&](const char* buf, int kt) {
+    // first accumulator row (relative to wm0) whose E value sits in this stage
+    const int r = kt * kW - 256 * bi - wm0;
     if (r < 0 || r >= MT * 32) return;
-    const char* lb = buf + kSlabA;
+    const char* lb = buf + kPanel;
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int row = mi * 32 + 8 * rg;  // rows row + 4*(lane/32) + q, q < 4
         if (row < r || row >= r + kW) continue;
-        const int kk = ch * kW + (row - r) + 4 * (lane >> 5);  // logical k within the slab
+        const int kk = (row - r) + 4 * (lane >> 5);  // logical k within the stage
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) {
           const int qrow = wn0 + ni * 32 + (lane & 31);
@@ -504,8 +518,8 @@ __device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int 
 #pragma unroll
           for (int q = 0; q < 4; ++q) e[q] = (float)hv[q];
           if (SPLIT) {
-            const bf16x4 lv =
-                *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, 4 + (kk >> 3)) + ((kk & 7) << 1));
+            const bf16x4 lv = *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, 2 + (kk >> 3)) +
+                                                               ((kk & 7) << 1));
 #pragma unroll
             for (int q = 0; q < 4; ++q) e[q] += (float)lv[q];
           }
@@ -515,10 +529,11 @@ __device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int 
         }
       }
   };
-  auto load = [&](const char* buf, int ch, int kt) {
-    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[SPLIT ? ch : 2 * ch], fa);
-    load_frags<MT, NT>(buf, buf + kSlabA, wm0, wn0, loff[SPLIT ? ch + 2 : 2 * ch + 1], fb);
-    if (E_TERM) take_e(buf, kt, ch);
+  auto load = [&](int kt) {
+    const char* buf = ring + (kt & (kNBuf - 1)) * kStage;
+    load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, loff[0], fa);
+    load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, loff[1], fb);
+    if (E_TERM) take_e(buf, kt);
   };
   auto mul = [&]() {
     if (SPLIT) {
@@ -535,28 +550,33 @@ __device__ __forceinline__ void pingpong(const bf::StageSrc& src, int wave, int 
       mfma_frags<MT, NT>(fb, acc);
     }
   };
-  // phase 0: group 0 loads chunk 0 of stage 0
-  if (G == 0) load(s0, 0, 0);
-  phase_barrier();
-  auto stage = [&](int kt, char* buf, char* nxt) {
-    if (G == 0) mul(); else load(buf, 0, kt);                   // 4s+1
-    phase_barrier();
-    if (G == 0) load(buf, 1, kt); else mul();                   // 4s+2
-    phase_barrier();
-    if (G == 0) mul(); else load(buf, 1, kt);                   // 4s+3
-    wait_vmcnt<0>();
-    phase_barrier();
-    if (kt + 2 < nk) issue_stage(src, wave, (int64_t)(kt + 2) * kRow, buf);  // 4s+4
+  auto refill = [&](int kt) { issue_share(dsrc, kt, ring_lds + (kt & (kNBuf - 1)) * kStage); };
+  // Phase 0: group 0 loads stage 0. Then per stage s:
+  //   2s+1: g0 multiplies stage s; g1 loads stage s, then refills its half of
+  //         stage s+3 (buffer of stage s-1, read by both groups before). At
+  //         the end every wave waits for its share of stage s+1: the only
+  //         refills it issued after that share are those of s+2 and s+3.
+  //   2s+2: g0 loads stage s+1, then refills its half of stage s+4 (buffer of
+  //         stage s, read by g1 in 2s+1); g1 multiplies stage s.
+  // Stages 0-3 are issued before the loop; refills of stage t are issued in
+  // phases 2t-6 (B half) and 2t-5 (A half) and waited for at the end of 2t-1.
+  if (G == 0) load(0);
+  phase_barrier<>();
+  for (int s = 0; s < nk; ++s) {
     if (G == 0) {
-      if (kt + 1 < nk) load(nxt, 0, kt + 1);
+      mul();
+    } else {
+      load(s);
+      if (s >= 1 && s + 3 < nk) refill(s + 3);
+    }
+    phase_barrier_n((s + 2 < nk) + (s + 3 < nk));
+    if (G == 0) {
+      if (s + 1 < nk) load(s + 1);
+      if (s + 4 < nk) refill(s + 4);
     } else {
       mul();
     }
-    phase_barrier();
-  };
-  for (int kt = 0; kt < nk; kt += 2) {
-    stage(kt, s0, s1);
-    stage(kt + 1, s1, s0);
+    phase_barrier<>();
   }
 }
 
@@ -566,8 +586,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   using C = Cfg<WGM, WGN>;
   constexpr int kWGN = WGN, kWTM = C::kWTM, kWTN = C::kWTN, kMT = C::kMT, kNT = C::kNT;
   constexpr bool kSym = (MODE != kApply);
-  __shared__ __attribute__((aligned(1024))) char s0[kSlabA + kSlabB];
-  __shared__ __attribute__((aligned(1024))) char s1[kSlabA + kSlabB];
+  __shared__ __attribute__((aligned(1024))) char ring[kNBuf * kStage];
 
   const int tid = threadIdx.x;
   // The wave index is uniform across a wave; readfirstlane lets the compiler
@@ -583,11 +602,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   tile_coords<kSym>(g, local - mat * g.tiles_per_mat, bi, bj);
 
   const char* blk = g.base + (int64_t)mat * g.mat_bytes;
-  // Row pitch in bytes: 2 per logical element, 4 with split operands.
+  // Bytes per logical element: 2, or 4 with split operands (hi + lo). A row
+  // block of 256 rows is ld * 256 * kEB bytes of consecutive panels.
   constexpr int kEB = SPLIT ? 4 : 2;
-  const int64_t ldp_b = (int64_t)g.ldp * kEB, ldq_b = (int64_t)g.ldq * kEB;
-  const char* P = blk + g.offP + (int64_t)bi * kBM * ldp_b;
-  const char* Q = blk + g.offQ + (int64_t)bj * kBN * ldq_b;
+  constexpr int kPK = SPLIT ? 16 : 32;  // logical k per panel
+  const char* P = blk + g.offP + (int64_t)bi * kBM * g.ldp * kEB;
+  const char* Q = blk + g.offQ + (int64_t)bj * kBN * g.ldq * kEB;
 
   f32x16 acc[kMT][kNT];
 #pragma unroll
@@ -595,46 +615,34 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 #pragma unroll
     for (int ni = 0; ni < kNT; ++ni) acc[mi][ni] = f32x16{};
 
-  const int nk = g.K / (SPLIT ? 32 : 64);  // slabs; even, since K is a multiple of kPad
+  const int nk = g.K / kPK;  // stages; a multiple of 8, since K is a multiple of kPad
   const int wm0 = wm * kWTM, wn0 = wn * kWTN;
-  // Ping-pong schedule. Stage s (a 64-wide K slab, full 128-byte rows) lives
-  // in buffer s % 2 and is consumed in two chunks of two 16-wide k steps.
-  // Waves 0-3 (group 0) and 4-7 (group 1) -- one of each per SIMD -- take
-  // turns: in every phase one group issues a cluster of 16 MFMAs while the
-  // other loads its next chunk's fragments from LDS, so each SIMD's matrix
-  // core always has a wave feeding it. Phases are separated by barriers.
-  // Phase 0: g0 loads chunk 0 of stage 0. Then per stage s:
-  //   4s+1: g0 multiplies chunk 0, g1 loads chunk 0
-  //   4s+2: g0 loads chunk 1, g1 multiplies chunk 0
-  //   4s+3: g0 multiplies chunk 1, g1 loads chunk 1; every wave then waits
-  //         for its loads of stage s+1, so the next barrier publishes it
-  //   4s+4: loads of stage s+2 into buffer s % 2 (last read in 4s+3);
-  //         g0 loads chunk 0 of stage s+1, g1 multiplies chunk 1.
-  // Stage s+2's loads thus have one stage of time to land.
-  int loff[kKS];
+  int loff[2];
   {
-    const int r = lane & 31, y = (lane >> 5) ^ ((r >> 1) & 7);
+    const int r = lane & 31, f = (r >> 2) & 3;
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) loff[ks] = r * kRow + (((2 * ks) ^ y) << 4);
+    for (int h = 0; h < 2; ++h) loff[h] = r * kPRow + (((2 * h + (lane >> 5)) ^ f) << 4);
   }
-  const StageSrc src = stage_src(P, Q, ldp_b, ldq_b, wave, lane);
-  issue_stage(src, wave, 0, s0);
-  issue_stage(src, wave, kRow, s1);
-  wait_vmcnt<8>();
-  phase_barrier();
+  const DmaSrc dsrc = dma_src(P, Q, wave, lane);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
+#pragma unroll
+  for (int st = 0; st < kNBuf; ++st) issue_share(dsrc, st, ring_lds + st * kStage);
+  phase_barrier<12>();  // this wave's share of stage 0 has landed
   const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
   if (wave < 4)
-    pingpong<0, kMT, kNT, MODE != kGram, SPLIT>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi,
-                                                seed, acc);
+    pingpong<0, kMT, kNT, MODE != kGram, SPLIT>(dsrc, nk, ring, ring_lds, wm0, wn0, loff, lane,
+                                                bi, seed, acc);
   else
-    pingpong<1, kMT, kNT, MODE != kGram, SPLIT>(src, wave, nk, s0, s1, wm0, wn0, loff, lane, bi,
-                                                seed, acc);
+    pingpong<1, kMT, kNT, MODE != kGram, SPLIT>(dsrc, nk, ring, ring_lds, wm0, wn0, loff, lane,
+                                                bi, seed, acc);
 
   // ---- epilogue. The E term is already in the accumulators (the
-  // polynomial's still needs its factor c). Outputs leave through the idle
-  // LDS ring, one 256x256 bf16 pass per layout (row-major, then transposed;
-  // with SPLIT one pass for the hi and one for the lo parts of each) so
-  // that every global store is a coalesced 16-byte store.
+  // polynomial's still needs its factor c). Every refill has landed (the last
+  // wait of the main loop was vmcnt(0)). Outputs leave through the idle LDS
+  // ring, one 256x256 bf16 pass per layout (row-major, then transposed; with
+  // split operands one pass for the hi and one for the lo parts of each):
+  // the tile's panels are one contiguous region of the output, written with
+  // coalesced 16-byte stores.
   const float scale = MODE == kPoly ? args.c1 : 1.f;
   bf16x4 vh[kMT][kNT][4], vl[kMT][kNT][4];
 #pragma unroll
@@ -654,24 +662,41 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
         if (SPLIT) vl[mi][ni][rg] = l;
       }
 
-  // The two 64 KB ring buffers hold 128 rows of 512 B each of the staging
-  // tile; ring(q) is the 32 KB quarter holding rows [64q, 64q + 64).
-  auto ring = [&](int q) -> char* { return (q < 2 ? s0 : s1) + (q & 1) * 32768; };
+  // The ring holds the 256 x 512 B staging tile: buffer q (32 KB) holds rows
+  // [64q, 64q + 64).
+  char* stg = const_cast<char*>(ring);
+  auto srow = [&](int row) -> char* { return stg + (row >> 6) * kStage + (row & 63) * 512; };
   char* O1 = g.offO1 < 0 ? nullptr : const_cast<char*>(blk) + g.offO1;
   char* O2 = g.offO2 < 0 ? nullptr : const_cast<char*>(blk) + g.offO2;
   char* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;  // transposed destination
-  const int64_t ld1_b = (int64_t)g.ldo1 * kEB, ldT_b = (int64_t)(kSym ? g.ldo1 : g.ldo2) * kEB;
-  // Byte offset, within a row, of the 16-byte chunk holding logical columns
-  // col .. col+7 (col a multiple of 8): plain rows are dense bf16; split rows
-  // are 128-byte blocks of 32 hi then 32 lo values.
-  auto col_off = [&](int col, bool lo) -> int64_t {
-    if (!SPLIT) return (int64_t)col * 2;
-    return (int64_t)(col >> 5) * 128 + ((col & 31) << 1) + (lo ? 64 : 0);
+  const int ldT = kSym ? g.ldo1 : g.ldo2;
+  // Store a staged 256x256 tile to the panels of output rows 256*rb .. +255,
+  // logical columns 256*cb .. +255, of a matrix with ld logical columns.
+  auto store_tile = [&](char* O, int ld, int rb, int cb, bool lo) {
+    char* region = O + (int64_t)rb * kBM * ld * kEB + (int64_t)cb * (256 / kPK) * kPanel;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = tid + i * C::kThreads;  // 16-byte chunk 0 .. 8191
+      int row, c;
+      char* dst;
+      if (!SPLIT) {  // 8 panels of 256 rows x 64 B: the region is linear in id
+        row = (id & 1023) >> 2;
+        c = ((id >> 10) << 2) | (id & 3);
+        dst = region + (int64_t)id * 16;
+      } else {  // 16 panels; this pass fills the hi (or lo) 32 B of each row
+        const int p = id >> 9, q = id & 511;
+        row = q >> 1;
+        c = (p << 1) | (q & 1);
+        dst = region + (int64_t)p * kPanel + row * kPRow + ((q & 1) << 4) + (lo ? 32 : 0);
+      }
+      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ (row & 31)) << 4));
+      *reinterpret_cast<u32x4*>(dst) = d;
+    }
   };
 
-  // Row-major pass into O1: LDS tile [row][col], 16-byte chunk c of row r
-  // stored at position c ^ (r & 31). A quad transpose first gives each lane
-  // 4 consecutive columns of one row, so the LDS writes are 8-byte writes.
+  // Row-major pass: LDS tile [row][col], 16-byte chunk c of row r stored at
+  // position c ^ (r & 31). A quad transpose first gives each lane 4
+  // consecutive columns of one row, so the LDS writes are 8-byte writes.
   auto pass_rows = [&](const bf16x4 (&v)[kMT][kNT][4], bool lo) {
     __syncthreads();
 #pragma unroll
@@ -688,24 +713,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
           quad_transpose(d0, d1, lane);
           d.x = d0;
           d.y = d1;
-          char* base = ring(row >> 6) + (row & 63) * 512;
           const int off = ((((col >> 3) ^ (row & 31)) << 4) | ((col & 7) << 1));
-          *reinterpret_cast<u32x2*>(base + off) = d;
+          *reinterpret_cast<u32x2*>(srow(row) + off) = d;
         }
       }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int id = tid + i * C::kThreads;  // 0 .. 8191
-      const int row = id >> 5, c = id & 31;
-      const u32x4 d = *reinterpret_cast<const u32x4*>(ring(row >> 6) + (row & 63) * 512 +
-                                                      ((c ^ (row & 31)) << 4));
-      *reinterpret_cast<u32x4*>(O1 + (int64_t)(bi * kBM + row) * ld1_b +
-                                col_off(bj * kBN + c * 8, lo)) = d;
-    }
+    store_tile(O1, g.ldo1, bi, bj, lo);
   };
-  // Transposed pass into OT: LDS tile [col][row], 16-byte chunk c of LDS
-  // row j stored at position c ^ (j & 31).
+  // Transposed pass: LDS tile [col][row], 16-byte chunk c of LDS row j
+  // stored at position c ^ (j & 31).
   auto pass_cols = [&](const bf16x4 (&v)[kMT][kNT][4], bool lo) {
     __syncthreads();
 #pragma unroll
@@ -713,7 +729,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 #pragma unroll
       for (int ni = 0; ni < kNT; ++ni) {
         const int col = wn0 + ni * 32 + (lane & 31);
-        char* base = ring(col >> 6) + (col & 63) * 512;
+        char* base = srow(col);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int row0 = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5);
@@ -722,15 +738,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
         }
       }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int id = tid + i * C::kThreads;
-      const int j = id >> 5, c = id & 31;
-      const u32x4 d = *reinterpret_cast<const u32x4*>(ring(j >> 6) + (j & 63) * 512 +
-                                                      ((c ^ (j & 31)) << 4));
-      *reinterpret_cast<u32x4*>(OT + (int64_t)(bj * kBN + j) * ldT_b +
-                                col_off(bi * kBM + c * 8, lo)) = d;
-    }
+    store_tile(OT, ldT, bj, bi, lo);
   };
   if (O1) {
     pass_rows(vh, false);
