@@ -218,8 +218,9 @@ struct Fmt<kFp32> {
 
 // --------------------------------------------------------------------------
 // X0 = M / (||M|| + eps): one 64x64 tile of the padded rp x cp domain per
-// block; written straight to D and transposed (through LDS) to E. Entries
-// outside rows x cols are written as zero.
+// block; written straight to D and/or transposed (through LDS) to E (an
+// offset of -1 skips that output). Entries outside rows x cols are written
+// as zero.
 // --------------------------------------------------------------------------
 template <int F>
 __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* const* M,
@@ -245,8 +246,9 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
     float v = 0.f;
     if (r < g.rows && c < g.cols) v = mp[(int64_t)r * g.cols + c] * scale;
     tile[rr][tx] = v;
-    Fmt<F>::store(D, r, c, g.cp, v);
+    if (g.offD >= 0) Fmt<F>::store(D, r, c, g.cp, v);
   }
+  if (g.offE < 0) return;
   __syncthreads();
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {

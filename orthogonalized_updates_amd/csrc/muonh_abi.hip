@@ -54,7 +54,11 @@ struct GroupPlan {
   int64_t n;            // rows * cols
   int64_t off;          // workspace byte offset of the group's first matrix block
   int64_t mat_bytes;    // bytes per matrix block
-  int64_t offX, offXt[2], offA, offB;
+  // Offsets within a matrix block. bf16 and split operands keep one layout of
+  // X (s x l) in two buffers that alternate between iterations (offXs; the
+  // apply reads X K-major); the fp32 debug kernel keeps X and two copies of
+  // X^T (offX, offXt). A and B are s x s.
+  int64_t offXs[2], offX, offXt[2], offA, offB;
   int bpm;              // streaming blocks per matrix
 };
 
@@ -92,9 +96,20 @@ bool check_ws(const muonh_plan* p, const void* ws, size_t bytes, int* err) {
   return true;
 }
 
+// Where O, the update of the last step, sits: in the matrix's own
+// orientation (rows x cols, padded), for every group.
+int64_t off_update(const muonh_plan* p, const GroupPlan& G) {
+  if (p->prec != kFp32) return G.offXs[1];
+  return G.trans ? G.offXt[0] : G.offX;
+}
+
 // Streaming (bpm blocks per matrix) or tile (64x64 tiles of the padded
 // domain) launch descriptors, in batches of at most kMaxEwGroups groups.
-std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final_xt) {
+// ns_iters < 0: D is O (the update and projection read it); otherwise D and
+// E are what the normalising cast writes before ns_iters iterations: X0 in
+// the buffer the first iteration reads (own orientation in D, transposed in
+// E, -1 where nothing is written); with 0 iterations, O itself.
+std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int ns_iters) {
   std::vector<EwArgs> out;
   const size_t ng = p->groups.size();
   for (size_t g0 = 0; g0 < ng; g0 += kMaxEwGroups) {
@@ -117,11 +132,24 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final
       const int cp = G.trans ? G.sp : G.lp;
       e.rp = rp;
       e.cp = cp;
-      // D holds the matrix's own orientation: X for wide matrices, X^T for
-      // tall ones; E the other layout.
-      const int64_t xt = G.offXt[final_xt];
-      e.offD = G.trans ? xt : G.offX;
-      e.offE = G.trans ? G.offX : xt;
+      // D holds the matrix's own orientation, E the transposed one.
+      if (ns_iters < 0) {
+        e.offD = off_update(p, G);
+        e.offE = -1;
+      } else if (p->prec == kFp32) {
+        // X, and the X^T copy that the last apply lands in copy 0 from
+        const int64_t xt = G.offXt[ns_iters & 1];
+        e.offD = G.trans ? xt : G.offX;
+        e.offE = G.trans ? G.offX : xt;
+      } else if (ns_iters == 0) {
+        e.offD = G.offXs[1];
+        e.offE = -1;
+      } else {
+        // X0 (s x l) in the buffer from which the last apply lands in buffer 1
+        const int64_t x0 = G.offXs[1 - (ns_iters & 1)];
+        e.offD = G.trans ? -1 : x0;
+        e.offE = G.trans ? x0 : -1;
+      }
       e.tiles_per_mat = (rp / 64) * (cp / 64);
       e.block_begin = (int)blocks;
       blocks += (int64_t)G.count * (tiles ? e.tiles_per_mat : G.bpm);
@@ -136,6 +164,9 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int final
 // GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
 std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters) {
   const int T = gemm_tile(p->prec);
+  // bf16 / split: the buffer iteration `it` reads X from (X0 goes to buffer
+  // 1 - iters%2, so that the last apply writes buffer 1)
+  const int src = (1 - (iters & 1)) ^ (it & 1);
   std::vector<GemmGroup> all;
   for (const GroupPlan& G : p->groups) {
     GemmGroup q;
@@ -145,8 +176,9 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     q.count = G.count;
     q.offE = q.offO1 = q.offO2 = -1;
     const int ts = G.sp / T, tl = G.lp / T;
+    const int64_t xcur = p->prec == kFp32 ? G.offX : G.offXs[src];
     if (mode == kGram) {
-      q.offP = q.offQ = G.offX;
+      q.offP = q.offQ = xcur;
       q.ldp = q.ldq = G.lp;
       q.K = G.lp;
       q.tm = q.tn = ts;
@@ -163,6 +195,28 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
       q.lde = G.sp;
       q.offO1 = G.offB;
       q.ldo1 = G.sp;
+    } else if (p->prec != kFp32) {
+      // X (s x l) from buffer src to buffer 1 - src; the last iteration
+      // writes O in the matrix's own orientation into buffer 1.
+      const bool last = it == iters - 1;
+      const int64_t xin = G.offXs[src], xout = G.offXs[1 - src];
+      q.offP = G.offB;
+      q.ldp = G.sp;
+      q.offQ = xin;  // read K-major (k along X's rows)
+      q.ldq = G.lp;
+      q.K = G.sp;
+      q.tm = ts;
+      q.tn = tl;
+      q.tiles_per_mat = ts * tl;
+      q.offE = xin;
+      q.lde = G.lp;
+      if (last && G.trans) {
+        q.offO2 = xout;
+        q.ldo2 = G.sp;
+      } else {
+        q.offO1 = xout;
+        q.ldo1 = G.lp;
+      }
     } else {
       const bool last = it == iters - 1;
       const int xin = (iters - it) & 1, xout = (iters - 1 - it) & 1;
@@ -297,7 +351,8 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   }
 
   // Workspace: norm partials, two per-matrix norm arrays, then per group the
-  // matrix blocks [X | X^T (two copies) | A | B].
+  // matrix blocks [X buffer 0 | X buffer 1 | A | B] (fp32: [X | X^T (two
+  // copies) | A | B]).
   int64_t off = 0;
   p->off_partials = off;
   off = round_up(off + n_mats * kMaxPartials * (int64_t)sizeof(double), 256);
@@ -326,12 +381,13 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
     const int64_t e = p->esize;
     const int64_t xs = round_up((int64_t)G.sp * G.lp * e, 256);
     const int64_t ss = round_up((int64_t)G.sp * G.sp * e, 256);
-    G.offX = 0;
-    G.offXt[0] = xs;
+    const int nx = p->prec == kFp32 ? 3 : 2;  // s x l buffers per matrix
+    G.offXs[0] = G.offX = 0;
+    G.offXs[1] = G.offXt[0] = xs;
     G.offXt[1] = 2 * xs;
-    G.offA = 3 * xs;
-    G.offB = 3 * xs + ss;
-    G.mat_bytes = 3 * xs + 2 * ss;
+    G.offA = nx * xs;
+    G.offB = nx * xs + ss;
+    G.mat_bytes = nx * xs + 2 * ss;
     G.off = off;
     off += G.mat_bytes * d.count;
     int64_t bpm = (G.n + kElemsPerBlock - 1) / kElemsPerBlock;
@@ -363,7 +419,7 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
   double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
   double* norms = reinterpret_cast<double*>(ws + plan->off_norm_w);
   hipError_t e;
-  for (const EwArgs& a : make_ew(plan, ws, false, 0)) {
+  for (const EwArgs& a : make_ew(plan, ws, false, -1)) {
     if ((e = launch_sumsq(a, W, partials, s)) != hipSuccess) return hip_fail(e, "init sumsq");
     if ((e = launch_finalize(a, partials, norms, R, s)) != hipSuccess)
       return hip_fail(e, "init finalize");
@@ -400,7 +456,6 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
   double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
   double* norm_m = reinterpret_cast<double*>(ws + plan->off_norm_m);
   double* norm_w = reinterpret_cast<double*>(ws + plan->off_norm_w);
-  const int x0 = ns_iters & 1;  // X^T copy that receives X0^T; the last apply lands in copy 0
   hipError_t e;
   int ev = 0;
   auto mark = [&]() -> hipError_t {
@@ -408,8 +463,8 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
     return hipEventRecord(reinterpret_cast<hipEvent_t>(events[ev++]), s);
   };
 
-  const std::vector<EwArgs> stream_args = make_ew(plan, ws, false, 0);
-  const std::vector<EwArgs> tile_args = make_ew(plan, ws, true, x0);
+  const std::vector<EwArgs> stream_args = make_ew(plan, ws, false, -1);
+  const std::vector<EwArgs> tile_args = make_ew(plan, ws, true, ns_iters);
 
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
   for (const EwArgs& a : stream_args) {
@@ -481,7 +536,7 @@ int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const v
   for (const GroupPlan& g : plan->groups)
     if (index >= g.first && index < g.first + g.count) G = &g;
   const char* blk = static_cast<const char*>(workspace) + G->off + (index - G->first) * G->mat_bytes;
-  const char* D = blk + (G->trans ? G->offXt[0] : G->offX);
+  const char* D = blk + off_update(plan, *G);
   const int ld = G->trans ? G->sp : G->lp;
   hipError_t e = launch_read_update(plan->prec, D, ld, G->rows, G->cols, dst,
                                     reinterpret_cast<hipStream_t>(stream));

@@ -46,10 +46,10 @@ struct EwGroup {
   // Newton-Schulz buffers of matrix m live at ns_base + m * mat_bytes.
   char* ns_base;
   int64_t mat_bytes;
-  // Layouts in the matrix's own orientation: D is rows x cols with leading
-  // dimension cp (holds X0 for wide matrices, X0^T for tall ones, and the
-  // final update O in both cases); E is its transpose, cols x rows with
-  // leading dimension rp.
+  // Byte offsets (-1: absent) of a matrix in its own orientation, D (rows x
+  // cols, leading dimension cp), and transposed, E (cols x rows, leading
+  // dimension rp). The cast writes X0 to one or both; the update and the
+  // projection read the final O from D.
   int64_t offD, offE;
   int rp, cp;           // padded rows / cols
   int tiles_per_mat;    // 64x64 tiles of the padded rp x cp domain

@@ -366,6 +366,67 @@ __device__ __forceinline__ void issue_share(const DmaSrc& d, int kt, uint32_t bu
   }
 }
 
+// Q operand of the apply (QT: Q is X itself, read K-major). A stage holds
+// rows k in [kPK*kt, kPK*kt + kPK) of X and the tile's 256 columns: 256/kPK
+// pieces of kPK rows x 64 bytes, one per column panel, each contiguous in X
+// (kPK*64 = 2 KB for bf16, 1 KB for split). Piece p lands at p*kPK*64 in the
+// stage's B panel, rows unswizzled: a transposed fragment read (4 rows x 16
+// columns per 16 lanes) then covers whole 256-byte bank windows. In split
+// mode the two 16-lane groups of a read fall on consecutive pieces, so odd
+// pieces store their two 32-byte halves swapped (chunk ^ 2) to keep the two
+// groups on different banks. Group 0 refills these; wave w takes the 16
+// 1 KB instructions 4*(w%4) .. 4*(w%4)+3 of the stage.
+struct QtSrc {
+  const char* g[2];  // per-lane source of even / odd instructions, tile column block included
+  int64_t rbs;       // bytes per 256-row block of X
+  uint32_t lds;      // LDS offset of this wave's instructions within a stage buffer
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ QtSrc qt_src(const char* X, int ldx, int bj, int wave, int lane) {
+  constexpr int kPK = SPLIT ? 16 : 32;
+  QtSrc d;
+  const char* base = X + (int64_t)bj * (256 / kPK) * kPanel;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int lo = SPLIT ? (lane >> 2) * kPRow + (((lane & 3) ^ (2 * par)) << 4) : lane * 16;
+    d.g[par] = base + lo;
+  }
+  d.rbs = (int64_t)(ldx / kPK) * kPanel;
+  d.lds = (uint32_t)(kPanel + (wave & 3) * 4096);
+  return d;
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void issue_share_qt(const QtSrc& d, int wave, int kt, uint32_t buf) {
+  constexpr int kPK = SPLIT ? 16 : 32;
+  const int k0 = kt * kPK;
+  const int64_t row_part = (int64_t)(k0 >> 8) * d.rbs + (k0 & 255) * kPRow;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * (wave & 3) + i;  // instruction of the stage
+    // bf16: piece j/2, its half j%2 (16 rows each); split: piece j
+    const int64_t piece = SPLIT ? (int64_t)j * kPanel : (int64_t)(j >> 1) * kPanel + (j & 1) * 1024;
+    const char* g = d.g[i & 1] + row_part + piece;
+    const uint32_t m0 = buf + d.lds + i * 1024;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0) : "memory");
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+// ds_read_b64_tr_b16: in each 16-lane group, lanes 4r .. 4r+3 name row r's
+// 16 consecutive values (4 each); lane i receives column i of the 4 rows.
+__device__ __forceinline__ bf16x4 read_tr(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(lds_ptr)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 x, bf16x4 y) {
+  return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
 template <int MT, int NT>
 struct Frags {
   bf16x8 a[MT], b[NT];
@@ -384,6 +445,19 @@ __device__ __forceinline__ void load_frags(const char* la, const char* lb, int w
   for (int mi = 0; mi < MT; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * kPRow);
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni) f.b[ni] = *reinterpret_cast<const bf16x8*>(pb + ni * 32 * kPRow);
+}
+
+// B fragments of a QT stage (see qt_src): lane l needs 8 consecutive k of
+// column n = (wn0 + 32 ni) + l%32, k = 8*(l/32) + 16h (bf16, k half h) or
+// 8*(l/32) (split: h = 0 hi, h = 1 lo). Two transposed reads give k .. k+3
+// and k+4 .. k+7; qoff[h] is the lane's part of the address.
+template <int NT, bool SPLIT>
+__device__ __forceinline__ void load_frags_qt(const char* lb, int wn0, int qoff, bf16x8 (&b)[NT]) {
+#pragma unroll
+  for (int ni = 0; ni < NT; ++ni) {
+    const char* p = lb + (SPLIT ? ((wn0 + 32 * ni) >> 4) * 1024 : ((wn0 + 32 * ni) >> 5) * 2048) + qoff;
+    b[ni] = cat8(read_tr(p), read_tr(p + 4 * kPRow));
+  }
 }
 
 template <int MT, int NT>
@@ -489,10 +563,17 @@ __device__ __forceinline__ void quad_transpose(uint32_t& d0, uint32_t& d1, int l
 // K range, it also reads, for the accumulator rows the stage covers, their 4
 // consecutive k values per column (one 8-byte LDS read per 4 elements, two
 // with split operands: E = hi + lo).
-template <int G, int MT, int NT, bool E_TERM, bool SPLIT>
-__device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, int nk, const char* ring,
-                                         uint32_t ring_lds, int wm0, int wn0,
-                                         const int (&loff)[2], int lane, int bi, float seed,
+// Lane parts of the LDS addresses a wave reads (see k_ns_gemm_bf16).
+struct LaneOffs {
+  int f[2];   // A fragments (and B fragments unless QT), k half / hi-lo h
+  int q[2];   // QT: transposed B fragment reads, h as above
+  int e[2];   // QT: transposed E reads, hi and lo
+};
+
+template <int G, int MT, int NT, bool E_TERM, bool SPLIT, bool QT>
+__device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, const bf::QtSrc& qsrc, int nk,
+                                         const char* ring, uint32_t ring_lds, int wave, int wm0,
+                                         int wn0, const LaneOffs& lo, int lane, int bi, float seed,
                                          f32x16 (&acc)[MT][NT]) {
   using namespace bf;
   constexpr int kW = SPLIT ? 16 : 32;  // logical k per stage
@@ -508,20 +589,35 @@ __device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, int nk, const c
       for (int rg = 0; rg < 4; ++rg) {
         const int row = mi * 32 + 8 * rg;  // rows row + 4*(lane/32) + q, q < 4
         if (row < r || row >= r + kW) continue;
-        const int kk = (row - r) + 4 * (lane >> 5);  // logical k within the stage
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) {
-          const int qrow = wn0 + ni * 32 + (lane & 31);
-          const bf16x4 hv =
-              *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, kk >> 3) + ((kk & 7) << 1));
           float e[4];
+          if (QT) {
+            // E = X: stage row k = accumulator row, read 4 rows of the lane's
+            // column with one transposed read (two with split operands)
+            const char* pe = lb + (SPLIT ? ((wn0 + 32 * ni) >> 4) * 1024 : ((wn0 + 32 * ni) >> 5) * 2048) +
+                             (row - r) * kPRow;
+            const bf16x4 hv = read_tr(pe + lo.e[0]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) e[q] = (float)hv[q];
-          if (SPLIT) {
-            const bf16x4 lv = *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, 2 + (kk >> 3)) +
-                                                               ((kk & 7) << 1));
+            for (int q = 0; q < 4; ++q) e[q] = (float)hv[q];
+            if (SPLIT) {
+              const bf16x4 lv = read_tr(pe + lo.e[1]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) e[q] += (float)lv[q];
+              for (int q = 0; q < 4; ++q) e[q] += (float)lv[q];
+            }
+          } else {
+            const int kk = (row - r) + 4 * (lane >> 5);  // logical k within the stage
+            const int qrow = wn0 + ni * 32 + (lane & 31);
+            const bf16x4 hv =
+                *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, kk >> 3) + ((kk & 7) << 1));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) e[q] = (float)hv[q];
+            if (SPLIT) {
+              const bf16x4 lv = *reinterpret_cast<const bf16x4*>(
+                  lb + bf::swz(qrow, 2 + (kk >> 3)) + ((kk & 7) << 1));
+#pragma unroll
+              for (int q = 0; q < 4; ++q) e[q] += (float)lv[q];
+            }
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -531,8 +627,19 @@ __device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, int nk, const c
   };
   auto load = [&](int kt) {
     const char* buf = ring + (kt & (kNBuf - 1)) * kStage;
-    load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, loff[0], fa);
-    load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, loff[1], fb);
+    if (QT) {
+      const char* pa = buf + wm0 * kPRow;
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        fa.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * kPRow + lo.f[0]);
+        fb.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * kPRow + lo.f[1]);
+      }
+      load_frags_qt<NT, SPLIT>(buf + kPanel, wn0, lo.q[0], fa.b);
+      load_frags_qt<NT, SPLIT>(buf + kPanel, wn0, lo.q[1], fb.b);
+    } else {
+      load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, lo.f[0], fa);
+      load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, lo.f[1], fb);
+    }
     if (E_TERM) take_e(buf, kt);
   };
   auto mul = [&]() {
@@ -550,7 +657,11 @@ __device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, int nk, const c
       mfma_frags<MT, NT>(fb, acc);
     }
   };
-  auto refill = [&](int kt) { issue_share(dsrc, kt, ring_lds + (kt & (kNBuf - 1)) * kStage); };
+  auto refill = [&](int kt) {
+    const uint32_t buf = ring_lds + (kt & (kNBuf - 1)) * kStage;
+    if (QT && G == 0) issue_share_qt<SPLIT>(qsrc, wave, kt, buf);
+    else issue_share(dsrc, kt, buf);
+  };
   // Phase 0: group 0 loads stage 0. Then per stage s:
   //   2s+1: g0 multiplies stage s; g1 loads stage s, then refills its half of
   //         stage s+3 (buffer of stage s-1, read by both groups before). At
@@ -606,8 +717,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   // block of 256 rows is ld * 256 * kEB bytes of consecutive panels.
   constexpr int kEB = SPLIT ? 4 : 2;
   constexpr int kPK = SPLIT ? 16 : 32;  // logical k per panel
+  // The apply reads its Q operand X K-major (QT): Q is then X's base and
+  // the tile's column block is selected per piece.
+  constexpr bool kQT = (MODE == kApply);
   const char* P = blk + g.offP + (int64_t)bi * kBM * g.ldp * kEB;
-  const char* Q = blk + g.offQ + (int64_t)bj * kBN * g.ldq * kEB;
+  const char* Q = blk + g.offQ + (kQT ? 0 : (int64_t)bj * kBN * g.ldq * kEB);
 
   f32x16 acc[kMT][kNT];
 #pragma unroll
@@ -617,24 +731,47 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 
   const int nk = g.K / kPK;  // stages; a multiple of 8, since K is a multiple of kPad
   const int wm0 = wm * kWTM, wn0 = wn * kWTN;
-  int loff[2];
+  // Lane parts of the LDS read addresses. Fragment reads (ds_read_b128):
+  // row (multiple of 32) + lane%32, chunk 2h + lane/32, swizzled. QT
+  // transposed reads: in 16-lane group gq = (lane/16)%2 of k group
+  // kg = lane/32, lane i = lane%16 names row 8kg + i/4 (fragments, plus 16h
+  // for bf16) or 4kg + i/4 (E), columns 16gq + 4(i%4) .. +3 of the tile's
+  // column block: bf16 piece rows hold 32 columns; split pieces hold 16
+  // (the group's own piece, hi then lo, halves swapped in odd pieces).
+  LaneOffs lo;
   {
-    const int r = lane & 31, f = (r >> 2) & 3;
+    const int r = lane & 31, f = (r >> 2) & 3, kg = lane >> 5, gq = (lane >> 4) & 1,
+              i = lane & 15;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) loff[h] = r * kPRow + (((2 * h + (lane >> 5)) ^ f) << 4);
+    for (int h = 0; h < 2; ++h) {
+      lo.f[h] = r * kPRow + (((2 * h + kg) ^ f) << 4);
+      if (!SPLIT) {
+        const int cb = (16 * gq + 4 * (i & 3)) * 2;
+        lo.q[h] = (16 * h + 8 * kg + (i >> 2)) * kPRow + cb;
+        lo.e[h] = (4 * kg + (i >> 2)) * kPRow + cb;
+      } else {
+        const int cb = gq * 1024 + (((((i & 3) >> 1) + 2 * h) ^ (2 * gq)) << 4) + (i & 1) * 8;
+        lo.q[h] = (8 * kg + (i >> 2)) * kPRow + cb;
+        lo.e[h] = (4 * kg + (i >> 2)) * kPRow + cb;
+      }
+    }
   }
   const DmaSrc dsrc = dma_src(P, Q, wave, lane);
+  const QtSrc qsrc = qt_src<SPLIT>(Q, g.ldq, bj, wave, lane);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
 #pragma unroll
-  for (int st = 0; st < kNBuf; ++st) issue_share(dsrc, st, ring_lds + st * kStage);
+  for (int st = 0; st < kNBuf; ++st) {
+    if (kQT && wave < 4) issue_share_qt<SPLIT>(qsrc, wave, st, ring_lds + st * kStage);
+    else issue_share(dsrc, st, ring_lds + st * kStage);
+  }
   phase_barrier<12>();  // this wave's share of stage 0 has landed
   const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
   if (wave < 4)
-    pingpong<0, kMT, kNT, MODE != kGram, SPLIT>(dsrc, nk, ring, ring_lds, wm0, wn0, loff, lane,
-                                                bi, seed, acc);
+    pingpong<0, kMT, kNT, MODE != kGram, SPLIT, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0,
+                                                     wn0, lo, lane, bi, seed, acc);
   else
-    pingpong<1, kMT, kNT, MODE != kGram, SPLIT>(dsrc, nk, ring, ring_lds, wm0, wn0, loff, lane,
-                                                bi, seed, acc);
+    pingpong<1, kMT, kNT, MODE != kGram, SPLIT, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0,
+                                                     wn0, lo, lane, bi, seed, acc);
 
   // ---- epilogue. The E term is already in the accumulators (the
   // polynomial's still needs its factor c). Every refill has landed (the last

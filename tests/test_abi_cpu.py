@@ -69,14 +69,17 @@ def test_plan_counts_and_workspace_growth():
     p = mh.Plan([(2048, 2048, 56), (512, 2048, 56), (6144, 2048, 56), (2048, 6144, 28)])
     assert p.num_matrices == 196
     assert p.num_params == 1_350_565_888
-    # bf16 operands: X, two X^T copies, A and B per matrix, padded to 256
+    # bf16 operands: two X buffers (s x l), A and B (s x s) per matrix, padded to 256
     ws = p.workspace_bytes
-    ns = 56 * 2 * (3 * 2048 * 2048 + 2 * 2048 * 2048) + 56 * 2 * (3 * 512 * 2048 + 2 * 512 * 512) \
-        + 84 * 2 * (3 * 2048 * 6144 + 2 * 2048 * 2048)
+    ns = 56 * 2 * (2 * 2048 * 2048 + 2 * 2048 * 2048) + 56 * 2 * (2 * 512 * 2048 + 2 * 512 * 512) \
+        + 84 * 2 * (2 * 2048 * 6144 + 2 * 2048 * 2048)
     assert ns <= ws <= ns + 196 * (256 * 8 + 16) + 4096
     shapes = [(2048, 2048, 56), (512, 2048, 56), (6144, 2048, 56), (2048, 6144, 28)]
+    # fp32 debug: X, two X^T copies, A and B, 4 bytes each
     p32 = mh.Plan(shapes, ns_fp32=True)
-    assert p32.workspace_bytes > 1.9 * ns
+    ns32 = 56 * 4 * (3 * 2048 * 2048 + 2 * 2048 * 2048) + 56 * 4 * (3 * 512 * 2048 + 2 * 512 * 512) \
+        + 84 * 4 * (3 * 2048 * 6144 + 2 * 2048 * 2048)
+    assert ns32 <= p32.workspace_bytes <= ns32 + 196 * (256 * 8 + 16) + 4096
     # split bf16: a hi and a lo value per element, so twice the operand bytes
     psp = mh.Plan(shapes, precision="split_bf16")
     assert 2 * ns <= psp.workspace_bytes <= 2 * ns + 196 * (256 * 8 + 16) + 4096
@@ -92,8 +95,8 @@ def test_binding_rejects_unknown_precision():
 
 def test_plan_padding_of_ragged_shapes():
     p = mh.Plan([(1, 1, 1)])
-    # one 256x256 block per operand buffer (X, 2 X^T, A, B) in bf16
-    assert p.workspace_bytes >= 5 * 256 * 256 * 2
+    # one 256x256 block per operand buffer (2 X, A, B) in bf16
+    assert 4 * 256 * 256 * 2 <= p.workspace_bytes <= 4 * 256 * 256 * 2 + 256 * 8 + 4096
     assert p.num_params == 1
 
 
