@@ -175,6 +175,11 @@ struct Fmt<kBf16> {
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
   }
+  __device__ static void store4(char* base, int64_t r, int c, int ld, float4 v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 h = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    *reinterpret_cast<bf16x4*>(base + off(r, c, ld)) = h;
+  }
 };
 template <>
 struct Fmt<kSplitBf16> {
@@ -191,6 +196,15 @@ struct Fmt<kSplitBf16> {
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
     const __bf16* p = reinterpret_cast<const __bf16*>(base + off(r, c, ld));
     return (float)p[0] + (float)p[16];
+  }
+  __device__ static void store4(char* base, int64_t r, int c, int ld, float4 v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 h = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    const bf16x4 l = {(__bf16)(v.x - (float)h[0]), (__bf16)(v.y - (float)h[1]),
+                      (__bf16)(v.z - (float)h[2]), (__bf16)(v.w - (float)h[3])};
+    char* p = base + off(r, c, ld);
+    *reinterpret_cast<bf16x4*>(p) = h;
+    *reinterpret_cast<bf16x4*>(p + 32) = l;
   }
   __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
     const char* p = base + off(r, c, ld);
@@ -214,6 +228,9 @@ struct Fmt<kFp32> {
   __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
     return *reinterpret_cast<const float4*>(base + off(r, c, ld));
   }
+  __device__ static void store4(char* base, int64_t r, int c, int ld, float4 v) {
+    *reinterpret_cast<float4*>(base + off(r, c, ld)) = v;
+  }
 };
 
 // --------------------------------------------------------------------------
@@ -236,24 +253,47 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
   const float scale = (float)(1.0 / (norms[mat] + kNsEps));
   const float* mp = M[mat];
   char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
-  char* D = blk + g.offD;
-  char* E = blk + g.offE;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int rr = i * 4 + ty;
+  // Each thread takes 4 consecutive columns of 4 rows: columns
+  // c0 + 4*(tid % 16), rows r0 + tid/16 + 16i.
+  const int tx = (threadIdx.x & 15) << 2, ty = threadIdx.x >> 4;
+  const bool vec = (g.cols & 3) == 0 && aligned16(mp);
+  const bool trans = g.offE >= 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = ty + 16 * i;
     const int r = r0 + rr, c = c0 + tx;
-    float v = 0.f;
-    if (r < g.rows && c < g.cols) v = mp[(int64_t)r * g.cols + c] * scale;
-    tile[rr][tx] = v;
-    if (g.offD >= 0) Fmt<F>::store(D, r, c, g.cp, v);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < g.rows) {
+      const float* row = mp + (int64_t)r * g.cols;
+      if (vec && c + 3 < g.cols) {
+        v = *reinterpret_cast<const float4*>(row + c);
+      } else {
+        if (c < g.cols) v.x = row[c];
+        if (c + 1 < g.cols) v.y = row[c + 1];
+        if (c + 2 < g.cols) v.z = row[c + 2];
+        if (c + 3 < g.cols) v.w = row[c + 3];
+      }
+    }
+    v.x *= scale;
+    v.y *= scale;
+    v.z *= scale;
+    v.w *= scale;
+    if (g.offD >= 0) Fmt<F>::store4(blk + g.offD, r, c, g.cp, v);
+    if (trans) {
+      tile[rr][tx] = v.x;
+      tile[rr][tx + 1] = v.y;
+      tile[rr][tx + 2] = v.z;
+      tile[rr][tx + 3] = v.w;
+    }
   }
-  if (g.offE < 0) return;
+  if (!trans) return;
   __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int cc = i * 4 + ty;
-    Fmt<F>::store(E, c0 + cc, r0 + tx, g.rp, tile[tx][cc]);
+  // transposed: row c0 + cc of E, its columns r0 + tx .. +3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cc = ty + 16 * i;
+    const float4 v = make_float4(tile[tx][cc], tile[tx + 1][cc], tile[tx + 2][cc], tile[tx + 3][cc]);
+    Fmt<F>::store4(blk + g.offE, c0 + cc, r0 + tx, g.rp, v);
   }
 }
 
