@@ -146,8 +146,8 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            get_lib().muonh_plan_destroy(h)
+        if h is not None and h.value and _LIB is not None:
+            _LIB.muonh_plan_destroy(h)
             self.handle = None
 
 

@@ -127,17 +127,18 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const float* co
 }
 
 // --------------------------------------------------------------------------
-// norms[mat] = sqrt(sum_c partials[mat][c]) in a fixed order
+// norms[mat] = sqrt(sum_c partials[mat][c]) in a fixed order, for exactly the
+// matrices of the launch's groups (thread t takes the t-th of them). The
+// groups need not cover a contiguous range of matrices: launches for other
+// matrices may run concurrently and own the rest of the arrays.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_finalize(EwArgs a, const double* partials,
                                                        double* norms, float* R) {
-  const int first = a.g[0].first;
-  const int last = a.g[a.ngroups - 1].first + a.g[a.ngroups - 1].count;
-  const int64_t mat = (int64_t)first + (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (mat >= last) return;
+  int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   int gi = 0;
-  for (int i = 1; i < a.ngroups; ++i)
-    if (mat >= a.g[i].first) gi = i;
+  while (gi < a.ngroups && t >= a.g[gi].count) t -= a.g[gi++].count;
+  if (gi >= a.ngroups) return;
+  const int64_t mat = (int64_t)a.g[gi].first + t;
   const int bpm = a.g[gi].bpm;
   const double* p = partials + mat * kMaxPartials;
   double s = 0.0;
@@ -395,7 +396,8 @@ hipError_t launch_momentum(const EwArgs& a, const float* const* G, float* const*
 
 hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norms, float* R,
                            hipStream_t s) {
-  const int64_t n = (int64_t)a.g[a.ngroups - 1].first + a.g[a.ngroups - 1].count - a.g[0].first;
+  int64_t n = 0;
+  for (int i = 0; i < a.ngroups; ++i) n += a.g[i].count;
   const int blocks = (int)((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(k_finalize, dim3(blocks), dim3(kThreads), 0, s, a, partials, norms, R);
   return hipGetLastError();

@@ -391,3 +391,41 @@ def test_large_full_size_sampled(k, prec):
     # split-bf16 operands.
     run_device_workload("large_4096x14336", steps=1, k=k, sample=[0, 63], prec=prec,
                         label=f"large k={k} {prec}")
+
+
+# ---------------------------------------------------------------------------
+# muonh_step against muonh_step_timed (the same schedule plus phase events):
+# the results must agree bit for bit, step after step, on a set with several
+# shape groups of both orientations.
+# ---------------------------------------------------------------------------
+
+def test_step_and_timed_step_agree_bitwise():
+    need_gpu()
+    dev = torch.device("cuda")
+    shapes = [(1024, 3072)] * 12 + [(3072, 1024)] * 12 + [(2048, 2048)] * 8 + [(256, 1024)] * 8
+    k = 5
+    W0 = [workloads.device_normal_(torch.empty(s, device=dev), 0.02, 70, i, 0, 0)
+          for i, s in enumerate(shapes)]
+    Gs = [[workloads.device_normal_(torch.empty(s, device=dev), 0.01, 70, i, st, 1)
+           for i, s in enumerate(shapes)] for st in range(3)]
+    runs = []
+    for timed in (False, True):
+        opt = make_opt(shapes, "bf16")
+        W = [w.clone() for w in W0]
+        M = [torch.zeros(s, device=dev) for s in shapes]
+        opt.init(W)
+        for st in range(3):
+            say(f"[step vs timed] timed={timed} step {st}")
+            if timed:
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * k + 3)]
+                for e in evs:
+                    e.record()
+                opt.step_timed(W, Gs[st], M, 0.02, 0.95, k, evs)
+            else:
+                opt.step(W, Gs[st], M, 0.02, 0.95, k)
+        torch.cuda.synchronize()
+        runs.append(([w.cpu() for w in W], [m.cpu() for m in M],
+                     [opt.read_update(i).cpu() for i in range(len(shapes))]))
+    for name, a, b in zip(("W", "M", "O"), runs[0], runs[1]):
+        for i, (x, y) in enumerate(zip(a, b)):
+            assert torch.equal(x, y), f"{name}[{i}] differs between step and step_timed"
