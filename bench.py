@@ -50,16 +50,18 @@ def ns_flops(shapes, k):
     return {"gram": gram, "poly": poly, "apply": apply}
 
 
-def elementwise_bytes(n_params, ns_bytes, layouts):
+def elementwise_bytes(n_params, ns_bytes, fused):
     """Algorithmic HBM bytes of the streaming phases, per step.
 
-    before Newton-Schulz: momentum reads G, M and writes M (12 B/param);
-      the cast reads M and writes X0 in `layouts` layouts (one for bf16 and
-      split operands, X and X^T for fp32): 4 + layouts*ns_bytes B/param;
+    before Newton-Schulz: momentum reads G, M and writes M (12 B/param) and
+      X0 is written once (ns_bytes); with bf16 or split operands and at least
+      one iteration the two happen in one pass (fused), otherwise the cast
+      reads M again and, in fp32 mode, writes X and X^T:
+      12 + 4 + 2*ns_bytes B/param;
     after: the trial-norm pass reads W and O (4 + ns_bytes), the projection
       reads W and O and writes W (8 + ns_bytes).
     """
-    pre = n_params * (12 + 4 + layouts * ns_bytes)
+    pre = n_params * (12 + ns_bytes if fused else 12 + 4 + 2 * ns_bytes)
     post = n_params * (4 + ns_bytes + 8 + ns_bytes)
     return pre, post
 
@@ -246,7 +248,7 @@ def main() -> int:
     fp32 = args.precision == "fp32"
     peak_mfma = PEAK_FP32_MFMA_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     ns_bytes = 2 if args.precision == "bf16" else 4
-    pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes, 2 if fp32 else 1)
+    pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes, fused=not fp32 and k >= 1)
     pre_ms, post_ms = pre / nst, post / nst
     dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
 

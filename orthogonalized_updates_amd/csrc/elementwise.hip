@@ -235,45 +235,63 @@ struct Fmt<kFp32> {
 };
 
 // --------------------------------------------------------------------------
-// X0 = M / (||M|| + eps): one 64x64 tile of the padded rp x cp domain per
-// block; written straight to D and/or transposed (through LDS) to E (an
-// offset of -1 skips that output). Entries outside rows x cols are written
-// as zero.
+// One 64x64 tile of the padded rp x cp domain of a matrix: X0 values written
+// straight to D and/or transposed (through LDS) to E (an offset of -1 skips
+// that output); entries outside rows x cols are written as zero. With
+// kMomentum the tile first takes M <- beta*M + G (written back) and returns
+// this thread's sum of squares of the new M; the values written are then
+// scale * M. Each thread takes 4 consecutive columns of 4 rows: columns
+// c0 + 4*(tid % 16), rows r0 + tid/16 + 16i. Every thread of the block must
+// call it (it synchronises when E is written).
 // --------------------------------------------------------------------------
-template <int F>
-__global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* const* M,
-                                                       const double* norms) {
-  __shared__ float tile[64][65];
-  const int gi = group_of_block(a, blockIdx.x);
-  const EwGroup& g = a.g[gi];
-  const int local = blockIdx.x - g.block_begin;
-  const int m = local / g.tiles_per_mat, t = local - m * g.tiles_per_mat;
-  const int mat = g.first + m;
-  const int tcols = g.cp >> 6;
-  const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
-  const float scale = (float)(1.0 / (norms[mat] + kNsEps));
-  const float* mp = M[mat];
-  char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
-  // Each thread takes 4 consecutive columns of 4 rows: columns
-  // c0 + 4*(tid % 16), rows r0 + tid/16 + 16i.
+template <int F, bool kMomentum>
+__device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const float* gp, float* mp,
+                                           float beta, int r0, int c0, float scale,
+                                           float (*tile)[65]) {
   const int tx = (threadIdx.x & 15) << 2, ty = threadIdx.x >> 4;
-  const bool vec = (g.cols & 3) == 0 && aligned16(mp);
+  const bool vec = (g.cols & 3) == 0 && aligned16(mp) && (!kMomentum || aligned16(gp));
   const bool trans = g.offE >= 0;
+  float acc = 0.f;
+  if (trans) __syncthreads();  // the previous tile's transposed reads are done
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = ty + 16 * i;
     const int r = r0 + rr, c = c0 + tx;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < g.rows) {
-      const float* row = mp + (int64_t)r * g.cols;
+      float* row = mp + (int64_t)r * g.cols;
+      const float* grow = kMomentum ? gp + (int64_t)r * g.cols : nullptr;
       if (vec && c + 3 < g.cols) {
         v = *reinterpret_cast<const float4*>(row + c);
+        if (kMomentum) {
+          const float4 gv = *reinterpret_cast<const float4*>(grow + c);
+          v.x = fmaf(beta, v.x, gv.x);
+          v.y = fmaf(beta, v.y, gv.y);
+          v.z = fmaf(beta, v.z, gv.z);
+          v.w = fmaf(beta, v.w, gv.w);
+          *reinterpret_cast<float4*>(row + c) = v;
+        }
       } else {
-        if (c < g.cols) v.x = row[c];
-        if (c + 1 < g.cols) v.y = row[c + 1];
-        if (c + 2 < g.cols) v.z = row[c + 2];
-        if (c + 3 < g.cols) v.w = row[c + 3];
+        float e[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (c + q < g.cols) {
+            float m = row[c + q];
+            if (kMomentum) {
+              m = fmaf(beta, m, grow[c + q]);
+              row[c + q] = m;
+            }
+            e[q] = m;
+          }
+        }
+        v = make_float4(e[0], e[1], e[2], e[3]);
       }
+    }
+    if (kMomentum) {
+      acc = fmaf(v.x, v.x, acc);
+      acc = fmaf(v.y, v.y, acc);
+      acc = fmaf(v.z, v.z, acc);
+      acc = fmaf(v.w, v.w, acc);
     }
     v.x *= scale;
     v.y *= scale;
@@ -287,14 +305,81 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
       tile[rr][tx + 3] = v.w;
     }
   }
-  if (!trans) return;
-  __syncthreads();
-  // transposed: row c0 + cc of E, its columns r0 + tx .. +3
+  if (trans) {
+    __syncthreads();
+    // transposed: row c0 + cc of E, its columns r0 + tx .. +3
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int cc = ty + 16 * i;
-    const float4 v = make_float4(tile[tx][cc], tile[tx + 1][cc], tile[tx + 2][cc], tile[tx + 3][cc]);
-    Fmt<F>::store4(blk + g.offE, c0 + cc, r0 + tx, g.rp, v);
+    for (int i = 0; i < 4; ++i) {
+      const int cc = ty + 16 * i;
+      const float4 v = make_float4(tile[tx][cc], tile[tx + 1][cc], tile[tx + 2][cc], tile[tx + 3][cc]);
+      Fmt<F>::store4(blk + g.offE, c0 + cc, r0 + tx, g.rp, v);
+    }
+  }
+  return acc;
+}
+
+// X0 = M / (||M|| + eps): one tile per block.
+template <int F>
+__global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* const* M,
+                                                       const double* norms) {
+  __shared__ float tile[64][65];
+  const int gi = group_of_block(a, blockIdx.x);
+  const EwGroup& g = a.g[gi];
+  const int local = blockIdx.x - g.block_begin;
+  const int m = local / g.tiles_per_mat, t = local - m * g.tiles_per_mat;
+  const int mat = g.first + m;
+  const int tcols = g.cp >> 6;
+  const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
+  const float scale = (float)(1.0 / (norms[mat] + kNsEps));
+  cast_tile<F, false>(g, g.ns_base + (int64_t)m * g.mat_bytes, nullptr, const_cast<float*>(M[mat]),
+                      0.f, r0, c0, scale, tile);
+}
+
+// Fused momentum and unscaled cast: block c of a matrix takes tiles
+// [c*tpb, (c+1)*tpb) of its padded domain and writes one partial sum.
+template <int F>
+__global__ __launch_bounds__(kThreads) void k_momentum_cast(EwArgs a, const float* const* G,
+                                                            float* const* M, float beta,
+                                                            double* partials) {
+  __shared__ float tile[64][65];
+  __shared__ double red[4];
+  const int gi = group_of_block(a, blockIdx.x);
+  const EwGroup& g = a.g[gi];
+  const int local = blockIdx.x - g.block_begin;
+  const int m = local / g.bpm, c = local - m * g.bpm;
+  const int mat = g.first + m;
+  char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
+  const int tcols = g.cp >> 6;
+  const int t1 = min((c + 1) * g.tpb, g.tiles_per_mat);
+  float acc = 0.f;
+  for (int t = c * g.tpb; t < t1; ++t) {
+    const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
+    acc += cast_tile<F, true>(g, blk, G[mat], M[mat], beta, r0, c0, 1.f, tile);
+  }
+  const double tot = block_sum((double)acc, red);
+  if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = tot;
+}
+
+// Fallback of the deferred normalisation: 8 blocks per matrix; for the
+// matrices whose norm fails xnorm_deferred they rewrite X0 normalised.
+template <int F>
+__global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const float* const* M,
+                                                            const double* norms) {
+  __shared__ float tile[64][65];
+  int b = blockIdx.x, gi = 0;
+  while (gi < a.ngroups && b >= a.g[gi].count * 8) b -= a.g[gi++].count * 8;
+  if (gi >= a.ngroups) return;
+  const EwGroup& g = a.g[gi];
+  const int m = b >> 3, j = b & 7;
+  const int mat = g.first + m;
+  const double n = norms[mat];
+  if (xnorm_deferred(n)) return;  // uniform for the block
+  const float scale = (float)(1.0 / (n + kNsEps));
+  char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
+  const int tcols = g.cp >> 6;
+  for (int t = j; t < g.tiles_per_mat; t += 8) {
+    const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
+    cast_tile<F, false>(g, blk, nullptr, const_cast<float*>(M[mat]), 0.f, r0, c0, scale, tile);
   }
 }
 
@@ -418,6 +503,25 @@ hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norm
 hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
                            const double* norms, hipStream_t s) {
   MUONH_PREC_DISPATCH(prec, K_NORMCAST, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms)
+  return hipGetLastError();
+}
+
+#define K_MOMCAST(F) k_momentum_cast<F>
+#define K_FALLBACK(F) k_cast_fallback<F>
+
+hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, const float* const* G,
+                                float* const* M, float beta, double* partials, hipStream_t s) {
+  MUONH_PREC_DISPATCH(prec, K_MOMCAST, dim3(a.nblocks), dim3(kThreads), 0, s, a, G, M, beta,
+                      partials)
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, const float* const* M,
+                                const double* norms, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < a.ngroups; ++i) blocks += (int64_t)a.g[i].count * 8;
+  if (blocks == 0) return hipSuccess;
+  MUONH_PREC_DISPATCH(prec, K_FALLBACK, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, M, norms)
   return hipGetLastError();
 }
 

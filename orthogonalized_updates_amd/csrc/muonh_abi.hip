@@ -103,13 +103,18 @@ int64_t off_update(const muonh_plan* p, const GroupPlan& G) {
   return G.trans ? G.offXt[0] : G.offX;
 }
 
-// Streaming (bpm blocks per matrix) or tile (64x64 tiles of the padded
-// domain) launch descriptors, in batches of at most kMaxEwGroups groups.
+// Launch descriptors of the streaming kernels (kind kEwStream: bpm blocks per
+// matrix), the cast (kEwTile: one block per 64x64 tile of the padded domain)
+// or the fused momentum + cast (kEwFused: blocks of tpb = ceil(tiles / 256)
+// tiles, so at most 256 partial sums per matrix), in batches of at most
+// kMaxEwGroups groups.
 // ns_iters < 0: D is O (the update and projection read it); otherwise D and
 // E are what the normalising cast writes before ns_iters iterations: X0 in
 // the buffer the first iteration reads (own orientation in D, transposed in
 // E, -1 where nothing is written); with 0 iterations, O itself.
-std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int ns_iters) {
+enum EwKind { kEwStream = 0, kEwTile = 1, kEwFused = 2 };
+
+std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, EwKind kind, int ns_iters) {
   std::vector<EwArgs> out;
   const size_t ng = p->groups.size();
   for (size_t g0 = 0; g0 < ng; g0 += kMaxEwGroups) {
@@ -151,8 +156,13 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int ns_it
         e.offE = G.trans ? x0 : -1;
       }
       e.tiles_per_mat = (rp / 64) * (cp / 64);
+      e.tpb = 1;
+      if (kind == kEwFused) {
+        e.tpb = (e.tiles_per_mat + kMaxPartials - 1) / kMaxPartials;
+        e.bpm = (e.tiles_per_mat + e.tpb - 1) / e.tpb;
+      }
       e.block_begin = (int)blocks;
-      blocks += (int64_t)G.count * (tiles ? e.tiles_per_mat : G.bpm);
+      blocks += (int64_t)G.count * (kind == kEwTile ? e.tiles_per_mat : e.bpm);
     }
     a.ngroups = (int)(g1 - g0);
     a.nblocks = (int)blocks;
@@ -162,7 +172,8 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, bool tiles, int ns_it
 }
 
 // GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
-std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters) {
+std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters,
+                                const double* xnorm = nullptr) {
   const int T = gemm_tile(p->prec);
   // bf16 / split: the buffer iteration `it` reads X from (X0 goes to buffer
   // 1 - iters%2, so that the last apply writes buffer 1)
@@ -174,6 +185,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     q.base = ws + G.off;
     q.mat_bytes = G.mat_bytes;
     q.count = G.count;
+    q.first = G.first;
     q.offE = q.offO1 = q.offO2 = -1;
     const int ts = G.sp / T, tl = G.lp / T;
     const int64_t xcur = p->prec == kFp32 ? G.offX : G.offXs[src];
@@ -256,6 +268,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     }
     a.ngroups = (int)(g1 - g0);
     a.ntiles = (int)tiles;
+    a.xnorm = mode == kPoly ? nullptr : xnorm;
     a.xcd_map = p->prec == kFp32 ? 0 : 1;
     if (a.xcd_map) {
       // slots per XCD: the longest of the 8 per-XCD lists
@@ -419,7 +432,7 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
   double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
   double* norms = reinterpret_cast<double*>(ws + plan->off_norm_w);
   hipError_t e;
-  for (const EwArgs& a : make_ew(plan, ws, false, -1)) {
+  for (const EwArgs& a : make_ew(plan, ws, kEwStream, -1)) {
     if ((e = launch_sumsq(a, W, partials, s)) != hipSuccess) return hip_fail(e, "init sumsq");
     if ((e = launch_finalize(a, partials, norms, R, s)) != hipSuccess)
       return hip_fail(e, "init finalize");
@@ -463,29 +476,44 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
     return hipEventRecord(reinterpret_cast<hipEvent_t>(events[ev++]), s);
   };
 
-  const std::vector<EwArgs> stream_args = make_ew(plan, ws, false, -1);
-  const std::vector<EwArgs> tile_args = make_ew(plan, ws, true, ns_iters);
+  const std::vector<EwArgs> stream_args = make_ew(plan, ws, kEwStream, -1);
+  // bf16 and split operands with at least one iteration: momentum and the
+  // unscaled cast in one pass, normalisation deferred to the first GEMMs
+  // (see xnorm_deferred); otherwise momentum, its norm, then the cast.
+  const bool fused = plan->prec != kFp32 && ns_iters >= 1;
 
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
-  for (const EwArgs& a : stream_args) {
-    if ((e = launch_momentum(a, G, M, beta, partials, s)) != hipSuccess)
-      return hip_fail(e, "momentum");
-    if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
-      return hip_fail(e, "momentum finalize");
+  if (fused) {
+    for (const EwArgs& a : make_ew(plan, ws, kEwFused, ns_iters)) {
+      if ((e = launch_momentum_cast(a, plan->prec, G, M, beta, partials, s)) != hipSuccess)
+        return hip_fail(e, "momentum + cast");
+      if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "momentum finalize");
+      if ((e = launch_cast_fallback(a, plan->prec, M, norm_m, s)) != hipSuccess)
+        return hip_fail(e, "cast fallback");
+    }
+  } else {
+    for (const EwArgs& a : stream_args) {
+      if ((e = launch_momentum(a, G, M, beta, partials, s)) != hipSuccess)
+        return hip_fail(e, "momentum");
+      if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "momentum finalize");
+    }
+    for (const EwArgs& a : make_ew(plan, ws, kEwTile, ns_iters))
+      if ((e = launch_normcast(a, plan->prec, M, norm_m, s)) != hipSuccess)
+        return hip_fail(e, "normcast");
   }
-  for (const EwArgs& a : tile_args)
-    if ((e = launch_normcast(a, plan->prec, M, norm_m, s)) != hipSuccess)
-      return hip_fail(e, "normcast");
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
 
   for (int it = 0; it < ns_iters; ++it) {
-    for (const GemmArgs& a : make_gemm(plan, ws, kGram, it, ns_iters))
+    const double* xnorm = (fused && it == 0) ? norm_m : nullptr;
+    for (const GemmArgs& a : make_gemm(plan, ws, kGram, it, ns_iters, xnorm))
       if ((e = launch_gemm(kGram, plan->prec, a, s)) != hipSuccess) return hip_fail(e, "ns gram");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
     for (const GemmArgs& a : make_gemm(plan, ws, kPoly, it, ns_iters))
       if ((e = launch_gemm(kPoly, plan->prec, a, s)) != hipSuccess) return hip_fail(e, "ns poly");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
-    for (const GemmArgs& a : make_gemm(plan, ws, kApply, it, ns_iters))
+    for (const GemmArgs& a : make_gemm(plan, ws, kApply, it, ns_iters, xnorm))
       if ((e = launch_gemm(kApply, plan->prec, a, s)) != hipSuccess)
         return hip_fail(e, "ns apply");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");

@@ -22,15 +22,32 @@ constexpr int kPad = 256;
 // Max number of per-matrix partial sums of a norm reduction.
 constexpr int kMaxPartials = 256;
 
-// Storage format of the Newton-Schulz operands (X, X^T, A, B):
-//   kBf16      bf16, rows dense;
-//   kSplitBf16 each value v as hi = bf16(v) and lo = bf16(v - hi); a row is a
-//              sequence of 128-byte blocks of 32 hi then 32 lo values;
-//   kFp32      fp32 (debug mode).
+// Storage format of the Newton-Schulz operands (X, A, B; X^T in fp32 mode):
+//   kBf16      bf16, panel-major: panels of 256 rows x 64 bytes (32 values
+//              per panel row), panel (r/256, c/32) at
+//              ((r/256) * (ld/32) + c/32) * 16 KB;
+//   kSplitBf16 each value v as hi = bf16(v) and lo = bf16(v - hi); the same
+//              panels with 16 hi then the 16 matching lo values per row;
+//   kFp32      fp32, row-major (debug mode).
 // Leading dimensions are always in logical elements; bytes per logical
 // element: 2, 4 and 4.
 enum NsPrec : int { kBf16 = 0, kSplitBf16 = 1, kFp32 = 2 };
 constexpr int ns_elem_bytes(NsPrec p) { return p == kBf16 ? 2 : 4; }
+
+// Deferred normalisation of X0 (bf16 and split operands with at least one
+// iteration): the momentum kernel writes Y = M rounded to the operand format,
+// unscaled, and the first iteration's GEMM epilogues apply
+// sigma = 1 / (||M|| + eps) (Gram: sigma^2, apply: sigma). That is exact
+// algebra (X0 = sigma * M), and safe while fp32 accumulation of Y neither
+// overflows nor underflows: for ||M|| in [2^-40, 2^40], or 0 (Y = 0). Other
+// norms (and non-finite ones) take a fallback that writes X0 normalised, and
+// the epilogues then use sigma = 1.
+__host__ __device__ inline bool xnorm_deferred(double n) {
+  return n == 0.0 || (n >= 0x1p-40 && n <= 0x1p40);
+}
+__host__ __device__ inline float x0_sigma(double n) {
+  return xnorm_deferred(n) ? (float)(1.0 / (n + kNsEps)) : 1.f;
+}
 
 // ---------------------------------------------------------------------------
 // Elementwise / reduction kernels (elementwise.hip)
@@ -40,7 +57,8 @@ constexpr int kMaxEwGroups = 16;
 struct EwGroup {
   int rows, cols;       // matrix shape (row-major fp32)
   int count, first;     // number of matrices, global index of the first one
-  int bpm;              // blocks per matrix for the streaming kernels
+  int bpm;              // blocks per matrix (= partial sums per matrix)
+  int tpb;              // tiles per block (fused momentum + cast)
   int block_begin;      // first block of this group in the launch
   int64_t n;            // rows * cols
   // Newton-Schulz buffers of matrix m live at ns_base + m * mat_bytes.
@@ -72,6 +90,14 @@ hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norm
 // X0 = M / (norm + eps) written to D (same orientation) and E (transposed).
 hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
                            const double* norms, hipStream_t s);
+// M <- beta*M + G with partial sums of squares, and Y = M (unscaled) written
+// to D / E as X0 would be (tile launch; bpm blocks of tpb tiles per matrix).
+hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, const float* const* G,
+                                float* const* M, float beta, double* partials, hipStream_t s);
+// For the matrices whose norm fails xnorm_deferred: X0 = M / (norm + eps)
+// written as launch_normcast would (8 blocks per matrix; the others return).
+hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, const float* const* M,
+                                const double* norms, hipStream_t s);
 hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, float lr,
                               double* partials, hipStream_t s);
 hipError_t launch_project(const EwArgs& a, NsPrec prec, float* const* W, const float* R,
@@ -82,7 +108,8 @@ hipError_t launch_read_update(NsPrec prec, const char* D, int ldD, int rows, int
 
 // ---------------------------------------------------------------------------
 // Newton-Schulz MFMA GEMM kernels (ns_gemm.hip)
-//   C[i][j] = sum_k P[i][k] * Q[j][k]  (both operands K-contiguous rows)
+//   C[i][j] = sum_k P[i][k] * Q[j][k]; the bf16 apply reads Q = X K-major
+//   (C = B X), every other operand is read along its rows.
 // ---------------------------------------------------------------------------
 constexpr int kMaxGemmGroups = 16;
 
@@ -102,6 +129,7 @@ struct GemmGroup {
   int tiles_per_mat;
   int tile_begin;
   int count;
+  int first;            // global index of the group's first matrix
 };
 
 struct GemmArgs {
@@ -111,6 +139,9 @@ struct GemmArgs {
   int grid;      // blocks launched (>= ntiles when the XCD mapping pads)
   int xcd_map;   // 1: deal each group's tiles to the 8 XCDs in contiguous eighths
   float c0, c1;
+  // First iteration after the fused momentum + cast: per-matrix ||M||; the
+  // output is scaled by x0_sigma (Gram: squared). nullptr: no scaling.
+  const double* xnorm;
 };
 
 // Tile edge (square tiles) used by the launchers for the given precision.

@@ -780,7 +780,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   // split operands one pass for the hi and one for the lo parts of each):
   // the tile's panels are one contiguous region of the output, written with
   // coalesced 16-byte stores.
-  const float scale = MODE == kPoly ? args.c1 : 1.f;
+  // The first iteration after the fused momentum + cast sees X0 unscaled:
+  // A = sigma^2 Y Y^T, and the apply's a*Y + B*Y takes sigma.
+  float scale = MODE == kPoly ? args.c1 : 1.f;
+  if (MODE != kPoly && args.xnorm) {
+    const float sg = x0_sigma(args.xnorm[g.first + mat]);
+    scale = MODE == kGram ? sg * sg : sg;
+  }
   bf16x4 vh[kMT][kNT][4], vl[kMT][kNT][4];
 #pragma unroll
   for (int mi = 0; mi < kMT; ++mi)

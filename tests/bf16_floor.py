@@ -11,6 +11,10 @@ values, so no averaging) it can exceed it.
 fmt="split_bf16" emulates the split storage instead: a stored value v is
 hi + lo with hi = bf16(v) and lo = bf16(v - hi) (the difference taken in
 fp32), and a product of two split operands omits lo*lo.
+
+deferred=True (the GPU path with at least one iteration) stores M itself
+rounded and folds 1/(||M|| + eps) into the first Gram (squared) and the
+first apply, for norms in [2^-40, 2^40] (or 0), as the kernels do.
 """
 from __future__ import annotations
 
@@ -37,11 +41,23 @@ def split_bf16(x):
     return hi, lo
 
 
-def _ns_emulated(m, k: int, fmt: str) -> np.ndarray:
+def _deferred(n: float) -> bool:
+    """Norms for which X0's normalisation is folded into the first GEMMs."""
+    return n == 0.0 or 2.0 ** -40 <= n <= 2.0 ** 40
+
+
+def _ns_emulated(m, k: int, fmt: str, deferred: bool = True) -> np.ndarray:
     if fmt == "bf16":
         def store(v):
             r = round_bf16(v)
             return r, r, None
+
+        def mul(p, q):
+            return p[0] @ q[0]
+    elif fmt == "exact":  # no rounding: checks the arithmetic of the scheme itself
+        def store(v):
+            v = np.asarray(v, dtype=np.float64)
+            return v, v, None
 
         def mul(p, q):
             return p[0] @ q[0]
@@ -58,8 +74,21 @@ def _ns_emulated(m, k: int, fmt: str) -> np.ndarray:
     t = x.shape[0] > x.shape[1]
     if t:
         x = x.T
-    x = store(x / (np.linalg.norm(x) + EPS))
-    for _ in range(int(k)):
+    nrm = float(np.linalg.norm(x))
+    first = 0
+    if deferred and int(k) >= 1 and _deferred(nrm):
+        # the stored operand is M itself; the first Gram takes sigma^2 and
+        # the first apply sigma
+        sigma = 1.0 / (nrm + EPS)
+        y = store(x)
+        yt = tuple(None if v is None else v.T for v in y)
+        a = store(sigma * sigma * mul(y, yt))
+        b = store(B_ * a[0] + C_ * mul(a, a))
+        x = store(sigma * (A_ * y[0] + mul(b, y)))
+        first = 1
+    else:
+        x = store(x / (nrm + EPS))
+    for _ in range(first, int(k)):
         xt = tuple(None if v is None else v.T for v in x)
         a = store(mul(x, xt))
         b = store(B_ * a[0] + C_ * mul(a, a))
@@ -75,8 +104,8 @@ def ns_split_bf16(m, k: int) -> np.ndarray:
     return _ns_emulated(m, k, "split_bf16")
 
 
-def floor(m, k: int, reference, fmt: str = "bf16") -> float:
+def floor(m, k: int, reference, fmt: str = "bf16", deferred: bool = True) -> float:
     """Relative Frobenius error of the emulated iteration vs `reference`."""
-    e = _ns_emulated(m, k, fmt)
+    e = _ns_emulated(m, k, fmt, deferred)
     nr = np.linalg.norm(reference)
     return float(np.linalg.norm(e - reference) / (nr if nr > 0 else 1.0))

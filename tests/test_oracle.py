@@ -415,6 +415,27 @@ def test_bf16_rounding_is_nearest_even():
     assert np.isnan(round_bf16(np.float32("nan")))
 
 
+@pytest.mark.parametrize("scale", [1e-9, 1.0, 1e6])
+@pytest.mark.parametrize("shape", [(48, 80), (80, 48)])
+def test_deferred_normalisation_is_exact_algebra(scale, shape):
+    # The GPU path stores M unscaled and applies sigma = 1/(||M|| + eps) as
+    # sigma^2 on the first Gram and sigma on the first apply (both terms).
+    # Without rounding that must be the oracle's iteration on M/(||M|| + eps),
+    # eps included (at ||M|| ~ 1e-7 it changes the result).
+    # sigma is far from 1 at scales 1e-9 and 1e6, so a wrong power of sigma
+    # on either GEMM would not match.
+    from bf16_floor import _ns_emulated
+    m = rand(shape, (23, shape[0]), 0.01 * scale)
+    for k in (1, 2, 5):
+        ref = oracle.newton_schulz(m, k)
+        got = _ns_emulated(m, k, "exact", deferred=True)
+        assert np.linalg.norm(got - ref) <= 1e-11 * max(np.linalg.norm(ref), 1e-300)
+    if scale == 1e-9:
+        # ||M|| ~ 6e-10 << eps: eps is honoured, the eps-free iteration differs
+        no_eps = oracle.newton_schulz(m, 1, eps=0.0)
+        assert np.linalg.norm(_ns_emulated(m, 1, "exact") - no_eps) > 1e-3 * np.linalg.norm(no_eps)
+
+
 def test_split_bf16_pair_carries_sixteen_bits():
     # hi + lo represents an fp32 value to within about 2^-17 of its magnitude
     # (hi has 8 significant bits, lo the next 8 and a rounding bit), and lo is

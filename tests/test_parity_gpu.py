@@ -429,3 +429,30 @@ def test_step_and_timed_step_agree_bitwise():
     for name, a, b in zip(("W", "M", "O"), runs[0], runs[1]):
         for i, (x, y) in enumerate(zip(a, b)):
             assert torch.equal(x, y), f"{name}[{i}] differs between step and step_timed"
+
+
+# ---------------------------------------------------------------------------
+# Deferred normalisation of X0 (bf16 and split operands): momentum norms far
+# outside [2^-40, 2^40] take the fallback that writes X0 normalised; a norm
+# of 1e-6 stays on the deferred path, where eps = 1e-7 still moves X0 by ~8 %.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("prec", ["bf16", "split_bf16"])
+def test_momentum_norm_extremes(prec):
+    need_gpu()
+    dev = torch.device("cuda")
+    shapes = [(96, 160), (160, 96), (128, 128), (200, 120)]
+    gscale = [1e-15, 1e15, 1e-6, 1.0]  # ||M|| ~ 1.2 * scale after the first step
+    opt, W, M = _setup(shapes, prec)
+    R = opt.init(W).cpu().numpy()
+    for st in range(2):
+        G_host = [(workloads.host_custom(sh, 0.01, (72, st, i)) * gscale[i]).astype(np.float32)
+                  for i, sh in enumerate(shapes)]
+        G = [torch.from_numpy(g).to(dev) for g in G_host]
+        W_pre = {i: W[i].cpu().numpy() for i in range(len(shapes))}
+        M_pre = {i: M[i].cpu().numpy() for i in range(len(shapes))}
+        say(f"[norm extremes {prec}] step {st}")
+        opt.step(W, G, M, 0.02, 0.95, 5)
+        torch.cuda.synchronize()
+        check_step(opt, W, M, G_host, W_pre, M_pre, R, 0.02, 0.95, 5, prec,
+                   list(range(len(shapes))), f"norm extremes {prec} step {st}")
