@@ -399,8 +399,6 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
   const int mat = g.first + m;
   float* w = W[mat];
   const char* D = g.ns_base + (int64_t)m * g.mat_bytes + g.offD;
-  int64_t lo, hi;
-  chunk_range(g.n, g.bpm, c, lo, hi);
   const float nlr = -lr;
   float scale = 1.f;
   if (kProject) {
@@ -410,33 +408,48 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
   float acc = 0.f;
   const int cols = g.cols;
   if ((cols & 3) == 0 && aligned16(w)) {
-    // 4 consecutive elements share a row; walk (row, col) incrementally.
-    const int64_t e0 = lo + 4 * (int64_t)threadIdx.x;
-    int64_t r = e0 / cols;
-    int col = (int)(e0 - r * cols);
-    const int step = 4 * kThreads;
-    const int dr = step / cols, dc = step - (step / cols) * cols;
-    for (int64_t e = e0; e < hi; e += step) {
-      float4 wv = *reinterpret_cast<const float4*>(w + e);
-      const float4 ov = Fmt<F>::load4(D, r, col, g.cp);
-      wv.x = fmaf(nlr, ov.x, wv.x);
-      wv.y = fmaf(nlr, ov.y, wv.y);
-      wv.z = fmaf(nlr, ov.z, wv.z);
-      wv.w = fmaf(nlr, ov.w, wv.w);
-      if (kProject) {
-        wv.x *= scale; wv.y *= scale; wv.z *= scale; wv.w *= scale;
-        *reinterpret_cast<float4*>(w + e) = wv;
-      } else {
-        acc = fmaf(wv.x, wv.x, acc);
-        acc = fmaf(wv.y, wv.y, acc);
-        acc = fmaf(wv.z, wv.z, acc);
-        acc = fmaf(wv.w, wv.w, acc);
+    // Work unit: 4 consecutive columns of the row pair (2p, 2p + 1). The two
+    // rows' O values share 128-byte lines of the panel layout (panel rows r
+    // and r + 1 are adjacent 64-byte halves), so each line is read once.
+    // Block c takes units [u0, u1); (pair, column group) walk incrementally.
+    const int cq = cols >> 2;
+    const int64_t npairs = (int64_t)(g.rows + 1) >> 1;
+    int64_t u0, u1;
+    chunk_range(npairs * cq, g.bpm, c, u0, u1);
+    int64_t u = u0 + threadIdx.x;
+    int64_t pr = u / cq;
+    int q = (int)(u - pr * cq);
+    const int dpr = kThreads / cq, dq = kThreads - (kThreads / cq) * cq;
+    for (; u < u1; u += kThreads) {
+      const int col = q << 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t r = 2 * pr + h;
+        if (h == 1 && r >= g.rows) break;
+        float* wp = w + r * cols + col;
+        float4 wv = *reinterpret_cast<const float4*>(wp);
+        const float4 ov = Fmt<F>::load4(D, r, col, g.cp);
+        wv.x = fmaf(nlr, ov.x, wv.x);
+        wv.y = fmaf(nlr, ov.y, wv.y);
+        wv.z = fmaf(nlr, ov.z, wv.z);
+        wv.w = fmaf(nlr, ov.w, wv.w);
+        if (kProject) {
+          wv.x *= scale; wv.y *= scale; wv.z *= scale; wv.w *= scale;
+          *reinterpret_cast<float4*>(wp) = wv;
+        } else {
+          acc = fmaf(wv.x, wv.x, acc);
+          acc = fmaf(wv.y, wv.y, acc);
+          acc = fmaf(wv.z, wv.z, acc);
+          acc = fmaf(wv.w, wv.w, acc);
+        }
       }
-      col += dc;
-      r += dr;
-      if (col >= cols) { col -= cols; ++r; }
+      q += dq;
+      pr += dpr;
+      if (q >= cq) { q -= cq; ++pr; }
     }
   } else {
+    int64_t lo, hi;
+    chunk_range(g.n, g.bpm, c, lo, hi);
     for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
       const int64_t r = e / cols;
       const int col = (int)(e - r * cols);
