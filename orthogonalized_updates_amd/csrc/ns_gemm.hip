@@ -837,16 +837,21 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
     }
   };
 
-  // Row-major pass: LDS tile [row][col], 16-byte chunk c of row r stored at
-  // position c ^ (r & 31). A quad transpose first gives each lane 4
-  // consecutive columns of one row, so the LDS writes are 8-byte writes.
+  // Row-major pass, straight from registers: a quad transpose gives each
+  // lane 4 consecutive columns (8 bytes) of one row; for one 32x32 block and
+  // accumulator group, lanes 0-31 then hold 4 consecutive rows x 32 columns
+  // and lanes 32-63 the next 4 rows, i.e. 8 consecutive 64-byte panel rows:
+  // 512 contiguous bytes per store in the bf16 panel layout (split: the hi
+  // or lo halves of the rows of two adjacent panels).
   auto pass_rows = [&](const bf16x4 (&v)[kMT][kNT][4], bool lo) {
-    __syncthreads();
+    char* region = O1 + (int64_t)bi * kBM * g.ldo1 * kEB + (int64_t)bj * (256 / kPK) * kPanel;
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
       for (int ni = 0; ni < kNT; ++ni) {
-        const int col = wn0 + ni * 32 + (lane & 28);  // first of the quad's 4 columns
+        const int col = wn0 + ni * 32 + (lane & 28);  // first of the lane's 4 columns
+        const int64_t cpart = SPLIT ? (int64_t)(col >> 4) * kPanel + ((col & 15) << 1) + (lo ? 32 : 0)
+                                    : (int64_t)(col >> 5) * kPanel + ((col & 31) << 1);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int row = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5) + (lane & 3);
@@ -856,12 +861,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
           quad_transpose(d0, d1, lane);
           d.x = d0;
           d.y = d1;
-          const int off = ((((col >> 3) ^ (row & 31)) << 4) | ((col & 7) << 1));
-          *reinterpret_cast<u32x2*>(srow(row) + off) = d;
+          *reinterpret_cast<u32x2*>(region + cpart + row * kPRow) = d;
         }
       }
-    __syncthreads();
-    store_tile(O1, g.ldo1, bi, bj, lo);
   };
   // Transposed pass: LDS tile [col][row], 16-byte chunk c of LDS row j
   // stored at position c ^ (j & 31).
