@@ -35,10 +35,10 @@
  *     Pointers that are 16-byte aligned take the vector path; others work
  *     through a scalar path. W, G and M must not overlap.
  *   - The workspace is a DEVICE buffer of at least muonh_workspace_bytes(plan)
- *     bytes, 256-byte aligned, owned by the caller. It holds the bf16 (split
- *     bf16, fp32)
- *     Newton-Schulz operands and the norm partials. Its contents after a step
- *     hold that step's update O until the next call that uses it.
+ *     bytes, 256-byte aligned, owned by the caller. It holds the
+ *     Newton-Schulz operands (bf16, split bf16 or fp32 by plan flag) and the
+ *     norm partials. After a step it holds that step's update O until the
+ *     next call that uses it.
  *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
  *     NULL is the default stream). No call synchronises the device.
  *   - Calls that share a workspace must be ordered by the caller (same stream,
@@ -79,7 +79,11 @@ enum {
 
 /* Plan flags (at most one). Default: Newton-Schulz operands in bf16, bf16
  * MFMA with fp32 accumulation; about 1e-2 relative error of O at 5
- * iterations, about 2e-2 at 8. */
+ * iterations, about 2e-2 at 8. With bf16 or split operands and
+ * ns_iters >= 1, X0's factor 1/(||M||_F + 1e-7) is applied inside the first
+ * iteration's products rather than before rounding M to the operand format
+ * (the same value up to that rounding; momentum norms outside
+ * [2^-40, 2^40] are normalised first). */
 enum {
   /* fp32 operands and fp32 MFMA. Debug/reference mode: about 1e-6 relative
    * error, an order of magnitude slower. */
