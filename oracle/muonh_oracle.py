@@ -127,3 +127,21 @@ def muonh_step(w, g, m, radius: float, lr: float, beta: float, ns_iters: int,
 def trial_norm(w, o, lr: float) -> float:
     """||W - lr*O||_F, the normaliser of the projection (for diagnostics)."""
     return frobenius_norm(_f64(w) - float(lr) * _f64(o))
+
+
+def muon_wd_step(w, g, m, lr: float, beta: float, weight_decay: float, ns_iters: int,
+                 coeffs=NS_COEFFS, eps: float = NS_EPS):
+    """Muon with decoupled weight decay: the baseline MuonH is measured against.
+
+    The digest page ("The load-bearing tricks aren't in the abstract" and its
+    footnote 3) quotes MuonH's speedup against standard weight decay, and the
+    report page (part 6/7, section 4.3 "Cost Estimation") its compute
+    multiplier relative to Muon. Neither prints the baseline's update. Reading:
+    the same momentum and Newton-Schulz orthogonalisation as MuonH, then weight
+    decay decoupled from the update, W <- (1 - lr*wd) W - lr O, and no
+    projection. Returns (W_new, M_new, O) in float64.
+    """
+    m_new = momentum_update(m, g, beta)
+    o = newton_schulz(m_new, ns_iters, coeffs, eps)
+    w_new = (1.0 - lr * weight_decay) * _f64(w) - lr * o
+    return w_new, m_new, o

@@ -53,6 +53,28 @@ def main() -> None:
     lines.append(" ".join(f"{v:.17g}" for v in vals))
     (here / "projection_2x3.txt").write_text("\n".join(lines) + "\n")
 
+    # Muon with decoupled weight decay on a rank-one momentum, exact: with
+    # M = u v^T, ||u|| = ||v|| = 1, X0 = M / (1 + eps) has the single singular
+    # value s0 = 1/(1 + eps), so O = p^5(s0) u v^T, and
+    # W_new = (1 - lr wd) W - lr O.
+    eps = Fraction(1, 10 ** 7)
+    u = [Fraction(3, 5), Fraction(4, 5)]
+    v = [Fraction(2, 3), Fraction(1, 3), Fraction(2, 3)]
+    w = [[1, -2, 3], [0, 5, -1]]
+    lr, wd = Fraction(1, 50), Fraction(1, 10)
+    s5 = orbit(1 / (1 + eps), 5)[5]
+    wn = [[(1 - lr * wd) * w[i][j] - lr * s5 * u[i] * v[j] for j in range(3)] for i in range(2)]
+    lines = [
+        "# Muon with decoupled weight decay, W <- (1 - lr wd) W - lr O, O = NS_5(M)",
+        "# (the baseline MuonH is measured against: digest page, section \"The",
+        "# load-bearing tricks aren't in the abstract\"; report part 6/7, 4.3).",
+        "# W = [[1,-2,3],[0,5,-1]], M0 = 0, G = u v^T with u = (3/5, 4/5),",
+        "# v = (2/3, 1/3, 2/3), lr = 1/50, wd = 1/10, 5 iterations, eps = 1e-7:",
+        "# O = p^5(1/(1+eps)) u v^T exactly. Row-major expected W_new:",
+        " ".join(f"{float(x):.17g}" for row in wn for x in row),
+    ]
+    (here / "muon_wd_2x3.txt").write_text("\n".join(lines) + "\n")
+
 
 if __name__ == "__main__":
     main()

@@ -474,3 +474,78 @@ def test_bf16_floor_by_shape(shape, k, limit):
     from bf16_floor import floor
     m = rand(shape, (20, shape[0]), 0.01)
     assert floor(m, k, oracle.newton_schulz(m, k)) < limit
+
+
+# ----------------------------------------------------------------------------
+# Muon with decoupled weight decay (the baseline MuonH is measured against)
+# ----------------------------------------------------------------------------
+
+def _muon_golden_inputs():
+    u = np.array([3 / 5, 4 / 5])
+    v = np.array([2 / 3, 1 / 3, 2 / 3])
+    w = np.array([[1.0, -2.0, 3.0], [0.0, 5.0, -1.0]])
+    return w, np.outer(u, v)
+
+
+def _golden_muon_wd():
+    rows = [l for l in (GOLDEN / "muon_wd_2x3.txt").read_text().splitlines() if not l.startswith("#")]
+    return np.array([float(x) for x in rows[0].split()]).reshape(2, 3)
+
+
+def check_muon_golden(step):
+    w, g = _muon_golden_inputs()
+    w_new, m_new, o = step(w, g, np.zeros_like(g), 0.02, 0.95, 0.1, 5)
+    return np.allclose(w_new, _golden_muon_wd(), rtol=0, atol=1e-13)
+
+
+def check_muon_decay_only(step):
+    w = rand((6, 9), (24, 0), 0.02)
+    z = np.zeros_like(w)
+    w_new, m_new, o = step(w, z, z, 0.02, 0.9, 0.1, 5)
+    return np.array_equal(w_new, (1.0 - 0.02 * 0.1) * w) and not np.any(o)
+
+
+def test_muon_wd_golden():
+    # exact-rational expected values (tests/golden/make_golden.py)
+    assert check_muon_golden(oracle.muon_wd_step)
+
+
+def test_muon_wd_decay_only():
+    assert check_muon_decay_only(oracle.muon_wd_step)
+
+
+def test_muon_wd_without_decay_is_the_muonh_trial_update():
+    # wd = 0: W - lr*O, i.e. MuonH's W' before the projection; projecting it
+    # gives MuonH's result.
+    w = rand((24, 40), (25, 0), 0.02)
+    g = rand((24, 40), (25, 1), 0.01)
+    m = rand((24, 40), (25, 2), 0.01)
+    w_new, m_new, o = oracle.muon_wd_step(w, g, m, 0.02, 0.95, 0.0, 5)
+    np.testing.assert_allclose(w_new, w - 0.02 * o, rtol=0, atol=1e-15)
+    r = oracle.init_radius(w)
+    w_h, m_h, o_h = oracle.muonh_step(w, g, m, r, 0.02, 0.95, 5)
+    np.testing.assert_array_equal(o, o_h)
+    np.testing.assert_allclose(w_h, r * w_new / np.linalg.norm(w_new), rtol=1e-14, atol=0)
+
+
+def _muon_mutant(kind):
+    def step(w, g, m, lr, beta, wd, k):
+        m_new = oracle.momentum_update(m, g, beta)
+        o = oracle.newton_schulz(m_new, k)
+        w = np.asarray(w, dtype=np.float64)
+        if kind == "coupled":
+            w_new = (1.0 - lr * wd) * (w - lr * o)
+        elif kind == "plus_decay":
+            w_new = (1.0 + lr * wd) * w - lr * o
+        elif kind == "decay_on_update":
+            w_new = w - lr * (o + wd * o)
+        else:  # "no_decay"
+            w_new = w - lr * o
+        return w_new, m_new, o
+    return step
+
+
+@pytest.mark.parametrize("kind", ["coupled", "plus_decay", "decay_on_update", "no_decay"])
+def test_planted_muon_wd_mistake_is_caught(kind):
+    step = _muon_mutant(kind)
+    assert not (check_muon_golden(step) and check_muon_decay_only(step))
