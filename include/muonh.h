@@ -167,9 +167,33 @@ int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const
                      int32_t n_events);
 
 /*
- * Copy the update O of matrix `index` computed by the last muonh_step that
- * used this workspace into dst, a DEVICE buffer of rows x cols fp32
- * (row-major, the matrix's own orientation). For inspection and tests.
+ * The baseline MuonH is measured against: Muon with decoupled weight decay
+ * (the digest page quotes MuonH's speedup against standard weight decay,
+ * section "The load-bearing tricks aren't in the abstract"; the report page,
+ * part 6/7, section 4.3 "Cost Estimation", its compute multiplier relative to
+ * Muon; neither prints the update). The same momentum and Newton-Schulz as
+ * muonh_step, then
+ *   W <- (1 - lr*weight_decay) * W - lr*O
+ * with no projection and no radius. Same plan, workspace and conventions as
+ * muonh_step (the two may share a plan; W and M are updated in place).
+ * weight_decay: finite, >= 0. Errors: as muonh_step.
+ */
+int muonh_step_muon_wd(const muonh_plan* plan, float* const* W, const float* const* G,
+                       float* const* M, float lr, float beta, float weight_decay,
+                       int32_t ns_iters, void* workspace, size_t workspace_bytes, void* stream);
+
+/* muonh_step_muon_wd with the phase events of muonh_step_timed (the last one
+ * after the decayed update). */
+int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const float* const* G,
+                             float* const* M, float lr, float beta, float weight_decay,
+                             int32_t ns_iters, void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events, int32_t n_events);
+
+/*
+ * Copy the update O of matrix `index` computed by the last muonh_step (or
+ * muonh_step_muon_wd) that used this workspace into dst, a DEVICE buffer of
+ * rows x cols fp32 (row-major, the matrix's own orientation). For inspection
+ * and tests.
  * Errors: MUONH_EINVAL, MUONH_ESHAPE (index out of range), MUONH_EWORKSPACE,
  * MUONH_EHIP.
  */

@@ -67,6 +67,9 @@ def _load_library() -> ctypes.CDLL:
         "muonh_step": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp, sz, vp]),
         "muonh_step_timed": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp, sz, vp,
                                             ctypes.POINTER(vp), i32]),
+        "muonh_step_muon_wd": (ctypes.c_int, [vp, vp, vp, vp, f32, f32, f32, i32, vp, sz, vp]),
+        "muonh_step_muon_wd_timed": (ctypes.c_int, [vp, vp, vp, vp, f32, f32, f32, i32, vp, sz,
+                                                    vp, ctypes.POINTER(vp), i32]),
         "muonh_read_update": (ctypes.c_int, [vp, i64, vp, vp, sz, vp]),
         "muonh_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "muonh_last_error": (ctypes.c_char_p, []),
@@ -259,6 +262,23 @@ class MuonH:
                                    self._R_plan.data_ptr(), float(lr), float(beta), int(ns_iters),
                                    self.workspace.data_ptr(), self.workspace.numel(),
                                    self._stream(), arr, len(events)))
+
+    def step_muon_wd(self, weights, grads, moms, lr: float, beta: float = 0.95,
+                     weight_decay: float = 0.1, ns_iters: int = 5, events=None) -> None:
+        """The baseline MuonH is measured against: Muon with decoupled weight
+        decay, W <- (1 - lr*wd) W - lr O (no projection, no radius). With
+        `events` (as for step_timed), records the phase boundaries."""
+        self._check(weights, "weights")
+        self._check(grads, "grads")
+        self._check(moms, "moms")
+        args = [self.plan.handle, self._ptr_array("W", weights), self._ptr_array("G", grads),
+                self._ptr_array("M", moms), float(lr), float(beta), float(weight_decay),
+                int(ns_iters), self.workspace.data_ptr(), self.workspace.numel(), self._stream()]
+        if events is None:
+            check(get_lib().muonh_step_muon_wd(*args))
+        else:
+            arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+            check(get_lib().muonh_step_muon_wd_timed(*args, arr, len(events)))
 
     def read_update(self, index: int):
         """The update O of matrix `index` from the last step (fp32, rows x cols)."""

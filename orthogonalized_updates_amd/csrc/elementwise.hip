@@ -384,13 +384,20 @@ __global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const floa
 }
 
 // --------------------------------------------------------------------------
-// Trial update W' = W - lr*O (O read from D) and partial sums of squares of
-// W'; the projection recomputes W' identically and rescales it.
+// Updates that read O from D, by mode:
+//   kTrialNorm  W' = W - lr*O, partial sums of squares of W' (W unchanged);
+//   kProject    W <- (R / ||W'||) W', W' recomputed identically;
+//   kDecay      W <- keep*W - lr*O with keep = 1 - lr*wd (Muon with
+//               decoupled weight decay; no norm).
 // --------------------------------------------------------------------------
-template <int F, bool kProject>
+enum UpdateMode : int { kTrialNorm = 0, kProjectMode = 1, kDecay = 2 };
+
+template <int F, int kMode>
 __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, float lr,
                                                      double* partials, const float* R,
-                                                     const double* norms) {
+                                                     const double* norms, float keep) {
+  constexpr bool kProject = kMode == kProjectMode;
+  constexpr bool kWrite = kMode != kTrialNorm;
   __shared__ double red[4];
   const int gi = group_of_block(a, blockIdx.x);
   const EwGroup& g = a.g[gi];
@@ -429,12 +436,17 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
         float* wp = w + r * cols + col;
         float4 wv = *reinterpret_cast<const float4*>(wp);
         const float4 ov = Fmt<F>::load4(D, r, col, g.cp);
+        if (kMode == kDecay) {
+          wv.x *= keep; wv.y *= keep; wv.z *= keep; wv.w *= keep;
+        }
         wv.x = fmaf(nlr, ov.x, wv.x);
         wv.y = fmaf(nlr, ov.y, wv.y);
         wv.z = fmaf(nlr, ov.z, wv.z);
         wv.w = fmaf(nlr, ov.w, wv.w);
-        if (kProject) {
-          wv.x *= scale; wv.y *= scale; wv.z *= scale; wv.w *= scale;
+        if (kWrite) {
+          if (kProject) {
+            wv.x *= scale; wv.y *= scale; wv.z *= scale; wv.w *= scale;
+          }
           *reinterpret_cast<float4*>(wp) = wv;
         } else {
           acc = fmaf(wv.x, wv.x, acc);
@@ -453,15 +465,16 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     for (int64_t e = lo + threadIdx.x; e < hi; e += kThreads) {
       const int64_t r = e / cols;
       const int col = (int)(e - r * cols);
-      float v = fmaf(nlr, Fmt<F>::load(D, r, col, g.cp), w[e]);
-      if (kProject) {
-        w[e] = v * scale;
+      const float wv = kMode == kDecay ? keep * w[e] : w[e];
+      float v = fmaf(nlr, Fmt<F>::load(D, r, col, g.cp), wv);
+      if (kWrite) {
+        w[e] = kProject ? v * scale : v;
       } else {
         acc = fmaf(v, v, acc);
       }
     }
   }
-  if (!kProject) {
+  if (!kWrite) {
     const double t = block_sum((double)acc, red);
     if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = t;
   }
@@ -509,8 +522,9 @@ hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norm
   }
 
 #define K_NORMCAST(F) k_normcast<F>
-#define K_UPDATE(F) (k_update<F, false>)
-#define K_PROJECT(F) (k_update<F, true>)
+#define K_UPDATE(F) (k_update<F, kTrialNorm>)
+#define K_PROJECT(F) (k_update<F, kProjectMode>)
+#define K_DECAY(F) (k_update<F, kDecay>)
 #define K_READ(F) k_read_update<F>
 
 hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
@@ -541,14 +555,21 @@ hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, const float* const
 hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, float lr,
                               double* partials, hipStream_t s) {
   MUONH_PREC_DISPATCH(prec, K_UPDATE, dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr, partials,
-                      nullptr, nullptr)
+                      nullptr, nullptr, 1.f)
   return hipGetLastError();
 }
 
 hipError_t launch_project(const EwArgs& a, NsPrec prec, float* const* W, const float* R,
                           const double* norms, float lr, hipStream_t s) {
   MUONH_PREC_DISPATCH(prec, K_PROJECT, dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr, nullptr,
-                      R, norms)
+                      R, norms, 1.f)
+  return hipGetLastError();
+}
+
+hipError_t launch_decay_update(const EwArgs& a, NsPrec prec, float* const* W, float lr, float keep,
+                               hipStream_t s) {
+  MUONH_PREC_DISPATCH(prec, K_DECAY, dim3(a.nblocks), dim3(kThreads), 0, s, a, W, lr, nullptr,
+                      nullptr, nullptr, keep)
   return hipGetLastError();
 }
 

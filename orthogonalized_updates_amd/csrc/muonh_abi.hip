@@ -444,11 +444,23 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
 
 namespace {
 
+// The update after Newton-Schulz: MuonH (trial update, its norm, projection
+// onto the radius-R sphere), or Muon with decoupled weight decay.
+struct Variant {
+  bool muon_wd;
+  float weight_decay;
+};
+
 int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
               const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
-              size_t workspace_bytes, void* stream, void* const* events, int32_t n_events) {
+              size_t workspace_bytes, void* stream, void* const* events, int32_t n_events,
+              Variant var = {false, 0.f}) {
   if (!plan) return fail(MUONH_EINVAL, "plan is NULL");
-  if (!W || !G || !M || !R) return fail(MUONH_EINVAL, "W, G, M and R must be device arrays");
+  if (!W || !G || !M || (!R && !var.muon_wd))
+    return fail(MUONH_EINVAL, var.muon_wd ? "W, G and M must be device arrays"
+                                          : "W, G, M and R must be device arrays");
+  if (var.muon_wd && (!std::isfinite(var.weight_decay) || var.weight_decay < 0.f))
+    return fail(MUONH_EINVAL, "weight_decay=%g must be finite and >= 0", var.weight_decay);
   if (!std::isfinite(lr) || lr < 0.f) return fail(MUONH_EINVAL, "lr=%g must be finite and >= 0", lr);
   if (!std::isfinite(beta) || beta < 0.f || beta >= 1.f)
     return fail(MUONH_EINVAL, "beta=%g must be in [0, 1)", beta);
@@ -519,13 +531,20 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
   }
 
-  for (const EwArgs& a : stream_args) {
-    if ((e = launch_update_norm(a, plan->prec, W, lr, partials, s)) != hipSuccess)
-      return hip_fail(e, "update norm");
-    if ((e = launch_finalize(a, partials, norm_w, nullptr, s)) != hipSuccess)
-      return hip_fail(e, "update finalize");
-    if ((e = launch_project(a, plan->prec, W, R, norm_w, lr, s)) != hipSuccess)
-      return hip_fail(e, "project");
+  if (var.muon_wd) {
+    const float keep = (float)(1.0 - (double)lr * (double)var.weight_decay);
+    for (const EwArgs& a : stream_args)
+      if ((e = launch_decay_update(a, plan->prec, W, lr, keep, s)) != hipSuccess)
+        return hip_fail(e, "decayed update");
+  } else {
+    for (const EwArgs& a : stream_args) {
+      if ((e = launch_update_norm(a, plan->prec, W, lr, partials, s)) != hipSuccess)
+        return hip_fail(e, "update norm");
+      if ((e = launch_finalize(a, partials, norm_w, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "update finalize");
+      if ((e = launch_project(a, plan->prec, W, R, norm_w, lr, s)) != hipSuccess)
+        return hip_fail(e, "project");
+    }
   }
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
   return MUONH_OK;
@@ -549,6 +568,22 @@ int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const
   if (!events) return fail(MUONH_EINVAL, "events is NULL");
   return step_impl(plan, W, G, M, R, lr, beta, ns_iters, workspace, workspace_bytes, stream,
                    events, n_events);
+}
+
+int muonh_step_muon_wd(const muonh_plan* plan, float* const* W, const float* const* G,
+                       float* const* M, float lr, float beta, float weight_decay,
+                       int32_t ns_iters, void* workspace, size_t workspace_bytes, void* stream) {
+  return step_impl(plan, W, G, M, nullptr, lr, beta, ns_iters, workspace, workspace_bytes, stream,
+                   nullptr, 0, Variant{true, weight_decay});
+}
+
+int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const float* const* G,
+                             float* const* M, float lr, float beta, float weight_decay,
+                             int32_t ns_iters, void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events, int32_t n_events) {
+  if (!events) return fail(MUONH_EINVAL, "events is NULL");
+  return step_impl(plan, W, G, M, nullptr, lr, beta, ns_iters, workspace, workspace_bytes, stream,
+                   events, n_events, Variant{true, weight_decay});
 }
 
 int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const void* workspace,

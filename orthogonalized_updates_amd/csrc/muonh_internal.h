@@ -102,6 +102,9 @@ hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, flo
                               double* partials, hipStream_t s);
 hipError_t launch_project(const EwArgs& a, NsPrec prec, float* const* W, const float* R,
                           const double* norms, float lr, hipStream_t s);
+// W <- keep*W - lr*O (Muon with decoupled weight decay, keep = 1 - lr*wd).
+hipError_t launch_decay_update(const EwArgs& a, NsPrec prec, float* const* W, float lr, float keep,
+                               hipStream_t s);
 // dst (rows x cols fp32) <- D of one matrix.
 hipError_t launch_read_update(NsPrec prec, const char* D, int ldD, int rows, int cols, float* dst,
                               hipStream_t s);

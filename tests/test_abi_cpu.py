@@ -22,7 +22,8 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("muonh_plan_create", "muonh_plan_destroy", "muonh_workspace_bytes", "muonh_init",
-              "muonh_step", "muonh_read_update", "muonh_last_error", "muonh_status_string"):
+              "muonh_step", "muonh_step_timed", "muonh_step_muon_wd", "muonh_step_muon_wd_timed",
+              "muonh_read_update", "muonh_last_error", "muonh_status_string"):
         assert n in names
 
 
@@ -124,6 +125,35 @@ def test_step_rejects_bad_scalars(lr, beta, iters, code):
     st = mh.lib.muonh_step(p.handle, f.ptr, f.ptr, f.ptr, f.ptr, lr, beta, iters, f.ws,
                            p.workspace_bytes, None)
     assert st == code
+
+
+@pytest.mark.parametrize("wd,lr,code", [
+    (-0.1, 0.02, mh.MUONH_EINVAL),
+    (float("nan"), 0.02, mh.MUONH_EINVAL),
+    (float("inf"), 0.02, mh.MUONH_EINVAL),
+    (0.1, float("nan"), mh.MUONH_EINVAL),
+])
+def test_muon_wd_step_rejects_bad_scalars(wd, lr, code):
+    p = mh.Plan([(8, 8, 1)])
+    f = _FakeDev
+    st = mh.lib.muonh_step_muon_wd(p.handle, f.ptr, f.ptr, f.ptr, lr, 0.95, wd, 5, f.ws,
+                                   p.workspace_bytes, None)
+    assert st == code
+    assert "weight_decay" in mh.lib.muonh_last_error().decode() or lr != lr
+
+
+def test_muon_wd_step_rejects_null_arrays_and_events():
+    p = mh.Plan([(8, 8, 1)])
+    f = _FakeDev
+    n = p.workspace_bytes
+    assert mh.lib.muonh_step_muon_wd(None, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 0.1, 5, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step_muon_wd(p.handle, f.ptr, None, f.ptr, 0.02, 0.9, 0.1, 5, f.ws, n, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step_muon_wd(p.handle, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 0.1, 5, f.ws, n - 1, None) == mh.MUONH_EWORKSPACE
+    assert mh.lib.muonh_step_muon_wd_timed(p.handle, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 0.1, 5, f.ws, n, None,
+                                           None, 18) == mh.MUONH_EINVAL
+    ev = (ctypes.c_void_p * 4)(*([0x1000] * 4))
+    assert mh.lib.muonh_step_muon_wd_timed(p.handle, f.ptr, f.ptr, f.ptr, 0.02, 0.9, 0.1, 5, f.ws, n, None,
+                                           ev, 4) == mh.MUONH_EINVAL  # needs 3*5+3 events
 
 
 def test_step_rejects_null_and_workspace_problems():

@@ -456,3 +456,102 @@ def test_momentum_norm_extremes(prec):
         torch.cuda.synchronize()
         check_step(opt, W, M, G_host, W_pre, M_pre, R, 0.02, 0.95, 5, prec,
                    list(range(len(shapes))), f"norm extremes {prec} step {st}")
+
+
+# ---------------------------------------------------------------------------
+# Muon with decoupled weight decay (muonh_step_muon_wd): same momentum and
+# Newton-Schulz, then W <- (1 - lr*wd) W - lr O. O and M as for MuonH. W is
+# checked against the oracle's update applied to the GPU's own O, and against
+# the oracle's full step within lr*||dO||. The two terms can cancel (a small
+# matrix whose decayed W nearly equals lr*O), so the fp32 part of both bounds
+# is relative to the terms, not to the result: per element the GPU rounds
+# (1 - lr*wd)*w once and the fused multiply-add once, i.e. a few ulps of
+# |w| + lr*|o|; 1e-6 * (||W|| + lr*||O||) allows about 16.
+# ---------------------------------------------------------------------------
+
+def check_muon_step(opt, W, M, G, W_pre, M_pre, lr, beta, wd, k, prec, indices, label):
+    for i in indices:
+        o_gpu = opt.read_update(i).cpu().numpy()
+        w_gpu = W[i].cpu().numpy()
+        m_gpu = M[i].cpu().numpy()
+        g = G[i].cpu().numpy() if hasattr(G[i], "cpu") else G[i]
+        w_o, m_o, o_o = oracle.muon_wd_step(W_pre[i], g, M_pre[i], lr, beta, wd, k)
+        e_o = rel(o_gpu, o_o)
+        tol_o = TOL_O[prec]
+        if prec != "fp32" and e_o > tol_o:
+            fl = bf16_floor(oracle.momentum_update(M_pre[i], g, beta), k, o_o, prec)
+            tol_o = max(tol_o, 1.3 * fl)
+        assert e_o <= tol_o, f"{label} mat {i}: O rel err {e_o:.3e} > {tol_o:.3e}"
+        assert rel(m_gpu, m_o) <= 1e-6, f"{label} mat {i}: M"
+        w_pre = W_pre[i].astype(np.float64)
+        w_own = (1.0 - lr * wd) * w_pre - lr * o_gpu
+        fp32 = 1e-6 * (np.linalg.norm(w_pre) + lr * np.linalg.norm(o_gpu))
+        d_own = np.linalg.norm(w_gpu - w_own)
+        assert d_own <= fp32, f"{label} mat {i}: W vs decayed update of GPU O: {d_own:.3e} > {fp32:.3e}"
+        d_full = np.linalg.norm(w_gpu - w_o)
+        bound = 1.5 * lr * np.linalg.norm(o_gpu - o_o) + fp32
+        assert d_full <= bound, f"{label} mat {i}: W vs oracle step: {d_full:.3e} > {bound:.3e}"
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("k", [0, 5])
+def test_muon_wd_ragged_groups(prec, k):
+    need_gpu()
+    dev = torch.device("cuda")
+    wl = workloads.Workload(wid=73, name="muon", shapes=tuple(RAGGED), steps=3, ns_iters=(k,),
+                            lr=0.02, beta=0.95, w_std=0.02, g_std=0.01, heavy_tail=False)
+    opt = make_opt(RAGGED, prec)
+    W = [torch.from_numpy(workloads.host_weight(wl, i)).to(dev) for i in range(len(RAGGED))]
+    M = [torch.zeros(s, device=dev) for s in RAGGED]
+    idx = list(range(len(RAGGED)))
+    for st in range(3):
+        G_host = [workloads.host_grad(wl, i, st) for i in idx]
+        G = [torch.from_numpy(g).to(dev) for g in G_host]
+        W_pre = {i: W[i].cpu().numpy() for i in idx}
+        M_pre = {i: M[i].cpu().numpy() for i in idx}
+        say(f"[muon-wd {prec} k={k}] step {st}")
+        opt.step_muon_wd(W, G, M, 0.02, 0.95, 0.1, k)
+        torch.cuda.synchronize()
+        check_muon_step(opt, W, M, G_host, W_pre, M_pre, 0.02, 0.95, 0.1, k, prec, idx,
+                        f"muon-wd {prec} k={k} step {st}")
+
+
+def test_muon_wd_decay_only():
+    need_gpu()
+    shapes = [(64, 96), (96, 64)]
+    opt, W, M = _setup(shapes)
+    W0 = [w.cpu().numpy().astype(np.float64) for w in W]
+    G = [torch.zeros(s, device="cuda") for s in shapes]
+    opt.step_muon_wd(W, G, M, 0.02, 0.9, 0.1, 5)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert rel(W[i].cpu().numpy(), (1 - 0.02 * 0.1) * W0[i]) <= 1e-7
+        assert torch.count_nonzero(opt.read_update(i)) == 0
+
+
+def test_muon_wd_full_size_sampled_after_a_muonh_step():
+    # one plan and workspace shared by both entry points
+    need_gpu()
+    torch.cuda.empty_cache()
+    wl = workloads.WORKLOADS["qwen3_2b"]
+    dev = torch.device("cuda")
+    opt = make_opt(wl.shapes, "bf16")
+    W = [workloads.device_weight_(wl, i, torch.empty(s, device=dev)) for i, s in enumerate(wl.shapes)]
+    M = [torch.zeros(s, device=dev) for s in wl.shapes]
+    G = [torch.empty(s, device=dev) for s in wl.shapes]
+    opt.init(W)
+    for i, s in enumerate(wl.shapes):
+        workloads.device_grad_(wl, i, 0, G[i])
+    say("[muon-wd qwen3_2b] muonh step")
+    opt.step(W, G, M, wl.lr, wl.beta, 5)
+    for i, s in enumerate(wl.shapes):
+        workloads.device_grad_(wl, i, 1, G[i])
+    sample = list(range(0, 7)) + list(range(27 * 7, 28 * 7)) + [100, 150]
+    W_pre = {i: W[i].cpu().numpy() for i in sample}
+    M_pre = {i: M[i].cpu().numpy() for i in sample}
+    G_host = {i: G[i].cpu().numpy() for i in sample}
+    say("[muon-wd qwen3_2b] muon-wd step")
+    opt.step_muon_wd(W, G, M, wl.lr, wl.beta, 0.1, 5)
+    torch.cuda.synchronize()
+    check_muon_step(opt, W, M, G_host, W_pre, M_pre, wl.lr, wl.beta, 0.1, 5, "bf16", sample,
+                    "muon-wd qwen3_2b")
