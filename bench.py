@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 METRIC = "MuonH step time & params updated/s (2B-shaped set); NS TFLOP/s % MFMA peak"
+METRIC_MUON_WD = ("Muon + decoupled weight decay (the baseline) step time & params updated/s "
+                  "(2B-shaped set); NS TFLOP/s % MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
@@ -50,7 +52,7 @@ def ns_flops(shapes, k):
     return {"gram": gram, "poly": poly, "apply": apply}
 
 
-def elementwise_bytes(n_params, ns_bytes, fused):
+def elementwise_bytes(n_params, ns_bytes, fused, variant="muonh"):
     """Algorithmic HBM bytes of the streaming phases, per step.
 
     before Newton-Schulz: momentum reads G, M and writes M (12 B/param) and
@@ -59,14 +61,18 @@ def elementwise_bytes(n_params, ns_bytes, fused):
       reads M again and, in fp32 mode, writes X and X^T:
       12 + 4 + 2*ns_bytes B/param;
     after: the trial-norm pass reads W and O (4 + ns_bytes), the projection
-      reads W and O and writes W (8 + ns_bytes).
+      reads W and O and writes W (8 + ns_bytes); the Muon baseline's decayed
+      update is one pass that reads W and O and writes W (8 + ns_bytes).
     """
     pre = n_params * (12 + ns_bytes if fused else 12 + 4 + 2 * ns_bytes)
-    post = n_params * (4 + ns_bytes + 8 + ns_bytes)
+    if variant == "muon_wd":
+        post = n_params * (8 + ns_bytes)
+    else:
+        post = n_params * (4 + ns_bytes + 8 + ns_bytes)
     return pre, post
 
 
-def cpu_baseline(wl, k, budget_s):
+def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1):
     """The fp64 oracle on the host, on one matrix of each distinct shape,
     extrapolated by count to the whole set (matrices are independent)."""
     import numpy as np
@@ -91,7 +97,10 @@ def cpu_baseline(wl, k, budget_s):
         runs = 0
         t0 = time.perf_counter()
         while True:
-            oracle.muonh_step(w, g, m, radius, wl.lr, wl.beta, k)
+            if variant == "muon_wd":
+                oracle.muon_wd_step(w, g, m, wl.lr, wl.beta, weight_decay, k)
+            else:
+                oracle.muonh_step(w, g, m, radius, wl.lr, wl.beta, k)
             runs += 1
             el = time.perf_counter() - t0
             if el >= per_shape_budget or runs >= 5:
@@ -105,9 +114,11 @@ def cpu_baseline(wl, k, budget_s):
         "unit": "params/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": ("one fp64 oracle step (momentum, Newton-Schulz k=%d, projection) of one matrix "
+        "sample": ("one fp64 oracle step (momentum, Newton-Schulz k=%d, %s) of one matrix "
                    "per distinct shape, timed over %.1f s and extrapolated by matrix count to the "
-                   "full set (%s); est. %.1f s per full step" % (k, used, "; ".join(parts), total)),
+                   "full set (%s); est. %.1f s per full step"
+                   % (k, "decayed update" if variant == "muon_wd" else "projection", used,
+                      "; ".join(parts), total)),
         "host_cpu": platform.processor() or platform.machine(),
     }
 
@@ -161,6 +172,11 @@ def main() -> int:
                     help="Newton-Schulz operands: bf16 (default), split_bf16 (hi + lo bf16 "
                          "pairs, 3 MFMAs per product) or fp32 (debug mode)")
     ap.add_argument("--ns-fp32", action="store_true", help="same as --precision fp32")
+    ap.add_argument("--variant", default="muonh", choices=["muonh", "muon_wd"],
+                    help="muonh (default): the MuonH step; muon_wd: the Muon baseline with "
+                         "decoupled weight decay on the same plan")
+    ap.add_argument("--weight-decay", type=float, default=0.1,
+                    help="weight decay of the muon_wd variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -208,7 +224,10 @@ def main() -> int:
     torch.cuda.synchronize(dev)
 
     for w in range(args.warmup):
-        opt.step(W, G[w % pool], M, wl.lr, wl.beta, k)
+        if args.variant == "muon_wd":
+            opt.step_muon_wd(W, G[w % pool], M, wl.lr, wl.beta, args.weight_decay, k)
+        else:
+            opt.step(W, G[w % pool], M, wl.lr, wl.beta, k)
     torch.cuda.synchronize(dev)
     print(f"[bench] warmup done ({args.warmup} steps), gradient pool {pool}", file=sys.stderr,
           flush=True)
@@ -224,7 +243,11 @@ def main() -> int:
 
     t0 = time.perf_counter()
     for s in range(args.steps):
-        opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
+        if args.variant == "muon_wd":
+            opt.step_muon_wd(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta,
+                             args.weight_decay, k, events=events[s])
+        else:
+            opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -248,7 +271,8 @@ def main() -> int:
     fp32 = args.precision == "fp32"
     peak_mfma = PEAK_FP32_MFMA_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     ns_bytes = 2 if args.precision == "bf16" else 4
-    pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes, fused=not fp32 and k >= 1)
+    pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes, fused=not fp32 and k >= 1,
+                                      variant=args.variant)
     pre_ms, post_ms = pre / nst, post / nst
     dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
 
@@ -269,7 +293,7 @@ def main() -> int:
                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_MUON_WD if args.variant == "muon_wd" else METRIC,
         "value": wl.n_params * nst / elapsed,
         "unit": "params/s",
         "n_gpus": 1,
@@ -283,7 +307,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.notes}", "matrices": wl.n_matrices,
                    "params": wl.n_params, "ns_iters": k, "lr": wl.lr, "beta": wl.beta,
-                   "master_weights": "fp32", "ns_operands": args.precision},
+                   "master_weights": "fp32", "ns_operands": args.precision,
+                   "update": ("muon_wd (weight_decay=%g)" % args.weight_decay
+                              if args.variant == "muon_wd" else "muonh")},
         "roofline": roofline,
         "phases": {
             "ns_ms": round(ns_ms, 4),
@@ -301,7 +327,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, k, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, k, args.cpu_budget, args.variant,
+                                              args.weight_decay)
     print(json.dumps(result), flush=True)
     return 0
 
