@@ -75,6 +75,36 @@ def main() -> None:
     ]
     (here / "muon_wd_2x3.txt").write_text("\n".join(lines) + "\n")
 
+    # Two AdamW steps with different gradients, computed from the definition
+    # in 50-digit decimal arithmetic (decoupled decay, bias-corrected moments,
+    # eps outside the square root).
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    D = Decimal
+    lr, b1, b2, ep, wd = D("0.001"), D("0.9"), D("0.95"), D("1e-8"), D("0.1")
+    p0 = [D("0.5"), D("-1.25"), D("0.0"), D("2.0")]
+    gs = [[D("0.3"), D("-0.2"), D("0.0"), D("1e-3")], [D("-0.1"), D("-0.4"), D("0.05"), D("2e-3")]]
+    pv, mv, vv = list(p0), [D(0)] * 4, [D(0)] * 4
+    for t, g in enumerate(gs, start=1):
+        for i in range(4):
+            pv[i] = pv[i] * (1 - lr * wd)
+            mv[i] = b1 * mv[i] + (1 - b1) * g[i]
+            vv[i] = b2 * vv[i] + (1 - b2) * g[i] * g[i]
+            mh = mv[i] / (1 - b1 ** t)
+            vh = vv[i] / (1 - b2 ** t)
+            pv[i] = pv[i] - lr * mh / (vh.sqrt() + ep)
+    lines = [
+        "# Two AdamW steps (model card page \"Puro\", section \"Training\": AdamW,",
+        "# weight decay 0.1), from the definition in 50-digit decimal arithmetic:",
+        "# lr = 1e-3, beta1 = 0.9, beta2 = 0.95, eps = 1e-8, wd = 0.1,",
+        "# p0 = (0.5, -1.25, 0, 2), m0 = v0 = 0,",
+        "# g1 = (0.3, -0.2, 0, 1e-3), g2 = (-0.1, -0.4, 0.05, 2e-3).",
+        "# lines: p2, m2, v2",
+    ]
+    for vec in (pv, mv, vv):
+        lines.append(" ".join(f"{float(x):.17g}" for x in vec))
+    (here / "adamw_2step.txt").write_text("\n".join(lines) + "\n")
+
 
 if __name__ == "__main__":
     main()

@@ -549,3 +549,101 @@ def _muon_mutant(kind):
 def test_planted_muon_wd_mistake_is_caught(kind):
     step = _muon_mutant(kind)
     assert not (check_muon_golden(step) and check_muon_decay_only(step))
+
+
+# ----------------------------------------------------------------------------
+# AdamW for the parameters outside the MuonH group
+# ----------------------------------------------------------------------------
+ADAMW_HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def check_adamw_first_step(step_fn):
+    # zero state, step 1: m_hat = g and v_hat = g^2 exactly, so every element
+    # moves by lr * g / (|g| + eps) after the decay
+    p = rand((300,), (26, 0), 1.0)
+    g = rand((300,), (26, 1), 0.01)
+    z = np.zeros_like(p)
+    h = ADAMW_HP
+    p1, m1, v1 = step_fn(p, g, z, z, h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], 1)
+    exp = p * (1 - h["lr"] * h["weight_decay"]) - h["lr"] * g / (np.abs(g) + h["eps"])
+    return np.allclose(p1, exp, rtol=1e-14, atol=1e-17) and np.allclose(m1, 0.1 * g, rtol=1e-14)
+
+
+def check_adamw_constant_gradient(step_fn, steps=7):
+    # constant g from zero state: m_hat = g and v_hat = g^2 at every step, so
+    # p_t = p0 c^t - lr s (1 + c + ... + c^(t-1)), c = 1 - lr wd, s = g/(|g|+eps)
+    h = ADAMW_HP
+    p0 = rand((200,), (27, 0), 1.0)
+    g = rand((200,), (27, 1), 0.01)
+    p, m, v = p0, np.zeros_like(p0), np.zeros_like(p0)
+    for t in range(1, steps + 1):
+        p, m, v = step_fn(p, g, m, v, h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], t)
+    c = 1 - h["lr"] * h["weight_decay"]
+    s = g / (np.abs(g) + h["eps"])
+    exp = p0 * c ** steps - h["lr"] * s * sum(c ** i for i in range(steps))
+    return np.allclose(p, exp, rtol=1e-12, atol=1e-15)
+
+
+def check_adamw_decay_only(step_fn):
+    h = ADAMW_HP
+    p = rand((64,), (28, 0), 1.0)
+    z = np.zeros_like(p)
+    p1, m1, v1 = step_fn(p, z, z, z, h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], 3)
+    return np.array_equal(p1, p * (1 - h["lr"] * h["weight_decay"])) and not np.any(m1) and not np.any(v1)
+
+
+def check_adamw_golden(step_fn):
+    rows = [l for l in (GOLDEN / "adamw_2step.txt").read_text().splitlines() if not l.startswith("#")]
+    p2e, m2e, v2e = (np.array([float(x) for x in r.split()]) for r in rows)
+    p = np.array([0.5, -1.25, 0.0, 2.0])
+    m = v = np.zeros(4)
+    for t, g in enumerate([np.array([0.3, -0.2, 0.0, 1e-3]), np.array([-0.1, -0.4, 0.05, 2e-3])], 1):
+        p, m, v = step_fn(p, g, m, v, 1e-3, 0.9, 0.95, 1e-8, 0.1, t)
+    return (np.allclose(p, p2e, rtol=1e-14, atol=1e-16) and np.allclose(m, m2e, rtol=1e-14)
+            and np.allclose(v, v2e, rtol=1e-14))
+
+
+def test_adamw_first_step_closed_form():
+    assert check_adamw_first_step(oracle.adamw_step)
+
+
+def test_adamw_constant_gradient_closed_form():
+    assert check_adamw_constant_gradient(oracle.adamw_step)
+
+
+def test_adamw_decay_only():
+    assert check_adamw_decay_only(oracle.adamw_step)
+
+
+def test_adamw_two_step_golden():
+    # 50-digit decimal evaluation of the definition (tests/golden/make_golden.py)
+    assert check_adamw_golden(oracle.adamw_step)
+
+
+def _adamw_mutant(kind):
+    def step(p, g, m, v, lr, b1, b2, eps, wd, t):
+        p = np.asarray(p, dtype=np.float64)
+        g = np.asarray(g, dtype=np.float64)
+        if kind == "coupled_l2":
+            g = g + wd * p
+        else:
+            p = p * (1 - lr * wd)
+        m = (b2 if kind == "swapped_betas" else b1) * m + (1 - (b2 if kind == "swapped_betas" else b1)) * g
+        v = (b1 if kind == "swapped_betas" else b2) * v + (1 - (b1 if kind == "swapped_betas" else b2)) * g * g
+        if kind == "no_bias_correction":
+            mh, vh = m, v
+        else:
+            mh, vh = m / (1 - b1 ** t), v / (1 - b2 ** t)
+        if kind == "eps_inside_sqrt":
+            den = np.sqrt(vh + eps)
+        else:
+            den = np.sqrt(vh) + eps
+        return p - lr * mh / den, m, v
+    return step
+
+
+@pytest.mark.parametrize("kind", ["coupled_l2", "no_bias_correction", "eps_inside_sqrt", "swapped_betas"])
+def test_planted_adamw_mistake_is_caught(kind):
+    s = _adamw_mutant(kind)
+    assert not (check_adamw_first_step(s) and check_adamw_constant_gradient(s)
+                and check_adamw_decay_only(s) and check_adamw_golden(s))
