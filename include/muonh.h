@@ -101,6 +101,7 @@ enum {
 #define MUONH_MAX_MATRICES (1 << 20)
 #define MUONH_MAX_DIM 65536      /* rows and cols */
 #define MUONH_MAX_NS_ITERS 32
+#define MUONH_MAX_TENSOR_ELEMS (1LL << 40) /* elements per AdamW tensor */
 
 /* Library ABI version (MUONH_ABI_VERSION of the built library). */
 int32_t muonh_abi_version(void);
@@ -188,6 +189,29 @@ int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const floa
                              float* const* M, float lr, float beta, float weight_decay,
                              int32_t ns_iters, void* workspace, size_t workspace_bytes,
                              void* stream, void* const* events, int32_t n_events);
+
+/*
+ * AdamW for the parameters outside the MuonH group (model card page "Puro",
+ * section "Training": AdamW with weight decay 0.1; the page gives no other
+ * hyperparameter). One step at step number `step` (1-based), per element of
+ * every tensor, in fp32 (decoupled decay, bias-corrected moments):
+ *   p <- p*(1 - lr*weight_decay)
+ *   m <- beta1*m + (1 - beta1)*g ;  v <- beta2*v + (1 - beta2)*g^2
+ *   p <- p - lr*(m/(1 - beta1^step)) / (sqrt(v/(1 - beta2^step)) + eps)
+ * sizes: HOST array of n_tensors element counts (0 allowed, at most
+ *   MUONH_MAX_TENSOR_ELEMS). P, G, M, V: DEVICE arrays of n_tensors DEVICE
+ *   pointers to flat fp32 tensors (parameters, gradients, first and second
+ *   moments); P, M, V are updated in place, G is read. No plan and no
+ *   workspace: tensors go in grouped launches of up to 64 tensors.
+ * lr, weight_decay: finite, >= 0; beta1, beta2 in [0, 1); eps finite, >= 0.
+ * n_tensors == 0 is a no-op. Deterministic; asynchronous on `stream`.
+ * Errors: MUONH_EINVAL (bad scalar, NULL array, step < 1, n_tensors < 0),
+ * MUONH_ESHAPE (a size out of range), MUONH_EHIP.
+ */
+int muonh_adamw_step(int32_t n_tensors, const int64_t* sizes, float* const* P,
+                     const float* const* G, float* const* M, float* const* V, float lr,
+                     float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                     void* stream);
 
 /*
  * Copy the update O of matrix `index` computed by the last muonh_step (or

@@ -71,6 +71,8 @@ def _load_library() -> ctypes.CDLL:
         "muonh_step_muon_wd_timed": (ctypes.c_int, [vp, vp, vp, vp, f32, f32, f32, i32, vp, sz,
                                                     vp, ctypes.POINTER(vp), i32]),
         "muonh_read_update": (ctypes.c_int, [vp, i64, vp, vp, sz, vp]),
+        "muonh_adamw_step": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
+                                            i32, vp]),
         "muonh_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "muonh_last_error": (ctypes.c_char_p, []),
     }
@@ -293,3 +295,64 @@ class MuonH:
 __all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
            "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
            "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32"]
+
+
+class AdamW:
+    """AdamW over a list of fp32 tensors on one GPU: the parameters outside
+    the MuonH group (model card page "Puro", section "Training": AdamW with
+    weight decay 0.1). Any shapes; tensors are treated as flat arrays and
+    updated in place by the library's grouped HIP launch (muonh_adamw_step).
+    """
+
+    def __init__(self, numels: Sequence[int], *, device=None):
+        import torch
+        get_lib()
+        self.torch = torch
+        self.numels = [int(n) for n in numels]
+        if any(n < 0 for n in self.numels):
+            raise ValueError("numels must be >= 0")
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.type != "cuda":
+            raise ValueError("AdamW runs on a ROCm GPU device only")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self._sizes = (ctypes.c_int64 * max(len(self.numels), 1))(*self.numels)
+        self._ptr_cache: Dict[str, Tuple[Tuple[int, ...], object]] = {}
+
+    def _check(self, tensors, name: str):
+        torch = self.torch
+        if len(tensors) != len(self.numels):
+            raise ValueError(f"{name}: expected {len(self.numels)} tensors, got {len(tensors)}")
+        for i, t in enumerate(tensors):
+            if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+                raise TypeError(f"{name}[{i}] must be a float32 torch tensor")
+            if t.device != self.device:
+                raise ValueError(f"{name}[{i}] is on {t.device}, expected {self.device}")
+            if t.numel() != self.numels[i] or not t.is_contiguous():
+                raise ValueError(f"{name}[{i}] must be contiguous with {self.numels[i]} elements")
+
+    def _ptr_array(self, name: str, tensors) -> int:
+        ptrs = tuple(int(t.data_ptr()) for t in tensors)
+        cached = self._ptr_cache.get(name)
+        if cached is None or cached[0] != ptrs:
+            arr = self.torch.tensor(ptrs, dtype=self.torch.int64).to(self.device)
+            self._ptr_cache[name] = (ptrs, arr)
+        return int(self._ptr_cache[name][1].data_ptr())
+
+    def step(self, params, grads, exp_avg, exp_avg_sq, lr: float, beta1: float = 0.9,
+             beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.1,
+             step: int = 1) -> None:
+        """One AdamW step (1-based `step`); params, exp_avg, exp_avg_sq in place."""
+        for ts, nm in ((params, "params"), (grads, "grads"), (exp_avg, "exp_avg"),
+                       (exp_avg_sq, "exp_avg_sq")):
+            self._check(ts, nm)
+        if not self.numels:
+            return
+        stream = int(self.torch.cuda.current_stream(self.device).cuda_stream)
+        check(get_lib().muonh_adamw_step(
+            len(self.numels), ctypes.cast(self._sizes, ctypes.c_void_p),
+            self._ptr_array("P", params), self._ptr_array("G", grads),
+            self._ptr_array("M", exp_avg), self._ptr_array("V", exp_avg_sq),
+            float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step),
+            stream))

@@ -14,7 +14,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libmuonh.so"
-SOURCES = ["muonh_abi.hip", "ns_gemm.hip", "elementwise.hip"]
+SOURCES = ["muonh_abi.hip", "ns_gemm.hip", "elementwise.hip", "adamw.hip"]
 ARCH = "gfx950"
 
 

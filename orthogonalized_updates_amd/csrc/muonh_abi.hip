@@ -27,8 +27,16 @@
 using namespace muonh;
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+// Shared with the other sources of the library (adamw.hip).
+int muonh::set_error(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+namespace {
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {

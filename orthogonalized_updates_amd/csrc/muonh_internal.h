@@ -147,6 +147,9 @@ struct GemmArgs {
   const double* xnorm;
 };
 
+// Sets the calling thread's muonh_last_error() message; returns `code`.
+int set_error(int code, const char* msg);
+
 // Tile edge (square tiles) used by the launchers for the given precision.
 int gemm_tile(NsPrec prec);
 hipError_t launch_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a, hipStream_t s);

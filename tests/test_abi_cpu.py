@@ -185,3 +185,40 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert mh.lib.muonh_status_string(code)
     assert mh.lib.muonh_status_string(7) == b"unknown status"
+
+
+# ----------------------------------------------------------------------------
+# muonh_adamw_step argument validation (nothing is dereferenced)
+# ----------------------------------------------------------------------------
+
+def _adamw_call(n=1, sizes=(8,), lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1, step=1, arrays=True):
+    f = _FakeDev
+    sz = (ctypes.c_int64 * max(len(sizes), 1))(*sizes) if sizes is not None else None
+    a = f.ptr if arrays else None
+    return mh.lib.muonh_adamw_step(n, ctypes.cast(sz, ctypes.c_void_p) if sz is not None else None,
+                                   a, a, a, a, lr, b1, b2, eps, wd, step, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), mh.MUONH_EINVAL),
+    (dict(sizes=None), mh.MUONH_EINVAL),
+    (dict(arrays=False), mh.MUONH_EINVAL),
+    (dict(lr=float("nan")), mh.MUONH_EINVAL),
+    (dict(lr=-1e-3), mh.MUONH_EINVAL),
+    (dict(b1=1.0), mh.MUONH_EINVAL),
+    (dict(b2=-0.1), mh.MUONH_EINVAL),
+    (dict(eps=float("nan")), mh.MUONH_EINVAL),
+    (dict(eps=-1.0), mh.MUONH_EINVAL),
+    (dict(wd=float("inf")), mh.MUONH_EINVAL),
+    (dict(step=0), mh.MUONH_EINVAL),
+    (dict(sizes=(-5,)), mh.MUONH_ESHAPE),
+    (dict(sizes=((1 << 40) + 1,)), mh.MUONH_ESHAPE),
+])
+def test_adamw_rejects_bad_arguments(kw, code):
+    assert _adamw_call(**kw) == code
+    assert mh.lib.muonh_last_error().decode()
+
+
+def test_adamw_zero_tensors_is_a_no_op():
+    assert mh.lib.muonh_adamw_step(0, None, None, None, None, None, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1,
+                                   None) == mh.MUONH_OK

@@ -100,6 +100,23 @@ WORKLOADS = {
 }
 
 
+def _qwen3_2b_rest() -> tuple:
+    """Element counts of the parameters outside the MuonH matrix group of a
+    Qwen3-style 2B model, for the AdamW step: a tied token embedding of
+    151,936 x 2048, then per layer two RMSNorm scales of 2048 and the q/k
+    norms of 128, then the final norm. The pages name a Qwen3 configuration
+    but print no vocabulary or norm layout; these sizes stand in for it."""
+    sizes = [151936 * 2048]
+    for _ in range(28):
+        sizes += [2048, 2048, 128, 128]
+    sizes.append(2048)
+    return tuple(sizes)
+
+
+# AdamW parameter sets: flat tensor sizes (elements).
+ADAMW_SETS = {"qwen3_2b_rest": _qwen3_2b_rest()}
+
+
 def seed_key(wid: int, mat: int, step: int, kind: int) -> np.random.SeedSequence:
     return np.random.SeedSequence([SEED_ROOT, int(wid), int(mat), int(step), int(kind)])
 
