@@ -12,7 +12,14 @@ the roofline of the dominant kernel (from HIP events recorded inside the
 timed steps), and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host.
 
+With --variant muon_wd the same plan runs the Muon baseline (decoupled
+weight decay instead of the projection); with --variant adamw the step is
+one AdamW update of the parameters outside the matrix group (the embedding
+and norm vectors of the same 2B-shaped model), an HBM-bound elementwise
+launch.
+
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload qwen3_2b]
+                       [--variant muonh|muon_wd|adamw]
 """
 from __future__ import annotations
 
@@ -32,6 +39,8 @@ import workloads  # noqa: E402
 METRIC = "MuonH step time & params updated/s (2B-shaped set); NS TFLOP/s % MFMA peak"
 METRIC_MUON_WD = ("Muon + decoupled weight decay (the baseline) step time & params updated/s "
                   "(2B-shaped set); NS TFLOP/s % MFMA peak")
+METRIC_ADAMW = ("AdamW step time & params updated/s (non-matrix parameters of the 2B-shaped "
+                "model); HBM GB/s % peak")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
@@ -123,21 +132,22 @@ def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1):
     }
 
 
-def committed_traffic(kernel_name: str, workload: str):
+def committed_traffic(kernel_name: str, summary: str, source: str = "ns_gemm.hip"):
     """HBM bytes per launch of `kernel_name` from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by its factor on a
-    plain copy of known size), or None when no summary exists for this
-    workload or the kernel source has changed since the counters were taken."""
+    counter summary profiles/`summary` (FETCH_SIZE + WRITE_SIZE, each scaled
+    by its factor on a plain copy of known size), or None when there is no
+    such summary or the kernel's source file has changed since the counters
+    were taken (the summary records the first 16 hex digits of its SHA-256)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"muonh_step_{workload}_hbm_counters.md")
-    src = os.path.join(ROOT, "orthogonalized_updates_amd", "csrc", "ns_gemm.hip")
+    path = os.path.join(ROOT, "profiles", summary)
+    src = os.path.join(ROOT, "orthogonalized_updates_amd", "csrc", source)
     try:
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         for line in open(path):
             line = line.strip()
             if line.startswith("{") and '"traffic_bytes_per_launch"' in line:
                 rec = json.loads(line)
-                if rec.get("kernel") == kernel_name and rec.get("ns_gemm_sha256_16") == sha:
+                if rec.get("kernel") == kernel_name and rec.get("source_sha256_16") == sha:
                     return int(rec["traffic_bytes_per_launch"])
     except (OSError, ValueError):
         return None
@@ -161,6 +171,117 @@ def calibrate_copy() -> int:
     return 0
 
 
+ADAMW_WID = 5          # seed id of the AdamW parameter sets
+ADAMW_HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+ADAMW_BYTES_PER_ELEM = 28   # reads p, g, m, v and writes p, m, v (fp32)
+
+
+def adamw_cpu_baseline(n_params, budget_s):
+    """The fp64 oracle AdamW step on a 2^22-element slice of synthetic
+    embedding-like data, repeated for about `budget_s` seconds; the rate
+    per element holds for the whole set (every element is independent)."""
+    import numpy as np
+
+    import oracle
+    n = 1 << 22
+    p = workloads.host_normal((n,), 0.02, ADAMW_WID, 0, 0, workloads.KIND_W0).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    grads = [workloads.host_normal((n,), 0.01, ADAMW_WID, 0, s, workloads.KIND_G)
+             for s in (1, 2)]
+    runs, el = 0, 0.0
+    while el < budget_s and runs < 10000:
+        t1 = time.perf_counter()
+        p, m, v = oracle.adamw_step(p, grads[runs % 2], m, v, step=runs + 1, **ADAMW_HP)
+        el += time.perf_counter() - t1
+        runs += 1
+    return {
+        "value": n * runs / el,
+        "unit": "params/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("%d fp64 oracle AdamW steps over a %d-element slice (two gradients "
+                   "alternating), %.1f s; numpy elementwise, one thread; est. %.2f s per full "
+                   "%d-element step" % (runs, n, el, n_params * el / (n * runs), n_params)),
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+def bench_adamw(args, mh, torch) -> int:
+    """AdamW over a non-matrix parameter set: one grouped launch per step."""
+    sizes = workloads.ADAMW_SETS[args.adamw_set]
+    n = int(sum(sizes))
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    opt = mh.AdamW(sizes, device=dev)
+    print(f"[bench] adamw {args.adamw_set}: {len(sizes)} tensors, {n} params",
+          file=sys.stderr, flush=True)
+    P = [workloads.device_normal_(torch.empty(k, device=dev), 0.02, ADAMW_WID, i, 0,
+                                  workloads.KIND_W0) for i, k in enumerate(sizes)]
+    M = [torch.zeros(k, device=dev) for k in sizes]
+    V = [torch.zeros(k, device=dev) for k in sizes]
+    pool = max(1, min(args.warmup + args.steps, int(96e9 // (4 * n))))
+    G = [[workloads.device_normal_(torch.empty(k, device=dev), 0.01, ADAMW_WID, i, p + 1,
+                                   workloads.KIND_G) for i, k in enumerate(sizes)]
+         for p in range(pool)]
+    torch.cuda.synchronize(dev)
+    for w in range(args.warmup):
+        opt.step(P, G[w % pool], M, V, step=w + 1, **ADAMW_HP)
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps), gradient pool {pool}", file=sys.stderr,
+          flush=True)
+    events = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for e in evs:
+            e.record()
+        events.append(evs)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        st = args.warmup + s + 1
+        events[s][0].record()
+        opt.step(P, G[(st - 1) % pool], M, V, step=st, **ADAMW_HP)
+        events[s][1].record()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    launches_per_step = -(-len(sizes) // mh.ADAMW_MAX_TENSORS_PER_LAUNCH)
+    kern_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    avg_launch_ms = kern_ms / launches_per_step
+    bytes_per_launch = ADAMW_BYTES_PER_ELEM * n / launches_per_step
+    gbs = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC_ADAMW,
+        "value": n * args.steps / elapsed,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.adamw_set}: token embedding and norm vectors of the "
+                               f"28-layer Qwen3-style 2B model",
+                   "tensors": len(sizes), "params": n, "update": "adamw", **ADAMW_HP},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": committed_traffic("k_adamw",
+                                                  f"adamw_step_{args.adamw_set}_hbm_counters.md",
+                                                  "adamw.hip"),
+                     "kernel": "k_adamw", "avg_launch_ms": round(avg_launch_ms, 4),
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = adamw_cpu_baseline(n, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,9 +293,11 @@ def main() -> int:
                     help="Newton-Schulz operands: bf16 (default), split_bf16 (hi + lo bf16 "
                          "pairs, 3 MFMAs per product) or fp32 (debug mode)")
     ap.add_argument("--ns-fp32", action="store_true", help="same as --precision fp32")
-    ap.add_argument("--variant", default="muonh", choices=["muonh", "muon_wd"],
+    ap.add_argument("--variant", default="muonh", choices=["muonh", "muon_wd", "adamw"],
                     help="muonh (default): the MuonH step; muon_wd: the Muon baseline with "
-                         "decoupled weight decay on the same plan")
+                         "decoupled weight decay on the same plan; adamw: AdamW over the "
+                         "non-matrix parameter set (--adamw-set)")
+    ap.add_argument("--adamw-set", default="qwen3_2b_rest", choices=sorted(workloads.ADAMW_SETS))
     ap.add_argument("--weight-decay", type=float, default=0.1,
                     help="weight decay of the muon_wd variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -202,6 +325,8 @@ def main() -> int:
     if not mh.LIB_PATH.exists():
         import __graft_entry__
         __graft_entry__.build()
+    if args.variant == "adamw":
+        return bench_adamw(args, mh, torch)
 
     wl = workloads.WORKLOADS[args.workload]
     k = args.ns_iters if args.ns_iters is not None else wl.ns_iters[0]
@@ -283,7 +408,8 @@ def main() -> int:
         achieved = flops[dom] / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma,
                     "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
-                    "traffic": (committed_traffic(kernel_names[dom], wl.name)
+                    "traffic": (committed_traffic(kernel_names[dom],
+                                                  f"muonh_step_{wl.name}_hbm_counters.md")
                                 if args.precision == "bf16" else None),
                     "kernel": kernel_names[dom], "avg_launch_ms": round(avg_ms, 4),
                     "algorithmic_flop_per_launch": flops[dom]}

@@ -202,7 +202,7 @@ int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const floa
  *   MUONH_MAX_TENSOR_ELEMS). P, G, M, V: DEVICE arrays of n_tensors DEVICE
  *   pointers to flat fp32 tensors (parameters, gradients, first and second
  *   moments); P, M, V are updated in place, G is read. No plan and no
- *   workspace: tensors go in grouped launches of up to 64 tensors.
+ *   workspace: tensors go in grouped launches of up to 128 tensors.
  * lr, weight_decay: finite, >= 0; beta1, beta2 in [0, 1); eps finite, >= 0.
  * n_tensors == 0 is a no-op. Deterministic; asynchronous on `stream`.
  * Errors: MUONH_EINVAL (bad scalar, NULL array, step < 1, n_tensors < 0),

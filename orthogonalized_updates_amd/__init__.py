@@ -33,6 +33,8 @@ MUONH_NS_SPLIT_BF16 = 2
 
 # Newton-Schulz operand precision -> plan flag
 PRECISIONS = {"bf16": 0, "split_bf16": MUONH_NS_SPLIT_BF16, "fp32": MUONH_NS_FP32}
+# Tensors per grouped AdamW launch (the library splits larger lists).
+ADAMW_MAX_TENSORS_PER_LAUNCH = 128
 
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
 

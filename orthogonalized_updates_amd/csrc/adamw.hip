@@ -1,16 +1,22 @@
 // AdamW for the parameters outside the MuonH group (model card page "Puro",
 // section "Training": those parameters use AdamW with weight decay 0.1).
 //
-// One grouped launch per batch of up to kMaxAdamTensors flat fp32 tensors:
-// each block takes kAdamBlockElems consecutive elements of one tensor and
+// One grouped launch per batch of up to kMaxAdamTensors flat fp32 tensors (a
+// model's whole non-matrix set fits one launch): each block takes
+// kAdamBlockElems consecutive elements of one tensor, found by binary search
+// over the batch's cumulative block counts, and
 // applies, per element (decoupled decay, bias-corrected moments),
 //   p <- p * (1 - lr*wd)
 //   m <- beta1*m + (1 - beta1)*g
 //   v <- beta2*v + (1 - beta2)*g^2
 //   p <- p - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
 // in fp32, the step constants computed in fp64 on the host. Reads p, g, m, v
-// and writes p, m, v: 28 bytes per element, HBM-bound. 16-byte vector
-// accesses when all four tensors of a block are 16-byte aligned.
+// and writes p, m, v: 28 bytes per element, HBM-bound. A full block whose four
+// tensors are 16-byte aligned issues all of its loads first (two float4 per
+// stream per thread), then computes and stores, with non-temporal loads and
+// stores: on MI355X this read-modify-write stream runs about 6% faster with
+// the hint on both sides (and no faster with it on one side only). Partial
+// and misaligned blocks take plain vector or scalar accesses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,8 +36,9 @@ int set_error(int code, const char* msg);
 namespace {
 
 constexpr int kAdamThreads = 256;
-constexpr int kAdamBlockElems = 4096;  // 4 float4 per thread
-constexpr int kMaxAdamTensors = 64;
+constexpr int kAdamUnroll = 2;         // float4 per stream per thread (full blocks)
+constexpr int kAdamBlockElems = kAdamThreads * 4 * kAdamUnroll;  // 2048
+constexpr int kMaxAdamTensors = 128;  // kernel arguments stay near 2 KB
 
 struct AdamArgs {
   int64_t n[kMaxAdamTensors];
@@ -54,11 +61,36 @@ __device__ __forceinline__ float adam_elem(float& p, float g, float& m, float& v
   return p;
 }
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_nt(const float* q) {
+  const f4v x = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(q));
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void store_nt(const float4& a, float* q) {
+  const f4v x = {a.x, a.y, a.z, a.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f4v*>(q));
+}
+
+__device__ __forceinline__ void adam4(float4& p, const float4& g, float4& m, float4& v,
+                                      const AdamArgs& a) {
+  adam_elem(p.x, g.x, m.x, v.x, a);
+  adam_elem(p.y, g.y, m.y, v.y, a);
+  adam_elem(p.z, g.z, m.z, v.z, a);
+  adam_elem(p.w, g.w, m.w, v.w, a);
+}
+
 __global__ __launch_bounds__(kAdamThreads) void k_adamw(AdamArgs a, float* const* P,
                                                        const float* const* G, float* const* M,
                                                        float* const* V) {
-  int t = 0;
-  while (t + 1 < a.count && blockIdx.x >= a.block_begin[t + 1]) ++t;  // uniform for the block
+  // First tensor whose block range ends after this block (empty tensors have
+  // empty ranges and are never chosen); uniform for the block.
+  const int64_t b = blockIdx.x;
+  int t = 0, last = a.count - 1;
+  while (t < last) {
+    const int mid = (t + last) >> 1;
+    if (a.block_begin[mid + 1] > b) last = mid; else t = mid + 1;
+  }
   const int idx = a.first + t;
   const int64_t lo = (int64_t)(blockIdx.x - a.block_begin[t]) * kAdamBlockElems;
   const int64_t hi = lo + kAdamBlockElems < a.n[t] ? lo + kAdamBlockElems : a.n[t];
@@ -68,6 +100,26 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw(AdamArgs a, float* const
   float* v = V[idx];
   const bool vec = ((reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(g) |
                      reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(v)) & 15u) == 0;
+  if (vec && hi - lo == kAdamBlockElems) {
+    float4 pv[kAdamUnroll], gv[kAdamUnroll], mv[kAdamUnroll], vv[kAdamUnroll];
+#pragma unroll
+    for (int u = 0; u < kAdamUnroll; ++u) {
+      const int64_t e = lo + 4 * (threadIdx.x + u * kAdamThreads);
+      pv[u] = load_nt(p + e);
+      gv[u] = load_nt(g + e);
+      mv[u] = load_nt(m + e);
+      vv[u] = load_nt(v + e);
+    }
+#pragma unroll
+    for (int u = 0; u < kAdamUnroll; ++u) {
+      const int64_t e = lo + 4 * (threadIdx.x + u * kAdamThreads);
+      adam4(pv[u], gv[u], mv[u], vv[u], a);
+      store_nt(pv[u], p + e);
+      store_nt(mv[u], m + e);
+      store_nt(vv[u], v + e);
+    }
+    return;
+  }
   int64_t mid = lo;
   if (vec) {
     const int64_t n4 = (hi - lo) >> 2;
@@ -77,10 +129,7 @@ __global__ __launch_bounds__(kAdamThreads) void k_adamw(AdamArgs a, float* const
       const float4 gv = *reinterpret_cast<const float4*>(g + e);
       float4 mv = *reinterpret_cast<const float4*>(m + e);
       float4 vv = *reinterpret_cast<const float4*>(v + e);
-      adam_elem(pv.x, gv.x, mv.x, vv.x, a);
-      adam_elem(pv.y, gv.y, mv.y, vv.y, a);
-      adam_elem(pv.z, gv.z, mv.z, vv.z, a);
-      adam_elem(pv.w, gv.w, mv.w, vv.w, a);
+      adam4(pv, gv, mv, vv, a);
       *reinterpret_cast<float4*>(p + e) = pv;
       *reinterpret_cast<float4*>(m + e) = mv;
       *reinterpret_cast<float4*>(v + e) = vv;
