@@ -47,6 +47,8 @@ from typing import Tuple
 
 import numpy as np
 
+from .bf16_state_oracle import momentum_update_bf16_state
+
 NS_COEFFS: Tuple[float, float, float] = (3.4445, -4.7750, 2.0315)
 NS_EPS: float = 1e-7
 
@@ -70,12 +72,16 @@ def init_radius(w0) -> float:
     return frobenius_norm(w0)
 
 
-def momentum_update(m, g, beta: float) -> np.ndarray:
+def momentum_update(m, g, beta: float, mom_bf16: bool = False) -> np.ndarray:
     """M <- beta*M + G (reading 1: heavy-ball, no dampening, no Nesterov).
 
     Muon's first stage; the digest page (same section) calls MuonH an
-    extension of Muon.
+    extension of Muon. With mom_bf16 the momentum is stored in bf16 (model
+    card, section "Training": state in FP32 or BF16): the new value is
+    rounded as bf16_state_oracle.momentum_update_bf16_state states.
     """
+    if mom_bf16:
+        return momentum_update_bf16_state(m, g, beta)
     return float(beta) * _f64(m) + _f64(g)
 
 
@@ -116,9 +122,12 @@ def hyperball_project(w, o, radius: float, lr: float) -> np.ndarray:
 
 
 def muonh_step(w, g, m, radius: float, lr: float, beta: float, ns_iters: int,
-               coeffs=NS_COEFFS, eps: float = NS_EPS):
-    """One MuonH step for one matrix. Returns (W_new, M_new, O) in float64."""
-    m_new = momentum_update(m, g, beta)
+               coeffs=NS_COEFFS, eps: float = NS_EPS, mom_bf16: bool = False):
+    """One MuonH step for one matrix. Returns (W_new, M_new, O) in float64.
+    With mom_bf16, M holds bf16 values and so does M_new (see
+    momentum_update); a bf16 gradient needs nothing special: its values are
+    the bf16 numbers given."""
+    m_new = momentum_update(m, g, beta, mom_bf16)
     o = newton_schulz(m_new, ns_iters, coeffs=coeffs, eps=eps)
     w_new = hyperball_project(w, o, radius, lr)
     return w_new, m_new, o
@@ -130,7 +139,7 @@ def trial_norm(w, o, lr: float) -> float:
 
 
 def muon_wd_step(w, g, m, lr: float, beta: float, weight_decay: float, ns_iters: int,
-                 coeffs=NS_COEFFS, eps: float = NS_EPS):
+                 coeffs=NS_COEFFS, eps: float = NS_EPS, mom_bf16: bool = False):
     """Muon with decoupled weight decay: the baseline MuonH is measured against.
 
     The digest page ("The load-bearing tricks aren't in the abstract" and its
@@ -139,9 +148,10 @@ def muon_wd_step(w, g, m, lr: float, beta: float, weight_decay: float, ns_iters:
     multiplier relative to Muon. Neither prints the baseline's update. Reading:
     the same momentum and Newton-Schulz orthogonalisation as MuonH, then weight
     decay decoupled from the update, W <- (1 - lr*wd) W - lr O, and no
-    projection. Returns (W_new, M_new, O) in float64.
+    projection. Returns (W_new, M_new, O) in float64. mom_bf16 as in
+    muonh_step.
     """
-    m_new = momentum_update(m, g, beta)
+    m_new = momentum_update(m, g, beta, mom_bf16)
     o = newton_schulz(m_new, ns_iters, coeffs, eps)
     w_new = (1.0 - lr * weight_decay) * _f64(w) - lr * o
     return w_new, m_new, o
