@@ -31,9 +31,12 @@
  *     matrix index i runs over group 0's matrices, then group 1's, etc.
  *   - W, G, M are DEVICE arrays of n_matrices DEVICE pointers (the layout of
  *     batched-BLAS pointer arrays); each points to a contiguous row-major
- *     rows x cols fp32 matrix. R is a DEVICE array of n_matrices floats.
- *     Pointers that are 16-byte aligned take the vector path; others work
- *     through a scalar path. W, G and M must not overlap.
+ *     rows x cols matrix: W in fp32; G and M in fp32, or in bf16 (bits of
+ *     IEEE binary32's upper half) under the plan flags MUONH_GRAD_BF16 and
+ *     MUONH_MOM_BF16 (so G and M are typed void). R is a DEVICE array of
+ *     n_matrices floats. Pointers aligned to 4 elements (16 bytes fp32,
+ *     8 bytes bf16) take the vector path; others work through a scalar path.
+ *     W, G and M must not overlap.
  *   - The workspace is a DEVICE buffer of at least muonh_workspace_bytes(plan)
  *     bytes, 256-byte aligned, owned by the caller. It holds the
  *     Newton-Schulz operands (bf16, split bf16 or fp32 by plan flag) and the
@@ -58,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MUONH_ABI_VERSION 1
+#define MUONH_ABI_VERSION 2
 
 typedef struct muonh_plan muonh_plan;
 
@@ -77,7 +80,7 @@ enum {
   MUONH_ENOMEM = -5      /* host allocation failed */
 };
 
-/* Plan flags (at most one). Default: Newton-Schulz operands in bf16, bf16
+/* Newton-Schulz plan flags (at most one). Default: operands in bf16, bf16
  * MFMA with fp32 accumulation; about 1e-2 relative error of O at 5
  * iterations, about 2e-2 at 8. With bf16 or split operands and
  * ns_iters >= 1, X0's factor 1/(||M||_F + 1e-7) is applied inside the first
@@ -96,6 +99,20 @@ enum {
   MUONH_NS_SPLIT_BF16 = 2u
 };
 
+/* Storage plan flags (any combination with the above; model card "Puro",
+ * section "Training": master weights and optimizer state in FP32 or BF16).
+ * W always stays fp32. */
+enum {
+  /* G is bf16: its values are taken as given. */
+  MUONH_GRAD_BF16 = 4u,
+  /* M is stored in bf16: the new momentum beta*M + G is computed in fp32
+   * (one fused multiply-add) and rounded to the nearest bf16, ties to even;
+   * that stored value is the momentum whose norm and Newton-Schulz update
+   * the step uses. Cuts the momentum pass from 12 to 8 bytes per parameter
+   * (6 with MUONH_GRAD_BF16). */
+  MUONH_MOM_BF16 = 8u
+};
+
 /* Limits. */
 #define MUONH_MAX_GROUPS 4096
 #define MUONH_MAX_MATRICES (1 << 20)
@@ -108,7 +125,8 @@ int32_t muonh_abi_version(void);
 
 /*
  * Create a plan for `n_groups` shape groups. Host-only: no HIP call.
- * flags: 0, MUONH_NS_FP32 or MUONH_NS_SPLIT_BF16. On success *out owns a plan
+ * flags: at most one of MUONH_NS_FP32 and MUONH_NS_SPLIT_BF16, or'd with any
+ * of MUONH_GRAD_BF16 and MUONH_MOM_BF16. On success *out owns a plan
  * that must be released with muonh_plan_destroy. Errors: MUONH_EINVAL (null
  * out/groups, n_groups out of [1, MUONH_MAX_GROUPS], unknown or conflicting
  * flags), MUONH_ESHAPE (a dim out
@@ -146,7 +164,7 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
  * Results are bitwise deterministic for a given plan and input.
  * Errors: MUONH_EINVAL, MUONH_EWORKSPACE, MUONH_EHIP.
  */
-int muonh_step(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
+int muonh_step(const muonh_plan* plan, float* const* W, const void* const* G, void* const* M,
                const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
                size_t workspace_bytes, void* stream);
 
@@ -162,8 +180,8 @@ int muonh_step(const muonh_plan* plan, float* const* W, const float* const* G, f
  * Errors: as muonh_step, plus MUONH_EINVAL for a NULL events array, a NULL
  * event or a wrong n_events.
  */
-int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const* G,
-                     float* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+int muonh_step_timed(const muonh_plan* plan, float* const* W, const void* const* G,
+                     void* const* M, const float* R, float lr, float beta, int32_t ns_iters,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                      int32_t n_events);
 
@@ -179,14 +197,14 @@ int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const
  * muonh_step (the two may share a plan; W and M are updated in place).
  * weight_decay: finite, >= 0. Errors: as muonh_step.
  */
-int muonh_step_muon_wd(const muonh_plan* plan, float* const* W, const float* const* G,
-                       float* const* M, float lr, float beta, float weight_decay,
+int muonh_step_muon_wd(const muonh_plan* plan, float* const* W, const void* const* G,
+                       void* const* M, float lr, float beta, float weight_decay,
                        int32_t ns_iters, void* workspace, size_t workspace_bytes, void* stream);
 
 /* muonh_step_muon_wd with the phase events of muonh_step_timed (the last one
  * after the decayed update). */
-int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const float* const* G,
-                             float* const* M, float lr, float beta, float weight_decay,
+int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const void* const* G,
+                             void* const* M, float lr, float beta, float weight_decay,
                              int32_t ns_iters, void* workspace, size_t workspace_bytes,
                              void* stream, void* const* events, int32_t n_events);
 

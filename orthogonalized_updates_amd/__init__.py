@@ -30,9 +30,14 @@ MUONH_EHIP = -4
 MUONH_ENOMEM = -5
 MUONH_NS_FP32 = 1
 MUONH_NS_SPLIT_BF16 = 2
+MUONH_GRAD_BF16 = 4
+MUONH_MOM_BF16 = 8
 
 # Newton-Schulz operand precision -> plan flag
 PRECISIONS = {"bf16": 0, "split_bf16": MUONH_NS_SPLIT_BF16, "fp32": MUONH_NS_FP32}
+# Storage dtype of the gradient / momentum -> whether it takes the bf16 flag
+STATE_DTYPES = ("fp32", "bf16")
+
 # Tensors per grouped AdamW launch (the library splits larger lists).
 ADAMW_MAX_TENSORS_PER_LAUNCH = 128
 
@@ -124,20 +129,27 @@ class Plan:
 
     precision: Newton-Schulz operand precision, "bf16" (default),
     "split_bf16" (hi + lo bf16 pairs, three bf16 products each) or "fp32";
-    ns_fp32=True is the same as precision="fp32".
+    ns_fp32=True is the same as precision="fp32". grad_dtype / mom_dtype:
+    storage of G and M, "fp32" (default) or "bf16".
     """
 
     def __init__(self, groups: Sequence[Tuple[int, int, int]], ns_fp32: bool = False,
-                 precision: str = "bf16"):
+                 precision: str = "bf16", grad_dtype: str = "fp32", mom_dtype: str = "fp32"):
         precision = _precision(precision, ns_fp32)
+        for name, v in (("grad_dtype", grad_dtype), ("mom_dtype", mom_dtype)):
+            if v not in STATE_DTYPES:
+                raise ValueError(f"{name} must be one of {STATE_DTYPES}, got {v!r}")
+        flags = (PRECISIONS[precision] | (MUONH_GRAD_BF16 if grad_dtype == "bf16" else 0)
+                 | (MUONH_MOM_BF16 if mom_dtype == "bf16" else 0))
         arr = (GroupDesc * len(groups))(*[GroupDesc(int(r), int(c), int(n)) for r, c, n in groups])
         handle = ctypes.c_void_p()
-        check(get_lib().muonh_plan_create(ctypes.byref(handle), arr, len(groups),
-                                          PRECISIONS[precision]))
+        check(get_lib().muonh_plan_create(ctypes.byref(handle), arr, len(groups), flags))
         self.handle = handle
         self.groups = [tuple(int(v) for v in g) for g in groups]
         self.precision = precision
         self.ns_fp32 = precision == "fp32"
+        self.grad_dtype = grad_dtype
+        self.mom_dtype = mom_dtype
 
     @property
     def num_matrices(self) -> int:
@@ -163,11 +175,13 @@ class MuonH:
 
     shapes: (rows, cols) of each matrix, in the caller's order. Matrices are
     grouped by shape internally; every method takes and returns lists in the
-    caller's order.
+    caller's order. grad_dtype / mom_dtype ("fp32" or "bf16"): the torch
+    dtype the gradients / momenta must have (float32 or bfloat16).
     """
 
     def __init__(self, shapes: Sequence[Tuple[int, int]], *, ns_fp32: bool = False,
-                 precision: str = "bf16", device=None):
+                 precision: str = "bf16", grad_dtype: str = "fp32", mom_dtype: str = "fp32",
+                 device=None):
         import torch
         get_lib()
         self.torch = torch
@@ -186,7 +200,10 @@ class MuonH:
         self.plan_order: List[int] = [i for idx in buckets.values() for i in idx]
         self.plan_index = {caller: p for p, caller in enumerate(self.plan_order)}
         self.plan = Plan([(r, c, len(idx)) for (r, c), idx in buckets.items()], ns_fp32=ns_fp32,
-                         precision=precision)
+                         precision=precision, grad_dtype=grad_dtype, mom_dtype=mom_dtype)
+        tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}
+        self._dtypes = {"weights": torch.float32, "grads": tdt[grad_dtype],
+                        "moms": tdt[mom_dtype]}
         nbytes = max(self.plan.workspace_bytes, 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         if self.workspace.data_ptr() % 256:
@@ -199,9 +216,10 @@ class MuonH:
         torch = self.torch
         if len(tensors) != len(self.shapes):
             raise ValueError(f"{name}: expected {len(self.shapes)} tensors, got {len(tensors)}")
+        dt = self._dtypes[name]
         for i, t in enumerate(tensors):
-            if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
-                raise TypeError(f"{name}[{i}] must be a float32 torch tensor")
+            if not isinstance(t, torch.Tensor) or t.dtype != dt:
+                raise TypeError(f"{name}[{i}] must be a {dt} torch tensor")
             if t.device != self.device:
                 raise ValueError(f"{name}[{i}] is on {t.device}, expected {self.device}")
             if tuple(t.shape) != self.shapes[i] or not t.is_contiguous():
@@ -296,7 +314,8 @@ class MuonH:
 
 __all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
            "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
-           "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32"]
+           "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32", "MUONH_NS_SPLIT_BF16", "MUONH_GRAD_BF16",
+           "MUONH_MOM_BF16", "AdamW"]
 
 
 class AdamW:

@@ -48,6 +48,58 @@ __device__ __forceinline__ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// Storage of the gradient and the momentum: fp32, or bf16 (BF). Element i of
+// a flat array; load4/store4 take 4 consecutive elements from i (a multiple
+// of 4, the address aligned to kVecAlign). A bf16 store rounds to nearest
+// even and returns the value stored, so that what the caller goes on with
+// (the norm, the cast) is exactly the stored momentum.
+template <bool BF>
+struct St;
+template <>
+struct St<false> {
+  static constexpr unsigned kVecAlign = 16;
+  __device__ static float load(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  __device__ static float4 load4(const void* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  }
+  __device__ static float store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+    return v;
+  }
+  __device__ static float4 store4(void* p, int64_t i, float4 v) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
+    return v;
+  }
+};
+template <>
+struct St<true> {
+  static constexpr unsigned kVecAlign = 8;
+  __device__ static float load(const void* p, int64_t i) {
+    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[i] << 16);
+  }
+  __device__ static float4 load4(const void* p, int64_t i) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+  __device__ static float store(void* p, int64_t i, float v) {
+    const __bf16 h = (__bf16)v;
+    static_cast<__bf16*>(p)[i] = h;
+    return (float)h;
+  }
+  __device__ static float4 store4(void* p, int64_t i, float4 v) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 h = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p) + i) = h;
+    return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+  }
+};
+
+template <bool BF>
+__device__ __forceinline__ bool vec_aligned(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & (St<BF>::kVecAlign - 1)) == 0;
+}
+
 // --------------------------------------------------------------------------
 // init: partial sums of squares of W
 // --------------------------------------------------------------------------
@@ -81,10 +133,12 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(EwArgs a, float* const* W, d
 }
 
 // --------------------------------------------------------------------------
-// M <- beta*M + G, with partial sums of squares of the new M
+// M <- beta*M + G, with partial sums of squares of the new (stored) M;
+// G and M in fp32 or bf16 (GB, MB)
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const float* const* G,
-                                                       float* const* M, float beta,
+template <bool GB, bool MB>
+__global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const void* const* G,
+                                                       void* const* M, float beta,
                                                        double* partials) {
   __shared__ double red[4];
   const int gi = group_of_block(a, blockIdx.x);
@@ -92,24 +146,23 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const float* co
   const int local = blockIdx.x - g.block_begin;
   const int m = local / g.bpm, c = local - m * g.bpm;
   const int mat = g.first + m;
-  const float* gp = G[mat];
-  float* mp = M[mat];
+  const void* gp = G[mat];
+  void* mp = M[mat];
   int64_t lo, hi;
   chunk_range(g.n, g.bpm, c, lo, hi);
   float acc = 0.f;
   int64_t mid = lo;
-  if (aligned16(gp) && aligned16(mp)) {
+  if (vec_aligned<GB>(gp) && vec_aligned<MB>(mp)) {
     const int64_t n4 = (hi - lo) >> 2;
-    const float4* g4 = reinterpret_cast<const float4*>(gp + lo);
-    float4* m4 = reinterpret_cast<float4*>(mp + lo);
     for (int64_t i = threadIdx.x; i < n4; i += kThreads) {
-      const float4 gv = g4[i];
-      float4 mv = m4[i];
+      const int64_t e = lo + 4 * i;
+      const float4 gv = St<GB>::load4(gp, e);
+      float4 mv = St<MB>::load4(mp, e);
       mv.x = fmaf(beta, mv.x, gv.x);
       mv.y = fmaf(beta, mv.y, gv.y);
       mv.z = fmaf(beta, mv.z, gv.z);
       mv.w = fmaf(beta, mv.w, gv.w);
-      m4[i] = mv;
+      mv = St<MB>::store4(mp, e, mv);
       acc = fmaf(mv.x, mv.x, acc);
       acc = fmaf(mv.y, mv.y, acc);
       acc = fmaf(mv.z, mv.z, acc);
@@ -118,8 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const float* co
     mid = lo + (n4 << 2);
   }
   for (int64_t e = mid + threadIdx.x; e < hi; e += kThreads) {
-    const float v = fmaf(beta, mp[e], gp[e]);
-    mp[e] = v;
+    const float v = St<MB>::store(mp, e, fmaf(beta, St<MB>::load(mp, e), St<GB>::load(gp, e)));
     acc = fmaf(v, v, acc);
   }
   const double t = block_sum((double)acc, red);
@@ -239,17 +291,17 @@ struct Fmt<kFp32> {
 // straight to D and/or transposed (through LDS) to E (an offset of -1 skips
 // that output); entries outside rows x cols are written as zero. With
 // kMomentum the tile first takes M <- beta*M + G (written back) and returns
-// this thread's sum of squares of the new M; the values written are then
-// scale * M. Each thread takes 4 consecutive columns of 4 rows: columns
+// this thread's sum of squares of the new stored M; the values written are
+// then scale * M. G and M are fp32 or bf16 (GB, MB). Each thread takes 4 consecutive columns of 4 rows: columns
 // c0 + 4*(tid % 16), rows r0 + tid/16 + 16i. Every thread of the block must
 // call it (it synchronises when E is written).
 // --------------------------------------------------------------------------
-template <int F, bool kMomentum>
-__device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const float* gp, float* mp,
+template <int F, bool kMomentum, bool GB, bool MB>
+__device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const void* gp, void* mp,
                                            float beta, int r0, int c0, float scale,
                                            float (*tile)[65]) {
   const int tx = (threadIdx.x & 15) << 2, ty = threadIdx.x >> 4;
-  const bool vec = (g.cols & 3) == 0 && aligned16(mp) && (!kMomentum || aligned16(gp));
+  const bool vec = (g.cols & 3) == 0 && vec_aligned<MB>(mp) && (!kMomentum || vec_aligned<GB>(gp));
   const bool trans = g.offE >= 0;
   float acc = 0.f;
   if (trans) __syncthreads();  // the previous tile's transposed reads are done
@@ -259,28 +311,24 @@ __device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const fl
     const int r = r0 + rr, c = c0 + tx;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < g.rows) {
-      float* row = mp + (int64_t)r * g.cols;
-      const float* grow = kMomentum ? gp + (int64_t)r * g.cols : nullptr;
+      const int64_t i0 = (int64_t)r * g.cols + c;
       if (vec && c + 3 < g.cols) {
-        v = *reinterpret_cast<const float4*>(row + c);
+        v = St<MB>::load4(mp, i0);
         if (kMomentum) {
-          const float4 gv = *reinterpret_cast<const float4*>(grow + c);
+          const float4 gv = St<GB>::load4(gp, i0);
           v.x = fmaf(beta, v.x, gv.x);
           v.y = fmaf(beta, v.y, gv.y);
           v.z = fmaf(beta, v.z, gv.z);
           v.w = fmaf(beta, v.w, gv.w);
-          *reinterpret_cast<float4*>(row + c) = v;
+          v = St<MB>::store4(mp, i0, v);
         }
       } else {
         float e[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (c + q < g.cols) {
-            float m = row[c + q];
-            if (kMomentum) {
-              m = fmaf(beta, m, grow[c + q]);
-              row[c + q] = m;
-            }
+            float m = St<MB>::load(mp, i0 + q);
+            if (kMomentum) m = St<MB>::store(mp, i0 + q, fmaf(beta, m, St<GB>::load(gp, i0 + q)));
             e[q] = m;
           }
         }
@@ -319,8 +367,8 @@ __device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const fl
 }
 
 // X0 = M / (||M|| + eps): one tile per block.
-template <int F>
-__global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* const* M,
+template <int F, bool MB>
+__global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const void* const* M,
                                                        const double* norms) {
   __shared__ float tile[64][65];
   const int gi = group_of_block(a, blockIdx.x);
@@ -331,15 +379,15 @@ __global__ __launch_bounds__(kThreads) void k_normcast(EwArgs a, const float* co
   const int tcols = g.cp >> 6;
   const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
   const float scale = (float)(1.0 / (norms[mat] + kNsEps));
-  cast_tile<F, false>(g, g.ns_base + (int64_t)m * g.mat_bytes, nullptr, const_cast<float*>(M[mat]),
-                      0.f, r0, c0, scale, tile);
+  cast_tile<F, false, false, MB>(g, g.ns_base + (int64_t)m * g.mat_bytes, nullptr,
+                                 const_cast<void*>(M[mat]), 0.f, r0, c0, scale, tile);
 }
 
 // Fused momentum and unscaled cast: block c of a matrix takes tiles
 // [c*tpb, (c+1)*tpb) of its padded domain and writes one partial sum.
-template <int F>
-__global__ __launch_bounds__(kThreads) void k_momentum_cast(EwArgs a, const float* const* G,
-                                                            float* const* M, float beta,
+template <int F, bool GB, bool MB>
+__global__ __launch_bounds__(kThreads) void k_momentum_cast(EwArgs a, const void* const* G,
+                                                            void* const* M, float beta,
                                                             double* partials) {
   __shared__ float tile[64][65];
   __shared__ double red[4];
@@ -354,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum_cast(EwArgs a, const floa
   float acc = 0.f;
   for (int t = c * g.tpb; t < t1; ++t) {
     const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
-    acc += cast_tile<F, true>(g, blk, G[mat], M[mat], beta, r0, c0, 1.f, tile);
+    acc += cast_tile<F, true, GB, MB>(g, blk, G[mat], M[mat], beta, r0, c0, 1.f, tile);
   }
   const double tot = block_sum((double)acc, red);
   if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = tot;
@@ -362,8 +410,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum_cast(EwArgs a, const floa
 
 // Fallback of the deferred normalisation: 8 blocks per matrix; for the
 // matrices whose norm fails xnorm_deferred they rewrite X0 normalised.
-template <int F>
-__global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const float* const* M,
+template <int F, bool MB>
+__global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const void* const* M,
                                                             const double* norms) {
   __shared__ float tile[64][65];
   int b = blockIdx.x, gi = 0;
@@ -379,7 +427,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const floa
   const int tcols = g.cp >> 6;
   for (int t = j; t < g.tiles_per_mat; t += 8) {
     const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
-    cast_tile<F, false>(g, blk, nullptr, const_cast<float*>(M[mat]), 0.f, r0, c0, scale, tile);
+    cast_tile<F, false, false, MB>(g, blk, nullptr, const_cast<void*>(M[mat]), 0.f, r0, c0, scale,
+                                   tile);
   }
 }
 
@@ -499,9 +548,24 @@ hipError_t launch_sumsq(const EwArgs& a, float* const* W, double* partials, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_momentum(const EwArgs& a, const float* const* G, float* const* M, float beta,
-                           double* partials, hipStream_t s) {
-  hipLaunchKernelGGL(k_momentum, dim3(a.nblocks), dim3(kThreads), 0, s, a, G, M, beta, partials);
+// Launches KERNEL<..., GB, MB> for the run-time storage formats of G and M.
+#define MUONH_STATE_DISPATCH(SF, KERNEL, ...)                                   \
+  do {                                                                          \
+    if ((SF).g_bf16) {                                                          \
+      if ((SF).m_bf16) hipLaunchKernelGGL(KERNEL(true, true), __VA_ARGS__);     \
+      else hipLaunchKernelGGL(KERNEL(true, false), __VA_ARGS__);                \
+    } else {                                                                    \
+      if ((SF).m_bf16) hipLaunchKernelGGL(KERNEL(false, true), __VA_ARGS__);    \
+      else hipLaunchKernelGGL(KERNEL(false, false), __VA_ARGS__);               \
+    }                                                                           \
+  } while (0)
+
+#define K_MOMENTUM(GB, MB) (k_momentum<GB, MB>)
+
+hipError_t launch_momentum(const EwArgs& a, StateFmt sf, const void* const* G, void* const* M,
+                           float beta, double* partials, hipStream_t s) {
+  MUONH_STATE_DISPATCH(sf, K_MOMENTUM, dim3(a.nblocks), dim3(kThreads), 0, s, a, G, M, beta,
+                       partials);
   return hipGetLastError();
 }
 
@@ -521,34 +585,58 @@ hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norm
     case kFp32: hipLaunchKernelGGL(KERNEL(kFp32), __VA_ARGS__); break; \
   }
 
-#define K_NORMCAST(F) k_normcast<F>
 #define K_UPDATE(F) (k_update<F, kTrialNorm>)
 #define K_PROJECT(F) (k_update<F, kProjectMode>)
 #define K_DECAY(F) (k_update<F, kDecay>)
 #define K_READ(F) k_read_update<F>
 
-hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
+// Kernels templated on the operand format F and the momentum storage MB.
+#define K_NORMCAST_M0(F) (k_normcast<F, false>)
+#define K_NORMCAST_M1(F) (k_normcast<F, true>)
+#define K_FALLBACK_M0(F) (k_cast_fallback<F, false>)
+#define K_FALLBACK_M1(F) (k_cast_fallback<F, true>)
+
+hipError_t launch_normcast(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* M,
                            const double* norms, hipStream_t s) {
-  MUONH_PREC_DISPATCH(prec, K_NORMCAST, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms)
+  if (sf.m_bf16) {
+    MUONH_PREC_DISPATCH(prec, K_NORMCAST_M1, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms)
+  } else {
+    MUONH_PREC_DISPATCH(prec, K_NORMCAST_M0, dim3(a.nblocks), dim3(kThreads), 0, s, a, M, norms)
+  }
   return hipGetLastError();
 }
 
-#define K_MOMCAST(F) k_momentum_cast<F>
-#define K_FALLBACK(F) k_cast_fallback<F>
+template <int F>
+void launch_momentum_cast_f(const EwArgs& a, StateFmt sf, const void* const* G, void* const* M,
+                            float beta, double* partials, hipStream_t s) {
+#define K_MOMCAST(GB, MB) (k_momentum_cast<F, GB, MB>)
+  MUONH_STATE_DISPATCH(sf, K_MOMCAST, dim3(a.nblocks), dim3(kThreads), 0, s, a, G, M, beta,
+                       partials);
+#undef K_MOMCAST
+}
 
-hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, const float* const* G,
-                                float* const* M, float beta, double* partials, hipStream_t s) {
-  MUONH_PREC_DISPATCH(prec, K_MOMCAST, dim3(a.nblocks), dim3(kThreads), 0, s, a, G, M, beta,
-                      partials)
+hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* G,
+                                void* const* M, float beta, double* partials, hipStream_t s) {
+  switch (prec) {
+    case kBf16: launch_momentum_cast_f<kBf16>(a, sf, G, M, beta, partials, s); break;
+    case kSplitBf16: launch_momentum_cast_f<kSplitBf16>(a, sf, G, M, beta, partials, s); break;
+    case kFp32: launch_momentum_cast_f<kFp32>(a, sf, G, M, beta, partials, s); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, const float* const* M,
+hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* M,
                                 const double* norms, hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < a.ngroups; ++i) blocks += (int64_t)a.g[i].count * 8;
   if (blocks == 0) return hipSuccess;
-  MUONH_PREC_DISPATCH(prec, K_FALLBACK, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, M, norms)
+  if (sf.m_bf16) {
+    MUONH_PREC_DISPATCH(prec, K_FALLBACK_M1, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, M,
+                        norms)
+  } else {
+    MUONH_PREC_DISPATCH(prec, K_FALLBACK_M0, dim3((unsigned)blocks), dim3(kThreads), 0, s, a, M,
+                        norms)
+  }
   return hipGetLastError();
 }
 

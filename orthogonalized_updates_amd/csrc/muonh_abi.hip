@@ -81,6 +81,7 @@ struct muonh_plan {
   int64_t n_params = 0;
   uint32_t flags = 0;
   NsPrec prec = kBf16;
+  StateFmt sf;  // storage of G and M
   int esize = 2;  // workspace bytes per logical Newton-Schulz element
   int64_t off_partials = 0, off_norm_m = 0, off_norm_w = 0;
   size_t ws_bytes = 0;
@@ -335,7 +336,7 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   if (!groups) return fail(MUONH_EINVAL, "groups is NULL");
   if (n_groups < 1 || n_groups > MUONH_MAX_GROUPS)
     return fail(MUONH_EINVAL, "n_groups=%d out of [1, %d]", n_groups, MUONH_MAX_GROUPS);
-  if (flags & ~uint32_t(MUONH_NS_FP32 | MUONH_NS_SPLIT_BF16))
+  if (flags & ~uint32_t(MUONH_NS_FP32 | MUONH_NS_SPLIT_BF16 | MUONH_GRAD_BF16 | MUONH_MOM_BF16))
     return fail(MUONH_EINVAL, "unknown flags 0x%x", flags);
   if ((flags & MUONH_NS_FP32) && (flags & MUONH_NS_SPLIT_BF16))
     return fail(MUONH_EINVAL, "MUONH_NS_FP32 and MUONH_NS_SPLIT_BF16 exclude each other");
@@ -345,6 +346,8 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   p->flags = flags;
   p->prec = (flags & MUONH_NS_FP32) ? kFp32 : (flags & MUONH_NS_SPLIT_BF16) ? kSplitBf16 : kBf16;
   p->esize = ns_elem_bytes(p->prec);
+  p->sf.g_bf16 = (flags & MUONH_GRAD_BF16) != 0;
+  p->sf.m_bf16 = (flags & MUONH_MOM_BF16) != 0;
 
   int64_t n_mats = 0;
   for (int32_t i = 0; i < n_groups; ++i) {
@@ -459,7 +462,7 @@ struct Variant {
   float weight_decay;
 };
 
-int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
+int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, void* const* M,
               const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
               size_t workspace_bytes, void* stream, void* const* events, int32_t n_events,
               Variant var = {false, 0.f}) {
@@ -505,22 +508,22 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
   if (fused) {
     for (const EwArgs& a : make_ew(plan, ws, kEwFused, ns_iters)) {
-      if ((e = launch_momentum_cast(a, plan->prec, G, M, beta, partials, s)) != hipSuccess)
+      if ((e = launch_momentum_cast(a, plan->prec, plan->sf, G, M, beta, partials, s)) != hipSuccess)
         return hip_fail(e, "momentum + cast");
       if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
         return hip_fail(e, "momentum finalize");
-      if ((e = launch_cast_fallback(a, plan->prec, M, norm_m, s)) != hipSuccess)
+      if ((e = launch_cast_fallback(a, plan->prec, plan->sf, M, norm_m, s)) != hipSuccess)
         return hip_fail(e, "cast fallback");
     }
   } else {
     for (const EwArgs& a : stream_args) {
-      if ((e = launch_momentum(a, G, M, beta, partials, s)) != hipSuccess)
+      if ((e = launch_momentum(a, plan->sf, G, M, beta, partials, s)) != hipSuccess)
         return hip_fail(e, "momentum");
       if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
         return hip_fail(e, "momentum finalize");
     }
     for (const EwArgs& a : make_ew(plan, ws, kEwTile, ns_iters))
-      if ((e = launch_normcast(a, plan->prec, M, norm_m, s)) != hipSuccess)
+      if ((e = launch_normcast(a, plan->prec, plan->sf, M, norm_m, s)) != hipSuccess)
         return hip_fail(e, "normcast");
   }
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
@@ -562,15 +565,15 @@ int step_impl(const muonh_plan* plan, float* const* W, const float* const* G, fl
 
 extern "C" {
 
-int muonh_step(const muonh_plan* plan, float* const* W, const float* const* G, float* const* M,
+int muonh_step(const muonh_plan* plan, float* const* W, const void* const* G, void* const* M,
                const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
                size_t workspace_bytes, void* stream) {
   return step_impl(plan, W, G, M, R, lr, beta, ns_iters, workspace, workspace_bytes, stream,
                    nullptr, 0);
 }
 
-int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const* G,
-                     float* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+int muonh_step_timed(const muonh_plan* plan, float* const* W, const void* const* G,
+                     void* const* M, const float* R, float lr, float beta, int32_t ns_iters,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events,
                      int32_t n_events) {
   if (!events) return fail(MUONH_EINVAL, "events is NULL");
@@ -578,15 +581,15 @@ int muonh_step_timed(const muonh_plan* plan, float* const* W, const float* const
                    events, n_events);
 }
 
-int muonh_step_muon_wd(const muonh_plan* plan, float* const* W, const float* const* G,
-                       float* const* M, float lr, float beta, float weight_decay,
+int muonh_step_muon_wd(const muonh_plan* plan, float* const* W, const void* const* G,
+                       void* const* M, float lr, float beta, float weight_decay,
                        int32_t ns_iters, void* workspace, size_t workspace_bytes, void* stream) {
   return step_impl(plan, W, G, M, nullptr, lr, beta, ns_iters, workspace, workspace_bytes, stream,
                    nullptr, 0, Variant{true, weight_decay});
 }
 
-int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const float* const* G,
-                             float* const* M, float lr, float beta, float weight_decay,
+int muonh_step_muon_wd_timed(const muonh_plan* plan, float* const* W, const void* const* G,
+                             void* const* M, float lr, float beta, float weight_decay,
                              int32_t ns_iters, void* workspace, size_t workspace_bytes,
                              void* stream, void* const* events, int32_t n_events) {
   if (!events) return fail(MUONH_EINVAL, "events is NULL");

@@ -49,6 +49,15 @@ __host__ __device__ inline float x0_sigma(double n) {
   return xnorm_deferred(n) ? (float)(1.0 / (n + kNsEps)) : 1.f;
 }
 
+// Storage of the gradient and the momentum (plan flags MUONH_GRAD_BF16 and
+// MUONH_MOM_BF16): fp32, or bf16. A bf16 momentum is stored rounded to
+// nearest even from the fp32 fma result, and the stored value is the one the
+// norm and Newton-Schulz see.
+struct StateFmt {
+  bool g_bf16 = false;
+  bool m_bf16 = false;
+};
+
 // ---------------------------------------------------------------------------
 // Elementwise / reduction kernels (elementwise.hip)
 // ---------------------------------------------------------------------------
@@ -81,22 +90,22 @@ struct EwArgs {
 
 // Norm partials: partials[mat * kMaxPartials + chunk] (double).
 hipError_t launch_sumsq(const EwArgs& a, float* const* W, double* partials, hipStream_t s);
-hipError_t launch_momentum(const EwArgs& a, const float* const* G, float* const* M, float beta,
-                           double* partials, hipStream_t s);
+hipError_t launch_momentum(const EwArgs& a, StateFmt sf, const void* const* G, void* const* M,
+                           float beta, double* partials, hipStream_t s);
 // norms[mat] = sqrt(sum of partials) for the matrices of the batch `a`;
 // if R != nullptr also R[mat] = (float)norms[mat].
 hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norms, float* R,
                            hipStream_t s);
 // X0 = M / (norm + eps) written to D (same orientation) and E (transposed).
-hipError_t launch_normcast(const EwArgs& a, NsPrec prec, const float* const* M,
+hipError_t launch_normcast(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* M,
                            const double* norms, hipStream_t s);
 // M <- beta*M + G with partial sums of squares, and Y = M (unscaled) written
 // to D / E as X0 would be (tile launch; bpm blocks of tpb tiles per matrix).
-hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, const float* const* G,
-                                float* const* M, float beta, double* partials, hipStream_t s);
+hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* G,
+                                void* const* M, float beta, double* partials, hipStream_t s);
 // For the matrices whose norm fails xnorm_deferred: X0 = M / (norm + eps)
 // written as launch_normcast would (8 blocks per matrix; the others return).
-hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, const float* const* M,
+hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* M,
                                 const double* norms, hipStream_t s);
 hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, float lr,
                               double* partials, hipStream_t s);

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert mh.lib.muonh_abi_version() == 1
+    assert mh.lib.muonh_abi_version() == 2
 
 
 def _create(groups, flags=0):
@@ -92,6 +92,28 @@ def test_binding_rejects_unknown_precision():
         mh.Plan([(4, 4, 1)], precision="fp16")
     with pytest.raises(ValueError):
         mh.Plan([(4, 4, 1)], ns_fp32=True, precision="split_bf16")
+
+
+@pytest.mark.parametrize("flags", [mh.MUONH_GRAD_BF16, mh.MUONH_MOM_BF16,
+                                   mh.MUONH_GRAD_BF16 | mh.MUONH_MOM_BF16 | mh.MUONH_NS_SPLIT_BF16,
+                                   mh.MUONH_MOM_BF16 | mh.MUONH_NS_FP32])
+def test_plan_accepts_state_storage_flags(flags):
+    st, h = _create([(4, 4, 1)], flags)
+    assert st == mh.MUONH_OK and h.value
+    # the storage of G and M does not change the workspace
+    ref = mh.Plan([(4, 4, 1)], precision="fp32" if flags & mh.MUONH_NS_FP32 else
+                  "split_bf16" if flags & mh.MUONH_NS_SPLIT_BF16 else "bf16")
+    assert mh.lib.muonh_workspace_bytes(h) == ref.workspace_bytes
+    mh.lib.muonh_plan_destroy(h)
+
+
+def test_binding_rejects_unknown_state_dtype():
+    with pytest.raises(ValueError):
+        mh.Plan([(4, 4, 1)], grad_dtype="fp16")
+    with pytest.raises(ValueError):
+        mh.Plan([(4, 4, 1)], mom_dtype="float32")
+    p = mh.Plan([(4, 4, 1)], grad_dtype="bf16", mom_dtype="bf16")
+    assert (p.grad_dtype, p.mom_dtype) == ("bf16", "bf16")
 
 
 def test_plan_padding_of_ragged_shapes():
