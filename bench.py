@@ -61,19 +61,20 @@ def ns_flops(shapes, k):
     return {"gram": gram, "poly": poly, "apply": apply}
 
 
-def elementwise_bytes(n_params, ns_bytes, fused, variant="muonh"):
+def elementwise_bytes(n_params, ns_bytes, fused, variant="muonh", g_bytes=4, m_bytes=4):
     """Algorithmic HBM bytes of the streaming phases, per step.
 
-    before Newton-Schulz: momentum reads G, M and writes M (12 B/param) and
-      X0 is written once (ns_bytes); with bf16 or split operands and at least
-      one iteration the two happen in one pass (fused), otherwise the cast
-      reads M again and, in fp32 mode, writes X and X^T:
-      12 + 4 + 2*ns_bytes B/param;
+    before Newton-Schulz: momentum reads G, M and writes M (g + 2m B/param:
+      12 with fp32 G and M, 6 with both in bf16) and X0 is written once
+      (ns_bytes); with bf16 or split operands and at least one iteration the
+      two happen in one pass (fused), otherwise the cast reads M again and,
+      in fp32 mode, writes X and X^T: g + 2m + m + 2*ns_bytes B/param;
     after: the trial-norm pass reads W and O (4 + ns_bytes), the projection
       reads W and O and writes W (8 + ns_bytes); the Muon baseline's decayed
       update is one pass that reads W and O and writes W (8 + ns_bytes).
     """
-    pre = n_params * (12 + ns_bytes if fused else 12 + 4 + 2 * ns_bytes)
+    mom = g_bytes + 2 * m_bytes
+    pre = n_params * (mom + ns_bytes if fused else mom + m_bytes + 2 * ns_bytes)
     if variant == "muon_wd":
         post = n_params * (8 + ns_bytes)
     else:
@@ -81,9 +82,10 @@ def elementwise_bytes(n_params, ns_bytes, fused, variant="muonh"):
     return pre, post
 
 
-def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1):
+def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1, mom_bf16=False):
     """The fp64 oracle on the host, on one matrix of each distinct shape,
-    extrapolated by count to the whole set (matrices are independent)."""
+    extrapolated by count to the whole set (matrices are independent). With
+    mom_bf16 the oracle keeps the momentum in bf16 (exact fma rounding)."""
     import numpy as np
 
     import oracle
@@ -107,9 +109,9 @@ def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1):
         t0 = time.perf_counter()
         while True:
             if variant == "muon_wd":
-                oracle.muon_wd_step(w, g, m, wl.lr, wl.beta, weight_decay, k)
+                oracle.muon_wd_step(w, g, m, wl.lr, wl.beta, weight_decay, k, mom_bf16=mom_bf16)
             else:
-                oracle.muonh_step(w, g, m, radius, wl.lr, wl.beta, k)
+                oracle.muonh_step(w, g, m, radius, wl.lr, wl.beta, k, mom_bf16=mom_bf16)
             runs += 1
             el = time.perf_counter() - t0
             if el >= per_shape_budget or runs >= 5:
@@ -298,6 +300,10 @@ def main() -> int:
                          "decoupled weight decay on the same plan; adamw: AdamW over the "
                          "non-matrix parameter set (--adamw-set)")
     ap.add_argument("--adamw-set", default="qwen3_2b_rest", choices=sorted(workloads.ADAMW_SETS))
+    ap.add_argument("--grad-dtype", default="fp32", choices=["fp32", "bf16"],
+                    help="storage of the gradients G (default fp32)")
+    ap.add_argument("--mom-dtype", default="fp32", choices=["fp32", "bf16"],
+                    help="storage of the momentum M (default fp32)")
     ap.add_argument("--weight-decay", type=float, default=0.1,
                     help="weight decay of the muon_wd variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -332,18 +338,23 @@ def main() -> int:
     k = args.ns_iters if args.ns_iters is not None else wl.ns_iters[0]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    opt = mh.MuonH(wl.shapes, precision=args.precision, device=dev)
+    opt = mh.MuonH(wl.shapes, precision=args.precision, grad_dtype=args.grad_dtype,
+                   mom_dtype=args.mom_dtype, device=dev)
+    gdt = torch.bfloat16 if args.grad_dtype == "bf16" else torch.float32
+    mdt = torch.bfloat16 if args.mom_dtype == "bf16" else torch.float32
+    g_bytes, m_bytes = (2 if args.grad_dtype == "bf16" else 4), (2 if args.mom_dtype == "bf16" else 4)
 
     print(f"[bench] {wl.name}: {wl.n_matrices} matrices, {wl.n_params} params, k={k}, "
           f"workspace {opt.plan.workspace_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
     W = [workloads.device_weight_(wl, i, torch.empty(s, device=dev)) for i, s in enumerate(wl.shapes)]
-    M = [torch.zeros(s, device=dev) for s in wl.shapes]
-    # Distinct gradients per step (pool bounded to ~96 GB), generated before timing.
-    per_set = 4 * wl.n_params
+    M = [torch.zeros(s, dtype=mdt, device=dev) for s in wl.shapes]
+    # Distinct gradients per step (pool bounded to ~96 GB), generated before
+    # timing (in fp32, then converted when G is stored in bf16).
+    per_set = g_bytes * wl.n_params
     pool = max(1, min(args.warmup + args.steps, int(96e9 // per_set)))
     G = []
     for p in range(pool):
-        G.append([workloads.device_grad_(wl, i, p, torch.empty(s, device=dev))
+        G.append([workloads.device_grad_(wl, i, p, torch.empty(s, device=dev)).to(gdt)
                   for i, s in enumerate(wl.shapes)])
     opt.init(W)
     torch.cuda.synchronize(dev)
@@ -397,7 +408,7 @@ def main() -> int:
     peak_mfma = PEAK_FP32_MFMA_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     ns_bytes = 2 if args.precision == "bf16" else 4
     pre_b, post_b = elementwise_bytes(wl.n_params, ns_bytes, fused=not fp32 and k >= 1,
-                                      variant=args.variant)
+                                      variant=args.variant, g_bytes=g_bytes, m_bytes=m_bytes)
     pre_ms, post_ms = pre / nst, post / nst
     dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
 
@@ -434,6 +445,7 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: {wl.notes}", "matrices": wl.n_matrices,
                    "params": wl.n_params, "ns_iters": k, "lr": wl.lr, "beta": wl.beta,
                    "master_weights": "fp32", "ns_operands": args.precision,
+                   "grad_dtype": args.grad_dtype, "mom_dtype": args.mom_dtype,
                    "update": ("muon_wd (weight_decay=%g)" % args.weight_decay
                               if args.variant == "muon_wd" else "muonh")},
         "roofline": roofline,
@@ -454,7 +466,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, k, args.cpu_budget, args.variant,
-                                              args.weight_decay)
+                                              args.weight_decay, args.mom_dtype == "bf16")
     print(json.dumps(result), flush=True)
     return 0
 
