@@ -79,9 +79,9 @@ __device__ __forceinline__ float4 widen4(uint2 u) {
 }
 
 // Storage of the gradient and the momentum: fp32, or bf16 (BF). Element i of
-// a flat array; load4/store4 take 4 consecutive elements from i (a multiple
-// of 4, the address aligned to kVecAlign). A bf16 store rounds to nearest
-// even and returns the value stored, so that what the caller goes on with
+// a flat array; load4/load4_nt/store4_nt take 4 consecutive elements from i
+// (a multiple of 4, the address aligned to kVecAlign). A bf16 store rounds to
+// nearest even and returns the value stored, so that what the caller goes on with
 // (the norm, the cast) is exactly the stored momentum.
 template <bool BF>
 struct St;
@@ -94,10 +94,6 @@ struct St<false> {
   }
   __device__ static float store(void* p, int64_t i, float v) {
     static_cast<float*>(p)[i] = v;
-    return v;
-  }
-  __device__ static float4 store4(void* p, int64_t i, float4 v) {
-    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
     return v;
   }
   __device__ static float4 load4_nt(const void* p, int64_t i) {
@@ -130,12 +126,6 @@ struct St<true> {
     const __bf16 h = (__bf16)v;
     static_cast<__bf16*>(p)[i] = h;
     return (float)h;
-  }
-  __device__ static float4 store4(void* p, int64_t i, float4 v) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 h = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p) + i) = h;
-    return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
   }
 };
 
@@ -260,9 +250,6 @@ struct Fmt<kBf16> {
   __device__ static int64_t off(int64_t r, int c, int ld) {
     return ((((r >> 8) * (ld >> 5)) + (c >> 5)) << 14) + ((r & 255) << 6) + ((c & 31) << 1);
   }
-  __device__ static void store(char* base, int64_t r, int c, int ld, float v) {
-    *reinterpret_cast<__bf16*>(base + off(r, c, ld)) = (__bf16)v;
-  }
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
     return (float)*reinterpret_cast<const __bf16*>(base + off(r, c, ld));
   }
@@ -280,13 +267,6 @@ template <>
 struct Fmt<kSplitBf16> {
   __device__ static int64_t off(int64_t r, int c, int ld) {  // of the hi value; lo at +32
     return ((((r >> 8) * (ld >> 4)) + (c >> 4)) << 14) + ((r & 255) << 6) + ((c & 15) << 1);
-  }
-  __device__ static void store(char* base, int64_t r, int c, int ld, float v) {
-    const __bf16 h = (__bf16)v;
-    const __bf16 l = (__bf16)(v - (float)h);
-    __bf16* p = reinterpret_cast<__bf16*>(base + off(r, c, ld));
-    p[0] = h;
-    p[16] = l;
   }
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
     const __bf16* p = reinterpret_cast<const __bf16*>(base + off(r, c, ld));
@@ -313,9 +293,6 @@ struct Fmt<kSplitBf16> {
 template <>
 struct Fmt<kFp32> {
   __device__ static int64_t off(int64_t r, int c, int ld) { return (r * ld + c) * 4; }
-  __device__ static void store(char* base, int64_t r, int c, int ld, float v) {
-    *reinterpret_cast<float*>(base + off(r, c, ld)) = v;
-  }
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
     return *reinterpret_cast<const float*>(base + off(r, c, ld));
   }

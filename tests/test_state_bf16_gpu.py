@@ -152,11 +152,14 @@ def test_state_ragged_groups(gdt, mdt, prec, k):
 
 
 @pytest.mark.parametrize("gdt,mdt", COMBOS)
-def test_state_misaligned_pointers(gdt, mdt):
+@pytest.mark.parametrize("prec,k", [("bf16", 5), ("fp32", 5), ("bf16", 0)])
+def test_state_misaligned_pointers(gdt, mdt, prec, k):
     # one element into each buffer: 2-byte (bf16) or 4-byte (fp32) offsets,
-    # so every tensor takes the scalar path
-    run_state([(37, 52), (52, 37), (64, 128)], steps=2, k=5, prec="bf16", gdt=gdt, mdt=mdt,
-              wid=91, offset=1, label=f"state misaligned G={gdt} M={mdt}")
+    # so every tensor takes the scalar path; bf16 operands with K >= 1 run
+    # the fused momentum + cast, fp32 operands and K = 0 the streaming
+    # momentum kernel
+    run_state([(37, 52), (52, 37), (64, 128)], steps=2, k=k, prec=prec, gdt=gdt, mdt=mdt,
+              wid=91, offset=1, label=f"state misaligned G={gdt} M={mdt} {prec} k={k}")
 
 
 @pytest.mark.parametrize("prec", ["bf16", "fp32"])
