@@ -162,6 +162,18 @@ def test_ragged_groups(prec, k):
     run_host_workload(RAGGED, steps=3, k=k, prec=prec, wid=51, label=f"ragged k={k} {prec}")
 
 
+# 40 distinct shapes: more shape groups than one launch descriptor holds
+# (16), so every phase runs as several grouped launches, and the finalize
+# kernels see matrix ranges that are not the whole plan.
+MANY = [(8 + 7 * i, 300 - 6 * i) for i in range(40)]
+
+
+@pytest.mark.parametrize("prec,k", [("bf16", 5), ("split_bf16", 5), ("fp32", 5), ("bf16", 0)])
+def test_more_shape_groups_than_one_launch_holds(prec, k):
+    assert len(set(MANY)) == 40
+    run_host_workload(MANY, steps=2, k=k, prec=prec, wid=57, label=f"40 groups {prec} k={k}")
+
+
 @pytest.mark.parametrize("prec", ["bf16", "split_bf16"])
 def test_eight_iterations(prec):
     run_host_workload([(384, 640), (640, 384)], steps=2, k=8, prec=prec, wid=52,
