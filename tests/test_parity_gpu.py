@@ -348,6 +348,38 @@ def test_tall_matrix_equals_transposed_wide(prec):
     assert rel(W[1].cpu().numpy(), W[0].cpu().numpy().T) <= tol_w
 
 
+def test_caller_stream_is_used():
+    # the same steps on a second stream (default priority) and on the default
+    # stream give identical bits; the second stream's work is ordered only by
+    # that stream, so a launch on the wrong stream would race with the copies
+    need_gpu()
+    import orthogonalized_updates_amd as mh
+    shapes = [(300, 200), (200, 300), (512, 512)]
+    outs = []
+    for use_side in (False, True):
+        side = torch.cuda.Stream()
+        ctx = torch.cuda.stream(side) if use_side else torch.cuda.stream(torch.cuda.current_stream())
+        with ctx:
+            opt = make_opt(shapes, "bf16")
+            W = [torch.from_numpy(workloads.host_custom(s, 0.02, (75, 0, i))).to("cuda") for i, s in enumerate(shapes)]
+            M = [torch.zeros(s, device="cuda") for s in shapes]
+            opt.init(W)
+            for st in range(3):
+                G = [torch.from_numpy(workloads.host_custom(s, 0.01, (75, st + 1, i))).to("cuda")
+                     for i, s in enumerate(shapes)]
+                opt.step(W, G, M, 0.02, 0.95, 5)
+            ad = mh.AdamW([1000, 4099])
+            P = [torch.from_numpy(workloads.host_custom((n,), 0.02, (75, 9, n))).to("cuda") for n in (1000, 4099)]
+            Z = [[torch.zeros(n, device="cuda") for n in (1000, 4099)] for _ in range(2)]
+            Gd = [torch.from_numpy(workloads.host_custom((n,), 0.01, (75, 10, n))).to("cuda") for n in (1000, 4099)]
+            ad.step(P, Gd, Z[0], Z[1], lr=1e-3, step=1)
+            res = [w.cpu().numpy() for w in W] + [m.cpu().numpy() for m in M] + [p.cpu().numpy() for p in P]
+        torch.cuda.synchronize()
+        outs.append(res)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads in the benchmark's launch configuration, sampled
 # ---------------------------------------------------------------------------
