@@ -1,11 +1,14 @@
 // HBM-bound phases of the MuonH step on gfx950: the init norm, the momentum
-// update with its norm, the bf16/fp32 cast of the normalised momentum into
-// both Newton-Schulz layouts, the trial update with its norm, and the
-// projection back onto the sphere. Every kernel is one grouped launch over all
-// matrices of all shape groups; blocks stream contiguous chunks with 16-byte
-// accesses. Norms are deterministic two-level reductions: fp32 per thread, a
-// fixed shuffle tree in fp64 per block, then a fixed-order fp64 sum of the
-// per-block partials in a separate finalize kernel (no float atomics).
+// update with its norm (alone, or fused with the cast of the unscaled
+// momentum into the Newton-Schulz operand layout), the normalised cast, the
+// trial update with its norm, the projection back onto the sphere, and the
+// Muon baseline's decayed update. G and M are fp32 or bf16 (St<BF>), W is
+// fp32. Every kernel is one grouped launch over the matrices of up to 16
+// shape groups; blocks stream contiguous chunks with 16-byte accesses
+// (8-byte for bf16 G and M), non-temporal on the M and W streams. Norms are
+// deterministic two-level reductions: fp32 per thread, a fixed shuffle tree
+// in fp64 per block, then a fixed-order fp64 sum of the per-block partials
+// in a separate finalize kernel (no float atomics).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

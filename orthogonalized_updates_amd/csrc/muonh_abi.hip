@@ -2,10 +2,16 @@
 // validation, workspace layout and the fixed launch sequence of one step.
 //
 // Step sequence (all grouped launches over every matrix of the plan):
-//   momentum (M <- beta M + G, partial ||M||^2)  -> finalize ||M||
-//   normcast (X0 = M/(||M||+eps) into X and X^T, bf16 or fp32, zero-padded)
+//   bf16 or split operands with ns_iters >= 1:
+//     momentum + cast (M <- beta M + G stored, Y = M unscaled in the
+//     operand layout, partial ||M||^2) -> finalize ||M|| -> cast fallback
+//     (rewrites X0 normalised only for norms outside [2^-40, 2^40]); the
+//     first Gram and apply then scale by 1/(||M||+eps)
+//   otherwise: momentum -> finalize -> normcast (X0 = M/(||M||+eps))
 //   ns_iters x { Gram A = X X^T ; Poly B = bA + cAA ; Apply X <- aX + BX }
-//   update (partial ||W - lr O||^2) -> finalize -> project (W <- R W'/||W'||)
+//   MuonH: update (partial ||W - lr O||^2) -> finalize -> project
+//          (W <- R W'/||W'||)
+//   Muon baseline: decayed update (W <- (1 - lr wd) W - lr O)
 // The projection onto the fixed sphere follows the digest page "Puro-2B
 // trains for $6.9K, attention sinks hit 99%, LoopArena tops at 24.69%",
 // section "The load-bearing tricks aren't in the abstract"; the absence of a

@@ -6,22 +6,23 @@
 // (s x l, zero-padded) the step computes
 //   A = X X^T                  (symmetric: upper tiles only, mirrored)
 //   B = b A + c A A            (A symmetric, so A A = A A^T: same kernel shape)
-//   X <- a X + B X             (B X = B (X^T)^T: operands are B rows, X^T rows)
-// so every product is C[i][j] = sum_k P[i][k] Q[j][k] with both operands read
-// along K. The apply step writes the new X in both layouts (X and X^T) so that
-// the next Gram and the next apply again read their operands along K.
+//   X <- a X + B X             (operands: rows of B, and X itself read K-major)
+// so every product is C[i][j] = sum_k P[i][k] Q[k][j].
 //
-// Every launch covers one phase for all matrices of all shape groups: one
-// workgroup per output tile, tiles dealt to the 8 XCDs in contiguous runs.
-// bf16 (the product path): operands stored panel-major (256 rows x 64 bytes
-// per panel), 256x256 tiles, 8 waves in two groups that take turns between
-// MFMA clusters (v_mfma_f32_32x32x16_bf16, fp32 accumulation) and LDS
-// fragment loads plus LDS DMA refills (global_load_lds_dwordx4) of a 4-stage
-// ring of 32 KB stages, the fp32 a*X or b*A term folded into the accumulators
-// from the operand stream, and epilogues staged through LDS for coalesced
-// stores of both output layouts.
+// Every launch covers one phase for all matrices of up to 16 shape groups:
+// one workgroup per output tile, tiles dealt to the 8 XCDs in contiguous runs.
+// bf16 and split bf16 (the product path): operands stored panel-major (256
+// rows x 64 bytes per panel), 256x256 tiles, 8 waves in two groups that take
+// turns between MFMA clusters (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
+// and LDS fragment loads plus LDS DMA refills (global_load_lds_dwordx4) of a
+// 4-stage ring of 32 KB stages. The apply reads its X operand K-major with
+// transposed LDS reads (ds_read_b64_tr_b16), so X has one layout; the fp32
+// a*X or b*A term is folded into the accumulators from the operand stream.
+// Row-major outputs are stored straight from registers, transposed ones
+// (mirrored tiles, O of tall matrices) staged through the idle ring.
 // fp32 debug: a simpler 128x128 kernel on v_mfma_f32_32x32x2f32 with
-// register-staged double buffering and direct epilogue stores.
+// register-staged double buffering and direct epilogue stores; it reads both
+// operands along K, so that mode keeps X and X^T copies.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
