@@ -10,8 +10,8 @@
  *     Frobenius norm at its initialization value by projecting updates onto a
  *     fixed hypersphere; Muon's overhead is its Newton-Schulz iterations;
  *   - model card "Puro", section "Training": MuonH with hyperball projection
- *     and zero weight decay on the matrix group; FP32 master weights and
- *     optimizer state.
+ *     and zero weight decay on the matrix group; master weights and optimizer
+ *     state in FP32 or BF16 (W fp32 here; G and M fp32 or bf16 by plan flag).
  *
  * One step, per matrix (rows x cols, row-major fp32):
  *   M  <- beta*M + G                                  (heavy-ball momentum)
