@@ -11,6 +11,12 @@ LoopArena tops at 24.69%", section "The load-bearing tricks aren't in the
 abstract"; model card "Puro", section "Training"): momentum, Newton-Schulz
 orthogonalization, then projection of every weight matrix back onto the
 sphere of its initial Frobenius norm, with no weight decay.
+
+MuonH(shapes, precision=..., grad_dtype=..., mom_dtype=...) runs the step
+(step, step_timed) and, on the same plan, the Muon baseline with decoupled
+weight decay (step_muon_wd); AdamW(numels) updates the parameters outside
+the matrix group. Gradients and momenta may be float32 or bfloat16 tensors
+(grad_dtype / mom_dtype); weights are float32.
 """
 from __future__ import annotations
 
