@@ -412,8 +412,11 @@ def main() -> int:
     pre_ms, post_ms = pre / nst, post / nst
     dom = max(phase, key=lambda p: phase[p]) if k > 0 else None
 
-    kernel_names = {"gram": "k_ns_gemm_bf16<Gram>", "poly": "k_ns_gemm_bf16<Poly>",
-                    "apply": "k_ns_gemm_bf16<Apply>"}
+    # bf16 operands run the 16x16x32 kernel, split bf16 the 32x32x16 one
+    kname = "k_ns_gemm_m16" if args.precision == "bf16" else "k_ns_gemm_bf16"
+    if fp32:
+        kname = "k_ns_gemm<fp32>"
+    kernel_names = {p: f"{kname}<{p.capitalize()}>" for p in ("gram", "poly", "apply")}
     if dom is not None:
         avg_ms = phase[dom] / launches
         achieved = flops[dom] / (avg_ms * 1e-3) / 1e12

@@ -13,9 +13,10 @@
 // one workgroup per output tile, tiles dealt to the 8 XCDs in contiguous runs.
 // bf16 and split bf16 (the product path): operands stored panel-major (256
 // rows x 64 bytes per panel), 256x256 tiles, 8 waves in two groups that take
-// turns between MFMA clusters (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
-// and LDS fragment loads plus LDS DMA refills (global_load_lds_dwordx4) of a
-// 4-stage ring of 32 KB stages. The apply reads its X operand K-major with
+// turns between MFMA clusters (bf16: v_mfma_f32_16x16x32_bf16; split:
+// v_mfma_f32_32x32x16_bf16; fp32 accumulation) and LDS fragment loads plus
+// LDS DMA refills (global_load_lds_dwordx4) of a 4-stage ring of 32 KB
+// stages. The apply reads its X operand K-major with
 // transposed LDS reads (ds_read_b64_tr_b16), so X has one layout; the fp32
 // a*X or b*A term is folded into the accumulators from the operand stream.
 // Row-major outputs are stored straight from registers, transposed ones
@@ -692,6 +693,9 @@ __device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, const bf::QtSrc
   }
 }
 
+// The 32x32x16 kernel. The library launches it for split-bf16 operands; the
+// plain bf16 instantiation (SPLIT = false) is the reference the 16x16x32
+// kernel below (k_ns_gemm_m16) was checked against, bit for bit.
 template <int MODE, int WGM, int WGN, bool SPLIT>
 __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf16(GemmArgs args) {
   using namespace bf;
@@ -896,17 +900,249 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel (the default operand format): the same tile, ring, DMA and
+// ping-pong schedule as k_ns_gemm_bf16, on v_mfma_f32_16x16x32_bf16. One
+// instruction takes a whole 32-k stage; a wave's 128 x 64 tile is 8 x 4
+// blocks of 16 x 16, 32 instructions per stage (the work of 16
+// 32x32x16). On random bf16 data this shape sustains about 16 % more
+// throughput than 32x32x16 at the same occupancy (register-only loop: 2.0
+// against 1.72 PFLOP/s; on all-zero data both reach ~2.47), and its results
+// are bit for bit those of the 32x32x16 kernel (every launch of the Gram,
+// polynomial and apply compared). Lane layouts: A and B fragments, lane l
+// holds row (column) l%16, k = 8(l/16) .. +7; accumulators, lane l holds
+// rows 4(l/16) .. +3 of column l%16.
+// ---------------------------------------------------------------------------
+namespace m16 {
+using namespace bf;
+constexpr int kMT = 8, kNT = 4;  // 16x16 blocks of a 128 x 64 wave tile
+struct F { bf16x8 a[kMT], b[kNT]; };
+// Lane parts of LDS addresses: f row fragments (row l%16, chunk l/16,
+// swizzled); q transposed B fragment reads of the apply (rows 8(l/16) +
+// (l%16)/4, columns 4(l%4) .. +3 of a 16-column block); e transposed E reads
+// (rows 4(l/16) + (l%16)/4).
+struct Offs { int f, q, e; };
+
+// QT stage for this kernel: as qt_src (bf16), but rows with bit 3 set hold
+// their two 32-byte halves swapped, so that the two 16-lane groups of a
+// transposed read (rows 8 apart, same columns) use different banks.
+__device__ __forceinline__ QtSrc qt_src16(const char* X, int ldx, int bj, int wave, int lane) {
+  QtSrc d;
+  const char* base = X + (int64_t)bj * 8 * kPanel;
+  const int lo = (lane >> 2) * kPRow + (((lane & 3) ^ (2 * ((lane >> 5) & 1))) << 4);
+  d.g[0] = d.g[1] = base + lo;
+  d.rbs = (int64_t)(ldx / 32) * kPanel;
+  d.lds = (uint32_t)(kPanel + (wave & 3) * 4096);
+  return d;
+}
+
+// Main loop: as pingpong (same phases, barriers and refills), with one
+// 32-k fragment set per stage. The E term: accumulator rows 16 mi .. +15 lie
+// in one stage, read as 4 consecutive k of the lane's column (transposed
+// read for the apply, a plain 8-byte read of A's row for the polynomial).
+template <int G, bool E_TERM, bool QT>
+__device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc, int nk,
+                                           const char* ring, uint32_t ring_lds, int wave, int wm0,
+                                           int wn0, const Offs& o, int lane, int bi, float seed,
+                                           f32x4 (&acc)[kMT][kNT]) {
+  F f;
+  const int g = lane >> 4;
+  auto take_e = [&](const char* buf, int kt) {
+    const int r = kt * 32 - 256 * bi - wm0;  // stage row of accumulator row 0 is -r
+    if (r < 0 || r >= kMT * 16) return;  // r is a multiple of 32
+    const char* lb = buf + kPanel;
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi) {
+      if (16 * mi < r || 16 * mi >= r + 32) continue;
+#pragma unroll
+      for (int ni = 0; ni < kNT; ++ni) {
+        const int n0 = wn0 + 16 * ni;
+        bf16x4 hv;
+        if (QT) {
+          hv = read_tr(lb + (n0 >> 5) * 2048 + (16 * mi - r) * kPRow + o.e +
+                       ((((n0 & 31) << 1) ^ (32 * ((g >> 1) & 1)))));
+        } else {
+          const int kk = 16 * mi - r + 4 * g;
+          const int qrow = n0 + (lane & 15);
+          hv = *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, kk >> 3) + ((kk & 7) << 1));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(seed, (float)hv[q], acc[mi][ni][q]);
+      }
+    }
+  };
+  auto load = [&](int kt) {
+    const char* buf = ring + (kt & (kNBuf - 1)) * kStage;
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+      f.a[mi] = *reinterpret_cast<const bf16x8*>(buf + (wm0 + 16 * mi) * kPRow + o.f);
+#pragma unroll
+    for (int ni = 0; ni < kNT; ++ni) {
+      const int n0 = wn0 + 16 * ni;
+      if (QT) {
+        const char* p = buf + kPanel + (n0 >> 5) * 2048 + o.q + ((((n0 & 31) << 1) ^ (32 * (g & 1))));
+        f.b[ni] = cat8(read_tr(p), read_tr(p + 4 * kPRow));
+      } else {
+        f.b[ni] = *reinterpret_cast<const bf16x8*>(buf + kPanel + n0 * kPRow + o.f);
+      }
+    }
+    if (E_TERM) take_e(buf, kt);
+  };
+  auto mul = [&]() {
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNT; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+  };
+  auto refill = [&](int kt) {
+    const uint32_t buf = ring_lds + (kt & (kNBuf - 1)) * kStage;
+    if (QT && G == 0) issue_share_qt<false>(qsrc, wave, kt, buf);
+    else issue_share(dsrc, kt, buf);
+  };
+  if (G == 0) load(0);
+  phase_barrier<>();
+  for (int s = 0; s < nk; ++s) {
+    if (G == 0) {
+      mul();
+    } else {
+      load(s);
+      if (s >= 1 && s + 3 < nk) refill(s + 3);
+    }
+    phase_barrier_n((s + 2 < nk) + (s + 3 < nk));
+    if (G == 0) {
+      if (s + 1 < nk) load(s + 1);
+      if (s + 4 < nk) refill(s + 4);
+    } else {
+      mul();
+    }
+    phase_barrier<>();
+  }
+}
+
+// The kernel: tile mapping, operand pointers, DMA prologue and scaling as in
+// k_ns_gemm_bf16; the epilogue stores row-major output from registers after
+// a quad transpose (lane: 4 columns of one row, 8 bytes) and stages the
+// transposed output through the ring.
+template <int MODE>
+__global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
+  constexpr bool kSym = (MODE != kApply);
+  constexpr bool kQT = (MODE == kApply);
+  __shared__ __attribute__((aligned(1024))) char ring[kNBuf * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / 4, wn = wave - (wave / 4) * 4;
+  int gi, local;
+  if (!map_tile(args, blockIdx.x, gi, local)) return;
+  const GemmGroup& g = args.g[gi];
+  const int mat = local / g.tiles_per_mat;
+  int bi, bj;
+  tile_coords<kSym>(g, local - mat * g.tiles_per_mat, bi, bj);
+  const char* blk = g.base + (int64_t)mat * g.mat_bytes;
+  const char* P = blk + g.offP + (int64_t)bi * kBM * g.ldp * 2;
+  const char* Q = blk + g.offQ + (kQT ? 0 : (int64_t)bj * kBN * g.ldq * 2);
+  f32x4 acc[kMT][kNT];
+#pragma unroll
+  for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNT; ++ni) acc[mi][ni] = f32x4{};
+  const int nk = g.K / 32;
+  const int wm0 = wm * 128, wn0 = wn * 64;
+  Offs o;
+  {
+    const int i = lane & 15, gg = lane >> 4;
+    o.f = i * kPRow + ((gg ^ ((i >> 2) & 3)) << 4);
+    o.q = (8 * gg + (i >> 2)) * kPRow + 8 * (i & 3);
+    o.e = (4 * gg + (i >> 2)) * kPRow + 8 * (i & 3);
+  }
+  const DmaSrc dsrc = dma_src(P, Q, wave, lane);
+  const QtSrc qsrc = qt_src16(Q, g.ldq, bj, wave, lane);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
+#pragma unroll
+  for (int st = 0; st < kNBuf; ++st) {
+    if (kQT && wave < 4) issue_share_qt<false>(qsrc, wave, st, ring_lds + st * kStage);
+    else issue_share(dsrc, st, ring_lds + st * kStage);
+  }
+  phase_barrier<12>();
+  const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
+  if (wave < 4)
+    pingpong16<0, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
+  else
+    pingpong16<1, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
+
+  float scale = MODE == kPoly ? args.c1 : 1.f;
+  if (MODE != kPoly && args.xnorm) {
+    const float sg = x0_sigma(args.xnorm[g.first + mat]);
+    scale = MODE == kGram ? sg * sg : sg;
+  }
+  bf16x4 vh[kMT][kNT];
+#pragma unroll
+  for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNT; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vh[mi][ni][q] = (__bf16)(scale * acc[mi][ni][q]);
+  char* stg = const_cast<char*>(ring);
+  auto srow = [&](int row) -> char* { return stg + (row >> 6) * kStage + (row & 63) * 512; };
+  char* O1 = g.offO1 < 0 ? nullptr : const_cast<char*>(blk) + g.offO1;
+  char* O2 = g.offO2 < 0 ? nullptr : const_cast<char*>(blk) + g.offO2;
+  char* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;
+  const int ldT = kSym ? g.ldo1 : g.ldo2;
+  if (O1) {
+    char* region = O1 + (int64_t)bi * kBM * g.ldo1 * 2 + (int64_t)bj * 8 * kPanel;
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNT; ++ni) {
+        const int col = wn0 + 16 * ni + (lane & 12);
+        const int row = wm0 + 16 * mi + 4 * (lane >> 4) + (lane & 3);
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 d = __builtin_bit_cast(u32x2, vh[mi][ni]);
+        uint32_t d0 = d.x, d1 = d.y;
+        quad_transpose(d0, d1, lane);
+        d.x = d0;
+        d.y = d1;
+        *reinterpret_cast<u32x2*>(region + (int64_t)(col >> 5) * kPanel + ((col & 31) << 1) + row * kPRow) = d;
+      }
+  }
+  if (OT) {
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < kNT; ++ni) {
+        const int col = wn0 + 16 * ni + (lane & 15);
+        const int row0 = wm0 + 16 * mi + 4 * (lane >> 4);
+        const int off = ((((row0 >> 3) ^ (col & 31)) << 4) | ((row0 & 7) << 1));
+        *reinterpret_cast<bf16x4*>(srow(col) + off) = vh[mi][ni];
+      }
+    __syncthreads();
+    char* region = OT + (int64_t)bj * kBM * ldT * 2 + (int64_t)bi * 8 * kPanel;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = tid + i * 512;
+      const int row = (id & 1023) >> 2;
+      const int c = ((id >> 10) << 2) | (id & 3);
+      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ (row & 31)) << 4));
+      *reinterpret_cast<u32x4*>(region + (int64_t)id * 16) = d;
+    }
+  }
+}
+}  // namespace m16
+
 // fp32 debug path: the generic 128x128 kernel with 4 waves (2 x 2).
 constexpr int kTile32 = 128;
 
 template <typename T, int MODE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s, bool split) {
   if constexpr (std::is_same<T, __bf16>::value) {
-    // bf16: 256x256 tiles, 8 waves in a 2 x 4 grid (wave tile 128 x 64).
+    // 256x256 tiles, 8 waves in a 2 x 4 grid (wave tile 128 x 64): bf16 on
+    // 16x16x32 MFMAs, split bf16 (hi + lo per 64-byte panel row, three
+    // products per stage) on 32x32x16.
     if (split)
       hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4, true>), dim3(a.grid), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4, false>), dim3(a.grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((m16::k_ns_gemm_m16<MODE>), dim3(a.grid), dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL((k_ns_gemm<T, kTile32, kTile32, 2, 2, MODE>), dim3(a.ntiles), dim3(256), 0,
                        s, a);
