@@ -134,17 +134,29 @@ def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1, mom_bf16=Fa
     }
 
 
+def code_sha16(path: str) -> str:
+    """First 16 hex digits of the SHA-256 of a source file's code: each line
+    with any // comment cut off and trailing blanks stripped, blank lines
+    dropped, so that comment edits do not count as changes."""
+    import hashlib
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def committed_traffic(kernel_name: str, summary: str, source: str = "ns_gemm.hip"):
     """HBM bytes per launch of `kernel_name` from the committed rocprofv3
     counter summary profiles/`summary` (FETCH_SIZE + WRITE_SIZE, each scaled
     by its factor on a plain copy of known size), or None when there is no
-    such summary or the kernel's source file has changed since the counters
-    were taken (the summary records the first 16 hex digits of its SHA-256)."""
-    import hashlib
+    such summary or the kernel's source code has changed since the counters
+    were taken (the summary records code_sha16 of the source)."""
     path = os.path.join(ROOT, "profiles", summary)
     src = os.path.join(ROOT, "orthogonalized_updates_amd", "csrc", source)
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = code_sha16(src)
         for line in open(path):
             line = line.strip()
             if line.startswith("{") and '"traffic_bytes_per_launch"' in line:

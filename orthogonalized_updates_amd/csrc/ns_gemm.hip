@@ -948,8 +948,9 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
   F f;
   const int g = lane >> 4;
   auto take_e = [&](const char* buf, int kt) {
-    const int r = kt * 32 - 256 * bi - wm0;  // stage row of accumulator row 0 is -r
-    if (r < 0 || r >= kMT * 16) return;  // r is a multiple of 32
+    // accumulator row rho (from wm0) takes its E value from stage row rho - r
+    const int r = kt * 32 - 256 * bi - wm0;  // a multiple of 32
+    if (r < 0 || r >= kMT * 16) return;
     const char* lb = buf + kPanel;
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi) {

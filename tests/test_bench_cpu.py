@@ -49,14 +49,18 @@ def test_committed_traffic_lookup(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     src_dir = tmp_path / "orthogonalized_updates_amd" / "csrc"
     src_dir.mkdir(parents=True)
-    (src_dir / "k.hip").write_text("kernel source\n")
-    sha = hashlib.sha256(b"kernel source\n").hexdigest()[:16]
+    (src_dir / "k.hip").write_text("// header\nkernel source\n\n")
+    sha = hashlib.sha256(b"kernel source").hexdigest()[:16]
+    assert bench.code_sha16(str(src_dir / "k.hip")) == sha
     rec = {"kernel": "k_x", "source": "k.hip", "source_sha256_16": sha, "traffic_bytes_per_launch": 1234}
     (tmp_path / "profiles" / "s.md").write_text("# summary\n\n```\n" + json.dumps(rec) + "\n```\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.committed_traffic("k_x", "s.md", "k.hip") == 1234
     assert bench.committed_traffic("k_y", "s.md", "k.hip") is None        # other kernel
     assert bench.committed_traffic("k_x", "missing.md", "k.hip") is None  # no summary
+    # comments and blank lines are not code: the counters stay valid
+    (src_dir / "k.hip").write_text("// reworded header\n\nkernel source  // note\n")
+    assert bench.committed_traffic("k_x", "s.md", "k.hip") == 1234
     (src_dir / "k.hip").write_text("kernel source, changed\n")
     assert bench.committed_traffic("k_x", "s.md", "k.hip") is None        # stale counters
 
