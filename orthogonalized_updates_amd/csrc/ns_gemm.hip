@@ -502,9 +502,8 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& args, int b, int& gi, i
 }
 
 // Tile coordinates of local tile t of a matrix. Symmetric modes walk the
-// upper triangle row by row; the apply walks bands of 8 tile rows column by
-// column (consecutive tiles share a column block of X and up to 8 row blocks
-// of B; 8 was 0.6 % faster than 4 and 1.5 % faster than 2 on 2048 x 6144).
+// upper triangle row by row; the apply groups rows in bands of 4 tile rows
+// (4 x 8 = 32 consecutive tiles share 4 B row-blocks and 8 X^T row-blocks).
 template <bool kSym>
 __device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, int& bj) {
   if (kSym) {
@@ -517,7 +516,7 @@ __device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, 
     }
     bj = bi + t;
   } else {
-    constexpr int kBand = 8;
+    constexpr int kBand = 4;
     const int gsz = kBand * g.tn;
     const int band = t / gsz;
     const int first = band * kBand;
