@@ -504,6 +504,9 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& args, int b, int& gi, i
 // Tile coordinates of local tile t of a matrix. Symmetric modes walk the
 // upper triangle row by row; the apply groups rows in bands of 4 tile rows
 // (4 x 8 = 32 consecutive tiles share 4 B row-blocks and 8 X^T row-blocks).
+// Bands of 8 ran the 2048 x 6144 apply 0.6 % faster in isolation but read
+// 23 % more from HBM in the full step (10.1 against 8.2 GB per launch) at
+// the same speed there.
 template <bool kSym>
 __device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, int& bj) {
   if (kSym) {
