@@ -174,6 +174,19 @@ def test_more_shape_groups_than_one_launch_holds(prec, k):
     run_host_workload(MANY, steps=2, k=k, prec=prec, wid=57, label=f"40 groups {prec} k={k}")
 
 
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_maximum_dimension(prec):
+    # the largest dimension a plan accepts (65536) on both sides: the Gram of
+    # the short side runs over K = 65536 (2048 ring stages), the tall matrix
+    # takes the transposed path
+    import orthogonalized_updates_amd as mh
+    need_gpu()
+    mh.get_lib()
+    top = 65536
+    run_host_workload([(top, 256), (256, top)], steps=1, k=5, prec=prec, wid=58,
+                      label=f"max dim {prec}")
+
+
 @pytest.mark.parametrize("prec", ["bf16", "split_bf16"])
 def test_eight_iterations(prec):
     run_host_workload([(384, 640), (640, 384)], steps=2, k=8, prec=prec, wid=52,
