@@ -435,6 +435,40 @@ def test_qwen3_2b_full_size_sampled():
     run_device_workload("qwen3_2b", steps=2, k=5, sample=sample, label="qwen3_2b")
 
 
+def test_long_run_stays_on_the_sphere():
+    # 60 consecutive steps on the full 2B-shaped set with fresh gradients:
+    # every matrix keeps its radius (projection error does not accumulate),
+    # W and M stay finite, and the last step still matches the oracle on
+    # sampled matrices
+    need_gpu()
+    torch.cuda.empty_cache()
+    wl = workloads.WORKLOADS["qwen3_2b"]
+    dev = torch.device("cuda")
+    opt = make_opt(wl.shapes, "bf16")
+    W = [workloads.device_weight_(wl, i, torch.empty(s, device=dev)) for i, s in enumerate(wl.shapes)]
+    M = [torch.zeros(s, device=dev) for s in wl.shapes]
+    G = [torch.empty(s, device=dev) for s in wl.shapes]
+    R_host = opt.init(W).cpu().numpy()
+    sample = [0, 6, 100, 195]
+    steps = 60
+    for step in range(steps):
+        for i in range(len(wl.shapes)):
+            workloads.device_grad_(wl, i, 1000 + step, G[i])
+        if step == steps - 1:
+            W_pre = {i: W[i].cpu().numpy() for i in sample}
+            M_pre = {i: M[i].cpu().numpy() for i in sample}
+            G_host = {i: G[i].cpu().numpy() for i in sample}
+        opt.step(W, G, M, wl.lr, wl.beta, 5)
+        if step % 20 == 0:
+            say(f"[long run] step {step}")
+    torch.cuda.synchronize()
+    norms = torch.stack([torch.linalg.vector_norm(w.double()) for w in W]).cpu().numpy()
+    assert np.max(np.abs(norms / R_host - 1.0)) <= 1e-5
+    assert all(bool(torch.isfinite(w).all()) and bool(torch.isfinite(m).all()) for w, m in zip(W, M))
+    check_step(opt, W, M, G_host, W_pre, M_pre, R_host, wl.lr, wl.beta, 5, "bf16", sample,
+               "long run, last step")
+
+
 def test_occupancy_full_size_sampled():
     run_device_workload("occupancy_512x1536", steps=2, k=5, sample=[0, 1, 255, 256, 300, 511],
                         label="occupancy")
