@@ -939,6 +939,20 @@ __device__ __forceinline__ QtSrc qt_src16(const char* X, int ldx, int bj, int wa
   return d;
 }
 
+// After quad_transpose, lanes l and l^4 hold the two 4-column halves of 8
+// columns of one row, for each of two blocks X and Y. Exchanging halves across
+// the pair (DPP row shifts by 4 lanes) leaves lane l (bit 2 clear) with the 8
+// columns of X and lane l^4 with those of Y: one 16-byte store each.
+__device__ __forceinline__ u32x4 pair_halves(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1, int lane) {
+  const bool hi = (lane & 4) != 0;
+  const uint32_t s0 = hi ? x0 : y0, s1 = hi ? x1 : y1;
+  const uint32_t a0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0x104, 0xF, 0xF, false);  // row_shl:4, from lane + 4
+  const uint32_t a1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x104, 0xF, 0xF, false);
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0x114, 0xF, 0xF, false);  // row_shr:4, from lane - 4
+  const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x114, 0xF, 0xF, false);
+  return hi ? u32x4{b0, b1, y0, y1} : u32x4{x0, x1, a0, a1};
+}
+
 // Main loop: as pingpong (same phases, barriers and refills), with one
 // 32-k fragment set per stage. The E term: accumulator rows 16 mi .. +15 lie
 // in one stage, read as 4 consecutive k of the lane's column (transposed
@@ -1026,8 +1040,8 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
 
 // The kernel: tile mapping, operand pointers, DMA prologue and scaling as in
 // k_ns_gemm_bf16; the epilogue stores row-major output from registers after
-// a quad transpose (lane: 4 columns of one row, 8 bytes) and stages the
-// transposed output through the ring.
+// a quad transpose and a pairwise exchange (lane: 8 columns of one row, 16
+// bytes) and stages the transposed output through the ring.
 template <int MODE>
 __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   constexpr bool kSym = (MODE != kApply);
@@ -1093,20 +1107,27 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   char* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;
   const int ldT = kSym ? g.ldo1 : g.ldo2;
   if (O1) {
+    // Blocks ni = 2p and 2p + 1 share one 64-byte panel row: after the
+    // exchange, lane l holds columns 8 * (l/8 % 2) .. +7 of block 2p + (l/4 % 2)
+    // in row 4 (l/16) + l%4 of the block row, so one store instruction writes
+    // 16 whole panel rows (1 KB, contiguous). With 8-byte stores (half rows)
+    // a CU wrote its 128 KB tile 3.5 times slower, and the L2 fetched part of
+    // the partially written lines from HBM.
     char* region = O1 + (int64_t)bi * kBM * g.ldo1 * 2 + (int64_t)bj * 8 * kPanel;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int chunk = ((lane >> 1) & 2) | ((lane >> 3) & 1);  // 16-byte chunk of the panel row
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < kNT; ++ni) {
-        const int col = wn0 + 16 * ni + (lane & 12);
+      for (int p = 0; p < kNT / 2; ++p) {
+        const u32x2 x = __builtin_bit_cast(u32x2, vh[mi][2 * p]);
+        const u32x2 y = __builtin_bit_cast(u32x2, vh[mi][2 * p + 1]);
+        uint32_t x0 = x.x, x1 = x.y, y0 = y.x, y1 = y.y;
+        quad_transpose(x0, x1, lane);
+        quad_transpose(y0, y1, lane);
+        const u32x4 d = pair_halves(x0, x1, y0, y1, lane);
         const int row = wm0 + 16 * mi + 4 * (lane >> 4) + (lane & 3);
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        u32x2 d = __builtin_bit_cast(u32x2, vh[mi][ni]);
-        uint32_t d0 = d.x, d1 = d.y;
-        quad_transpose(d0, d1, lane);
-        d.x = d0;
-        d.y = d1;
-        *reinterpret_cast<u32x2*>(region + (int64_t)(col >> 5) * kPanel + ((col & 31) << 1) + row * kPRow) = d;
+        *reinterpret_cast<u32x4*>(region + (int64_t)((wn0 + 32 * p) >> 5) * kPanel + row * kPRow + (chunk << 4)) = d;
       }
   }
   if (OT) {
