@@ -295,13 +295,15 @@ struct Cfg {
   static_assert(kWaves == 8, "the ping-pong schedule and the DMA split assume 8 waves");
 };
 
-// Chunk (16 B) c of panel row r sits at r*64 + ((c ^ ((r >> 2) & 3)) << 4).
-// A ds_read_b128 is served 16 lanes at a time from 64 four-byte banks (256
-// bytes); the 16 consecutive rows one pass reads (one chunk each) then fall
-// on 16 distinct 16-byte slots: r & 3 picks the 64-byte quarter of the bank
-// window, the swizzled chunk a slot within it.
+// Chunk (16 B) c of panel row r sits at r*64 + ((c ^ ((r >> SH) & 3)) << 4).
+// The shift matches the fragment reads of each kernel, measured with an LDS
+// probe (8 waves per CU, ds_read_b128): a 32x32x16 fragment read (32 rows,
+// 2 chunks) is conflict-free with SH = 2, a 16x16x32 read (16 rows, 4
+// chunks) with SH = 1, and each runs at half the rate (8 instead of 4.3
+// cycles per instruction per CU, two-way bank conflicts) with the other.
+template <int SH = 2>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kPRow + ((chunk ^ ((row >> 2) & 3)) << 4);
+  return row * kPRow + ((chunk ^ ((row >> SH) & 3)) << 4);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -335,18 +337,20 @@ __device__ __forceinline__ void phase_barrier_n(int n) {
 // (waves 4-7) refills the A panels, group 0 the B panels; wave w takes rows
 // 64*(w%4) .. +63. Lane l fills LDS bytes 16l .. 16l+15 of an instruction's
 // 1 KB block: panel row l/4 of the instruction's 16, position l%4, which must
-// hold chunk (l%4) ^ ((row >> 2) & 3); for every instruction of every wave
-// (row >> 2) & 3 = (l >> 4) & 3, so the per-lane source offset is fixed.
+// hold chunk (l%4) ^ ((row >> SH) & 3); for every instruction of every wave
+// (row >> SH) & 3 = (l >> (2 + SH)) & 3, so the per-lane source offset is
+// fixed.
 struct DmaSrc {
   const char* g;  // per-lane source address of instruction 0, stage 0
   uint32_t lds;   // LDS offset of this wave's share within a stage buffer
 };
 
+template <int SH = 2>
 __device__ __forceinline__ DmaSrc dma_src(const char* P, const char* Q, int wave, int lane) {
   const bool isA = wave >= 4;
   DmaSrc d;
   d.g = (isA ? P : Q) + (wave & 3) * 4096 + (lane >> 2) * kPRow +
-        (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+        (((lane & 3) ^ ((lane >> (2 + SH)) & 3)) << 4);
   d.lds = (uint32_t)((isA ? 0 : kPanel) + (wave & 3) * 4096);
   return d;
 }
@@ -914,7 +918,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 // are bit for bit those of the 32x32x16 kernel (every launch of the Gram,
 // polynomial and apply compared). Lane layouts: A and B fragments, lane l
 // holds row (column) l%16, k = 8(l/16) .. +7; accumulators, lane l holds
-// rows 4(l/16) .. +3 of column l%16.
+// rows 4(l/16) .. +3 of column l%16. Two differences from that kernel's ring:
+// panels are swizzled with SH = 1 (see swz), and in the apply group 1
+// issues the K-major Q refills and group 0 the A refills (the loading group
+// of the second phase of a stage has less work then, measured 1 % faster).
 // ---------------------------------------------------------------------------
 namespace m16 {
 using namespace bf;
@@ -982,7 +989,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
         } else {
           const int kk = 16 * mi - r + 4 * g;
           const int qrow = n0 + (lane & 15);
-          hv = *reinterpret_cast<const bf16x4*>(lb + bf::swz(qrow, kk >> 3) + ((kk & 7) << 1));
+          hv = *reinterpret_cast<const bf16x4*>(lb + bf::swz<1>(qrow, kk >> 3) + ((kk & 7) << 1));
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[mi][ni][q] = fmaf(seed, (float)hv[q], acc[mi][ni][q]);
@@ -1015,7 +1022,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
   };
   auto refill = [&](int kt) {
     const uint32_t buf = ring_lds + (kt & (kNBuf - 1)) * kStage;
-    if (QT && G == 0) issue_share_qt<false>(qsrc, wave, kt, buf);
+    if (QT && G == 1) issue_share_qt<false>(qsrc, wave, kt, buf);
     else issue_share(dsrc, kt, buf);
   };
   if (G == 0) load(0);
@@ -1069,16 +1076,17 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   Offs o;
   {
     const int i = lane & 15, gg = lane >> 4;
-    o.f = i * kPRow + ((gg ^ ((i >> 2) & 3)) << 4);
+    o.f = i * kPRow + ((gg ^ ((i >> 1) & 3)) << 4);
     o.q = (8 * gg + (i >> 2)) * kPRow + 8 * (i & 3);
     o.e = (4 * gg + (i >> 2)) * kPRow + 8 * (i & 3);
   }
-  const DmaSrc dsrc = dma_src(P, Q, wave, lane);
+  // apply: waves 0-3 refill the A panel (dma_src takes waves 4-7 for A)
+  const DmaSrc dsrc = dma_src<1>(P, Q, kQT ? (wave ^ 4) : wave, lane);
   const QtSrc qsrc = qt_src16(Q, g.ldq, bj, wave, lane);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
 #pragma unroll
   for (int st = 0; st < kNBuf; ++st) {
-    if (kQT && wave < 4) issue_share_qt<false>(qsrc, wave, st, ring_lds + st * kStage);
+    if (kQT && wave >= 4) issue_share_qt<false>(qsrc, wave, st, ring_lds + st * kStage);
     else issue_share(dsrc, st, ring_lds + st * kStage);
   }
   phase_barrier<12>();
