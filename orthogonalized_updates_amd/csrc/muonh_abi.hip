@@ -79,6 +79,15 @@ struct GroupPlan {
 // Elements one streaming block handles (before the per-matrix partial cap).
 constexpr int64_t kElemsPerBlock = 16384;
 
+// GEMM tail balancing (GemmArgs::sched): fraction of every XCD list claimed
+// at run time, and blocks launched per claimed position (the surplus lets an
+// XCD that runs faster take positions of the others; extra blocks find no
+// position left and exit). Used for launches of at least two rounds of
+// tiles on kCUs compute units: in A/B runs of the 84 x 2048x6144 launches
+// this took 0.7-1.2 % off the Gram, polynomial and apply.
+constexpr double kTailFrac = 0.08, kTailBlocks = 1.5;
+constexpr int64_t kCUs = 256;
+
 }  // namespace
 
 struct muonh_plan {
@@ -89,7 +98,7 @@ struct muonh_plan {
   NsPrec prec = kBf16;
   StateFmt sf;  // storage of G and M
   int esize = 2;  // workspace bytes per logical Newton-Schulz element
-  int64_t off_partials = 0, off_norm_m = 0, off_norm_w = 0;
+  int64_t off_partials = 0, off_norm_m = 0, off_norm_w = 0, off_sched = 0;
   size_t ws_bytes = 0;
 };
 
@@ -294,9 +303,23 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
           const int64_t tot = (int64_t)a.g[gi].count * a.g[gi].tiles_per_mat;
           len += ((x + 1) * tot >> 3) - (x * tot >> 3);
         }
+        a.xlen[x] = (int)len;
         longest = std::max(longest, len);
       }
       a.grid = (int)(8 * longest);
+      // bf16 launches of two or more rounds of tiles: the last kTailFrac of
+      // every list is claimed at run time by kTailBlocks times as many
+      // blocks (the step sets the counters; see GemmArgs::sched)
+      if (p->prec == kBf16 && tiles >= 2 * kCUs) {
+        int64_t slots = 0;
+        for (int x = 0; x < 8; ++x) {
+          const int tail = (int)std::ceil(a.xlen[x] * kTailFrac);
+          a.xstatic[x] = a.xlen[x] - tail;
+          slots = std::max<int64_t>(slots, a.xstatic[x] + (int64_t)std::ceil(tail * kTailBlocks));
+        }
+        a.grid = (int)(8 * slots);
+        a.sched = reinterpret_cast<int*>(ws + p->off_sched);  // set per launch by the step
+      }
     } else {
       a.grid = a.ntiles;
     }
@@ -390,6 +413,8 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   off = round_up(off + n_mats * (int64_t)sizeof(double), 256);
   p->off_norm_w = off;
   off = round_up(off + n_mats * (int64_t)sizeof(double), 256);
+  p->off_sched = off;  // two sets of 8 tail counters (see GemmArgs::sched)
+  off = round_up(off + 16 * (int64_t)sizeof(int), 256);
 
   int first = 0;
   int64_t params = 0;
@@ -534,17 +559,30 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
   }
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
 
+  // Tail counters: both sets zeroed here; each balanced launch uses one set
+  // and zeroes the other for the next.
+  int* sched = reinterpret_cast<int*>(ws + plan->off_sched);
+  int parity = 0;
+  if (ns_iters >= 1 && plan->prec == kBf16 && (e = launch_zero_i32(sched, 16, s)) != hipSuccess)
+    return hip_fail(e, "tail counters");
+  auto gemm = [&](GemmMode mode, GemmArgs a) -> hipError_t {
+    if (a.sched) {
+      a.sched = sched + 8 * parity;
+      a.sched_clear = sched + 8 * (1 - parity);
+      parity ^= 1;
+    }
+    return launch_gemm(mode, plan->prec, a, s);
+  };
   for (int it = 0; it < ns_iters; ++it) {
     const double* xnorm = (fused && it == 0) ? norm_m : nullptr;
     for (const GemmArgs& a : make_gemm(plan, ws, kGram, it, ns_iters, xnorm))
-      if ((e = launch_gemm(kGram, plan->prec, a, s)) != hipSuccess) return hip_fail(e, "ns gram");
+      if ((e = gemm(kGram, a)) != hipSuccess) return hip_fail(e, "ns gram");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
     for (const GemmArgs& a : make_gemm(plan, ws, kPoly, it, ns_iters))
-      if ((e = launch_gemm(kPoly, plan->prec, a, s)) != hipSuccess) return hip_fail(e, "ns poly");
+      if ((e = gemm(kPoly, a)) != hipSuccess) return hip_fail(e, "ns poly");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
     for (const GemmArgs& a : make_gemm(plan, ws, kApply, it, ns_iters, xnorm))
-      if ((e = launch_gemm(kApply, plan->prec, a, s)) != hipSuccess)
-        return hip_fail(e, "ns apply");
+      if ((e = gemm(kApply, a)) != hipSuccess) return hip_fail(e, "ns apply");
     if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
   }
 

@@ -154,6 +154,15 @@ struct GemmArgs {
   // First iteration after the fused momentum + cast: per-matrix ||M||; the
   // output is scaled by x0_sigma (Gram: squared). nullptr: no scaling.
   const double* xnorm;
+  // Tail balancing (bf16 kernel with xcd_map; sched == nullptr: off). XCD x
+  // has xlen[x] positions in its list; blocks of slot (blockIdx / 8) below
+  // xstatic[x] take their own position, the others claim tail positions
+  // [xstatic, xlen) of any list through the counters sched[0..7], which are
+  // zero when the launch starts; block b < 8 zeroes sched_clear[b], the
+  // counters of the next launch on the stream.
+  int* sched;
+  int* sched_clear;
+  int xlen[8], xstatic[8];
 };
 
 // Sets the calling thread's muonh_last_error() message; returns `code`.
@@ -162,5 +171,7 @@ int set_error(int code, const char* msg);
 // Tile edge (square tiles) used by the launchers for the given precision.
 int gemm_tile(NsPrec prec);
 hipError_t launch_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a, hipStream_t s);
+// Zeroes n ints at p (a kernel, so that the call may sit in a captured graph).
+hipError_t launch_zero_i32(int* p, int n, hipStream_t s);
 
 }  // namespace muonh

@@ -1058,7 +1058,47 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / 4, wn = wave - (wave / 4) * 4;
   int gi, local;
-  if (!map_tile(args, blockIdx.x, gi, local)) return;
+  int vb = blockIdx.x;  // position 8 * slot + XCD in the XCD lists
+  if (args.sched) {
+    // Tail balancing: XCDs run at different clocks under this load (their
+    // last blocks finished up to 7 % apart with a fixed deal), so the last
+    // positions of every list are claimed at run time, own list first.
+    if (blockIdx.x < 8 && tid == 0) args.sched_clear[blockIdx.x] = 0;
+    const int x = blockIdx.x & 7;
+    if ((int)(blockIdx.x >> 3) >= args.xstatic[x]) {
+      __shared__ int pick;
+      if (tid < 64) {
+        // lanes 0-7 look at lists x .. x+7; a failed claim marks its list
+        // exhausted (the counter only grows), so at most 8 rounds fail and a
+        // block gives up only when every tail position has been taken
+        const int k8 = tid & 7, y = (x + k8) & 7;
+        const int tail = args.xlen[y] - args.xstatic[y];
+        uint32_t failed = 0;
+        int p = -1;
+        for (int round = 0; round < 9 && p < 0; ++round) {
+          bool avail = false;
+          if (tid < 8 && !((failed >> k8) & 1u))
+            avail = __hip_atomic_load(args.sched + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tail;
+          const uint64_t m = __ballot(avail);
+          if (m == 0) break;
+          const int k = __builtin_ctzll(m);
+          int got = -1;
+          if (tid == 0) {
+            const int yy = (x + k) & 7;
+            const int at = atomicAdd(args.sched + yy, 1);
+            if (at < args.xlen[yy] - args.xstatic[yy]) got = 8 * (args.xstatic[yy] + at) + yy;
+          }
+          p = __shfl(got, 0);
+          failed |= 1u << k;
+        }
+        if (tid == 0) pick = p;
+      }
+      __syncthreads();
+      vb = pick;
+      if (vb < 0) return;
+    }
+  }
+  if (!map_tile(args, vb, gi, local)) return;
   const GemmGroup& g = args.g[gi];
   const int mat = local / g.tiles_per_mat;
   int bi, bj;
@@ -1185,7 +1225,16 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s, bool split) {
 
 }  // namespace
 
+__global__ void k_zero_i32(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 int gemm_tile(NsPrec prec) { return prec == kFp32 ? kTile32 : bf::kBM; }
+
+hipError_t launch_zero_i32(int* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a, hipStream_t s) {
   if (a.ntiles <= 0) return hipSuccess;
