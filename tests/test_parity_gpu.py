@@ -337,6 +337,35 @@ def test_bitwise_determinism_and_batch_invariance(prec):
     assert torch.equal(w_c[0], w_a[2]) and torch.equal(o_c[0], o_a[2])
 
 
+def test_tail_balanced_launches_compute_every_tile():
+    # 192 small matrices: every GEMM launch has two or more rounds of tiles,
+    # so the last positions of each XCD's tile list are claimed at run time.
+    # Each matrix must come out bit for bit as it does alone (a launch of a
+    # few tiles, fixed deal), over two steps (both counter sets in use).
+    need_gpu()
+    shapes = [(512, 512)] * 96 + [(768, 512)] * 96
+    dev = torch.device("cuda")
+    W_init = [torch.from_numpy(workloads.host_custom(s, 0.02, (68, i))) for i, s in enumerate(shapes)]
+    G_host = [torch.from_numpy(workloads.host_custom(s, 0.01, (69, i))) for i, s in enumerate(shapes)]
+
+    def run(sel):
+        opt = make_opt([shapes[i] for i in sel], "bf16")
+        W = [W_init[i].to(dev) for i in sel]
+        M = [torch.zeros(shapes[i], device=dev) for i in sel]
+        G = [G_host[i].to(dev) for i in sel]
+        opt.init(W)
+        for _ in range(2):
+            opt.step(W, G, M, 0.02, 0.95, 5)
+        torch.cuda.synchronize()
+        return [w.cpu() for w in W], [opt.read_update(j).cpu() for j in range(len(sel))]
+
+    w_all, o_all = run(list(range(len(shapes))))
+    say("[tail balance] batch done")
+    for i in range(len(shapes)):
+        w_1, o_1 = run([i])
+        assert torch.equal(w_1[0], w_all[i]) and torch.equal(o_1[0], o_all[i]), f"matrix {i}"
+
+
 # the tall matrix runs on the transposed layout: equal up to summation order
 TOL_TALL = {"fp32": (1e-6, 1e-6), "split_bf16": (1e-4, 1e-5), "bf16": (1e-2, 1e-3)}
 
