@@ -960,6 +960,16 @@ __device__ __forceinline__ u32x4 pair_halves(uint32_t x0, uint32_t x1, uint32_t 
   return hi ? u32x4{b0, b1, y0, y1} : u32x4{x0, x1, a0, a1};
 }
 
+// Chunk permutation of the transposed-output staging (row r: 512 bytes, 32
+// chunks of 16 bytes; chunk k stored at k ^ ot_swz(r)). The writes of one
+// 16-lane pass cover 16 consecutive rows with one chunk each, the reads 4
+// consecutive rows with 4 chunks each: rotating the low 4 bits of r keeps
+// both on 16 distinct 16-byte slots (r & 31 left the reads 4-way
+// conflicted).
+__device__ __forceinline__ int ot_swz(int r) {
+  return (r & 16) | ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
 // Main loop: as pingpong (same phases, barriers and refills), with one
 // 32-k fragment set per stage. The E term: accumulator rows 16 mi .. +15 lie
 // in one stage, read as 4 consecutive k of the lane's column (transposed
@@ -1186,7 +1196,7 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
       for (int ni = 0; ni < kNT; ++ni) {
         const int col = wn0 + 16 * ni + (lane & 15);
         const int row0 = wm0 + 16 * mi + 4 * (lane >> 4);
-        const int off = ((((row0 >> 3) ^ (col & 31)) << 4) | ((row0 & 7) << 1));
+        const int off = ((((row0 >> 3) ^ ot_swz(col & 31)) << 4) | ((row0 & 7) << 1));
         *reinterpret_cast<bf16x4*>(srow(col) + off) = vh[mi][ni];
       }
     __syncthreads();
@@ -1196,7 +1206,7 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
       const int id = tid + i * 512;
       const int row = (id & 1023) >> 2;
       const int c = ((id >> 10) << 2) | (id & 3);
-      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ (row & 31)) << 4));
+      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ ot_swz(row & 31)) << 4));
       *reinterpret_cast<u32x4*>(region + (int64_t)id * 16) = d;
     }
   }
