@@ -974,7 +974,9 @@ __device__ __forceinline__ int ot_swz(int r) {
 // 32-k fragment set per stage. The E term: accumulator rows 16 mi .. +15 lie
 // in one stage, read as 4 consecutive k of the lane's column (transposed
 // read for the apply, a plain 8-byte read of A's row for the polynomial).
-template <int G, bool E_TERM, bool QT>
+// NT: 16-column blocks the wave computes (kNT, or 2 for the second group on
+// a diagonal tile of the symmetric modes).
+template <int G, bool E_TERM, bool QT, int NT = kNT>
 __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc, int nk,
                                            const char* ring, uint32_t ring_lds, int wave, int wm0,
                                            int wn0, const Offs& o, int lane, int bi, float seed,
@@ -990,7 +992,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
     for (int mi = 0; mi < kMT; ++mi) {
       if (16 * mi < r || 16 * mi >= r + 32) continue;
 #pragma unroll
-      for (int ni = 0; ni < kNT; ++ni) {
+      for (int ni = 0; ni < NT; ++ni) {
         const int n0 = wn0 + 16 * ni;
         bf16x4 hv;
         if (QT) {
@@ -1012,7 +1014,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
     for (int mi = 0; mi < kMT; ++mi)
       f.a[mi] = *reinterpret_cast<const bf16x8*>(buf + (wm0 + 16 * mi) * kPRow + o.f);
 #pragma unroll
-    for (int ni = 0; ni < kNT; ++ni) {
+    for (int ni = 0; ni < NT; ++ni) {
       const int n0 = wn0 + 16 * ni;
       if (QT) {
         const char* p = buf + kPanel + (n0 >> 5) * 2048 + o.q + ((((n0 & 31) << 1) ^ (32 * (g & 1))));
@@ -1027,7 +1029,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < kNT; ++ni)
+      for (int ni = 0; ni < NT; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
   };
   auto refill = [&](int kt) {
@@ -1141,10 +1143,19 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   }
   phase_barrier<12>();
   const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
+  // Diagonal tile of a symmetric product: its lower-left quadrant is the
+  // transpose of the upper-right one, so the second group computes only the
+  // lower-right quadrant (a 128 x 32 strip per wave, half the MFMAs) and the
+  // epilogue mirrors the upper-right quadrant (first group, waves 2 and 3).
+  const bool diag = kSym && bi == bj;
+  const bool half = diag && wave >= 4;
+  const int wnc = half ? 128 + 32 * (wave - 4) : wn0;  // first column of the wave's strip
   if (wave < 4)
     pingpong16<0, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
-  else
+  else if (!half)
     pingpong16<1, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
+  else
+    pingpong16<1, MODE != kGram, kQT, 2>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wnc, o, lane, bi, seed, acc);
 
   float scale = MODE == kPoly ? args.c1 : 1.f;
   if (MODE != kPoly && args.xnorm) {
@@ -1178,6 +1189,7 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
     for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
       for (int p = 0; p < kNT / 2; ++p) {
+        if (half && p > 0) break;
         const u32x2 x = __builtin_bit_cast(u32x2, vh[mi][2 * p]);
         const u32x2 y = __builtin_bit_cast(u32x2, vh[mi][2 * p + 1]);
         uint32_t x0 = x.x, x1 = x.y, y0 = y.x, y1 = y.y;
@@ -1185,11 +1197,39 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
         quad_transpose(y0, y1, lane);
         const u32x4 d = pair_halves(x0, x1, y0, y1, lane);
         const int row = wm0 + 16 * mi + 4 * (lane >> 4) + (lane & 3);
-        *reinterpret_cast<u32x4*>(region + (int64_t)((wn0 + 32 * p) >> 5) * kPanel + row * kPRow + (chunk << 4)) = d;
+        *reinterpret_cast<u32x4*>(region + (int64_t)((wnc + 32 * p) >> 5) * kPanel + row * kPRow + (chunk << 4)) = d;
       }
   }
+  if (diag && O1) {
+    // lower-left quadrant (rows 128-255, columns 0-127) = transpose of the
+    // upper-right one: staging row i holds column 128 + i of the tile's rows
+    // 0-127, i.e. row 128 + i of the quadrant (the main loop's last barrier
+    // retired every fragment read, so the ring is free)
+    if (wave == 2 || wave == 3) {
+#pragma unroll
+      for (int mi = 0; mi < kMT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < kNT; ++ni) {
+          const int r = wn0 + 16 * ni + (lane & 15) - 128;
+          const int row0 = 16 * mi + 4 * (lane >> 4);
+          const int off = ((((row0 >> 3) ^ ot_swz(r & 31)) << 4) | ((row0 & 7) << 1));
+          *reinterpret_cast<bf16x4*>(srow(r) + off) = vh[mi][ni];
+        }
+    }
+    phase_barrier<>();
+    char* region = O1 + (int64_t)bi * kBM * g.ldo1 * 2 + (int64_t)bj * 8 * kPanel;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + i * 512;
+      const int row = id >> 4, c = id & 15;  // quadrant row, 16-byte chunk (8 columns)
+      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ ot_swz(row & 31)) << 4));
+      *reinterpret_cast<u32x4*>(region + (int64_t)(c >> 2) * kPanel + (128 + row) * kPRow + ((c & 3) << 4)) = d;
+    }
+  }
   if (OT) {
-    __syncthreads();
+    // staging only: the ring is free after the main loop's last barrier, and a
+    // barrier without a vmcnt wait lets the row-major stores above drain
+    phase_barrier<>();
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
@@ -1199,7 +1239,7 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
         const int off = ((((row0 >> 3) ^ ot_swz(col & 31)) << 4) | ((row0 & 7) << 1));
         *reinterpret_cast<bf16x4*>(srow(col) + off) = vh[mi][ni];
       }
-    __syncthreads();
+    phase_barrier<>();
     char* region = OT + (int64_t)bj * kBM * ldT * 2 + (int64_t)bi * 8 * kPanel;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
