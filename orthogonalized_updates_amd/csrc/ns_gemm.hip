@@ -21,6 +21,9 @@
 // a*X or b*A term is folded into the accumulators from the operand stream.
 // Row-major outputs are stored straight from registers, transposed ones
 // (mirrored tiles, O of tall matrices) staged through the idle ring.
+// In the bf16 kernel, diagonal tiles of the symmetric products compute three
+// quadrants and mirror the fourth, and the last positions of every XCD's
+// tile list are claimed at run time (tail balancing, see GemmArgs::sched).
 // fp32 debug: a simpler 128x128 kernel on v_mfma_f32_32x32x2f32 with
 // register-staged double buffering and direct epilogue stores; it reads both
 // operands along K, so that mode keeps X and X^T copies.
@@ -916,7 +919,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 // throughput than 32x32x16 at the same occupancy (register-only loop: 2.0
 // against 1.72 PFLOP/s; on all-zero data both reach ~2.47), and its results
 // are bit for bit those of the 32x32x16 kernel (every launch of the Gram,
-// polynomial and apply compared). Lane layouts: A and B fragments, lane l
+// polynomial and apply compared; the polynomial's mirrored quadrants of
+// diagonal tiles assume a symmetric A, which the Gram's mirror guarantees). Lane layouts: A and B fragments, lane l
 // holds row (column) l%16, k = 8(l/16) .. +7; accumulators, lane l holds
 // rows 4(l/16) .. +3 of column l%16. Two differences from that kernel's ring:
 // panels are swizzled with SH = 1 (see swz), and in the apply group 1
