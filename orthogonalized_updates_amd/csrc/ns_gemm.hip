@@ -509,11 +509,13 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& args, int b, int& gi, i
 }
 
 // Tile coordinates of local tile t of a matrix. Symmetric modes walk the
-// upper triangle row by row; the apply groups rows in bands of 4 tile rows
-// (4 x 8 = 32 consecutive tiles share 4 B row-blocks and 8 X^T row-blocks).
-// Bands of 8 ran the 2048 x 6144 apply 0.6 % faster in isolation but read
-// 23 % more from HBM in the full step (10.1 against 8.2 GB per launch) at
-// the same speed there.
+// upper triangle row by row; the apply groups rows in bands of 8 tile rows
+// (8 x 4 = 32 consecutive tiles share 8 B row-blocks and 4 column blocks of
+// X; for s = 2048 a band is a whole column of tiles, so each column block of
+// X streams through the L2 once). With the conflict-free fragment reads this
+// ran the apply 0.9 % faster in the 2B step than bands of 4 (1.6 % on the 84
+// x 2048x6144 launches) for 2 % more HBM reads; before that change bands of 8
+// were no faster and read 23 % more.
 template <bool kSym>
 __device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, int& bj) {
   if (kSym) {
@@ -526,7 +528,7 @@ __device__ __forceinline__ void tile_coords(const GemmGroup& g, int t, int& bi, 
     }
     bj = bi + t;
   } else {
-    constexpr int kBand = 4;
+    constexpr int kBand = 8;
     const int gsz = kBand * g.tn;
     const int band = t / gsz;
     const int first = band * kBand;
