@@ -43,13 +43,16 @@
  *     norm partials. After a step it holds that step's update O until the
  *     next call that uses it.
  *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
- *     NULL is the default stream). No call synchronises the device.
+ *     NULL is the default stream). No call synchronises the device, except
+ *     muonh_step_status, which waits for `stream`.
  *   - Calls that share a workspace must be ordered by the caller (same stream,
  *     or events). A plan itself is read-only after creation and may be shared.
  *   - All argument checks run before any work is enqueued; a call that returns
  *     an error has enqueued nothing. Negative return values are errors;
  *     muonh_last_error() gives a message for the calling thread.
- *   - Non-finite inputs are not errors: they propagate into the results.
+ *   - Non-finite inputs are not errors: they propagate into the results. A
+ *     step records in the workspace whether a norm it took was not finite
+ *     (muonh_step_status reads that record).
  */
 #ifndef MUONH_H
 #define MUONH_H
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MUONH_ABI_VERSION 2
+#define MUONH_ABI_VERSION 3
 
 typedef struct muonh_plan muonh_plan;
 
@@ -241,6 +244,30 @@ int muonh_adamw_step(int32_t n_tensors, const int64_t* sizes, float* const* P,
  */
 int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Non-finite report of the last muonh_step or muonh_step_muon_wd that used
+ * this workspace: each step clears the record when it starts and then sets
+ *   MUONH_NONFINITE_MOMENTUM  when ||M|| (after the momentum update) of any
+ *                             matrix is NaN or infinite: its X0, O and W are
+ *                             then not finite either;
+ *   MUONH_NONFINITE_UPDATE    (muonh_step only) when ||W - lr*O|| of any
+ *                             matrix is NaN or infinite, so the projected W
+ *                             is not finite.
+ * (the two norms the step divides by, formula at the top of this file). The
+ * kernels that finalize the norms write the record; it never changes the
+ * results. *flags (HOST) receives the bits.
+ * This call copies 4 bytes to the host and waits for `stream` (the only
+ * synchronising call of the library); order it after the step like any
+ * other call on the workspace.
+ * Errors: MUONH_EINVAL (NULL plan or flags), MUONH_EWORKSPACE, MUONH_EHIP.
+ */
+enum {
+  MUONH_NONFINITE_MOMENTUM = 1,
+  MUONH_NONFINITE_UPDATE = 2,
+};
+int muonh_step_status(const muonh_plan* plan, const void* workspace, size_t workspace_bytes,
+                      void* stream, uint32_t* flags);
 
 /* Static description of a status code. */
 const char* muonh_status_string(int status);

@@ -38,6 +38,8 @@ MUONH_NS_FP32 = 1
 MUONH_NS_SPLIT_BF16 = 2
 MUONH_GRAD_BF16 = 4
 MUONH_MOM_BF16 = 8
+MUONH_NONFINITE_MOMENTUM = 1
+MUONH_NONFINITE_UPDATE = 2
 
 # Newton-Schulz operand precision -> plan flag
 PRECISIONS = {"bf16": 0, "split_bf16": MUONH_NS_SPLIT_BF16, "fp32": MUONH_NS_FP32}
@@ -86,6 +88,7 @@ def _load_library() -> ctypes.CDLL:
         "muonh_read_update": (ctypes.c_int, [vp, i64, vp, vp, sz, vp]),
         "muonh_adamw_step": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
                                             i32, vp]),
+        "muonh_step_status": (ctypes.c_int, [vp, vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]),
         "muonh_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "muonh_last_error": (ctypes.c_char_p, []),
     }
@@ -317,11 +320,21 @@ class MuonH:
                                     self._stream()))
         return out
 
+    def status(self) -> int:
+        """Non-finite bits of the last step (MUONH_NONFINITE_MOMENTUM: a
+        momentum norm was NaN or infinite; MUONH_NONFINITE_UPDATE: a trial
+        update norm was). Waits for the current stream."""
+        flags = ctypes.c_uint32(0)
+        check(get_lib().muonh_step_status(self.plan.handle, self.workspace.data_ptr(),
+                                          self.workspace.numel(), self._stream(),
+                                          ctypes.byref(flags)))
+        return int(flags.value)
+
 
 __all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
            "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
            "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32", "MUONH_NS_SPLIT_BF16", "MUONH_GRAD_BF16",
-           "MUONH_MOM_BF16", "AdamW"]
+           "MUONH_MOM_BF16", "MUONH_NONFINITE_MOMENTUM", "MUONH_NONFINITE_UPDATE", "AdamW"]
 
 
 class AdamW:

@@ -222,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const void* con
 // matrices may run concurrently and own the rest of the arrays.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_finalize(EwArgs a, const double* partials,
-                                                       double* norms, float* R) {
+                                                       double* norms, float* R, uint32_t* flags,
+                                                       uint32_t bit) {
   int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   int gi = 0;
   while (gi < a.ngroups && t >= a.g[gi].count) t -= a.g[gi++].count;
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(EwArgs a, const double* p
   const double nrm = sqrt(s);
   norms[mat] = nrm;
   if (R) R[mat] = (float)nrm;
+  if (flags && !isfinite(nrm)) atomicOr(flags, bit);
 }
 
 // --------------------------------------------------------------------------
@@ -596,11 +598,12 @@ hipError_t launch_momentum(const EwArgs& a, StateFmt sf, const void* const* G, v
 }
 
 hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norms, float* R,
-                           hipStream_t s) {
+                           hipStream_t s, uint32_t* flags, uint32_t bit) {
   int64_t n = 0;
   for (int i = 0; i < a.ngroups; ++i) n += a.g[i].count;
   const int blocks = (int)((n + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(k_finalize, dim3(blocks), dim3(kThreads), 0, s, a, partials, norms, R);
+  hipLaunchKernelGGL(k_finalize, dim3(blocks), dim3(kThreads), 0, s, a, partials, norms, R, flags,
+                     bit);
   return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ constexpr int64_t kElemsPerBlock = 16384;
 // this took 0.7-1.2 % off the Gram, polynomial and apply.
 constexpr double kTailFrac = 0.08, kTailBlocks = 1.5;
 constexpr int64_t kCUs = 256;
+// Index of the non-finite status word after the 16 tail counters.
+constexpr int kStatusWord = 16;
 
 }  // namespace
 
@@ -344,6 +346,23 @@ extern "C" {
 
 int32_t muonh_abi_version(void) { return MUONH_ABI_VERSION; }
 
+int muonh_step_status(const muonh_plan* plan, const void* workspace, size_t workspace_bytes,
+                      void* stream, uint32_t* flags) {
+  if (!plan || !flags) return fail(MUONH_EINVAL, "plan and flags must not be NULL");
+  int err = 0;
+  if (!check_ws(plan, workspace, workspace_bytes, &err)) return err;
+  const uint32_t* src =
+      reinterpret_cast<const uint32_t*>(static_cast<const char*>(workspace) + plan->off_sched) +
+      kStatusWord;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, src, sizeof v, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "step status");
+  *flags = v;
+  return MUONH_OK;
+}
+
 const char* muonh_status_string(int status) {
   switch (status) {
     case MUONH_OK: return "ok";
@@ -413,8 +432,8 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   off = round_up(off + n_mats * (int64_t)sizeof(double), 256);
   p->off_norm_w = off;
   off = round_up(off + n_mats * (int64_t)sizeof(double), 256);
-  p->off_sched = off;  // two sets of 8 tail counters (see GemmArgs::sched)
-  off = round_up(off + 16 * (int64_t)sizeof(int), 256);
+  p->off_sched = off;  // two sets of 8 tail counters (GemmArgs::sched), then the status word
+  off = round_up(off + (kStatusWord + 1) * (int64_t)sizeof(int), 256);
 
   int first = 0;
   int64_t params = 0;
@@ -529,6 +548,13 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
     if (!events) return hipSuccess;
     return hipEventRecord(reinterpret_cast<hipEvent_t>(events[ev++]), s);
   };
+  // Tail counters (two sets of 8) and the non-finite flags, cleared by a
+  // kernel (no memset, so the step can be captured in a graph); each
+  // balanced GEMM launch uses one counter set and zeroes the other for the
+  // next; the norm finalizes set the non-finite bits in the flags.
+  int* sched = reinterpret_cast<int*>(ws + plan->off_sched);
+  uint32_t* nf_flags = reinterpret_cast<uint32_t*>(sched + kStatusWord);
+  if ((e = launch_zero_i32(sched, kStatusWord + 1, s)) != hipSuccess) return hip_fail(e, "step status");
 
   const std::vector<EwArgs> stream_args = make_ew(plan, ws, kEwStream, -1);
   // bf16 and split operands with at least one iteration: momentum and the
@@ -541,7 +567,8 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
     for (const EwArgs& a : make_ew(plan, ws, kEwFused, ns_iters)) {
       if ((e = launch_momentum_cast(a, plan->prec, plan->sf, G, M, beta, partials, s)) != hipSuccess)
         return hip_fail(e, "momentum + cast");
-      if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
+      if ((e = launch_finalize(a, partials, norm_m, nullptr, s, nf_flags, MUONH_NONFINITE_MOMENTUM)) !=
+          hipSuccess)
         return hip_fail(e, "momentum finalize");
       if ((e = launch_cast_fallback(a, plan->prec, plan->sf, M, norm_m, s)) != hipSuccess)
         return hip_fail(e, "cast fallback");
@@ -550,7 +577,8 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
     for (const EwArgs& a : stream_args) {
       if ((e = launch_momentum(a, plan->sf, G, M, beta, partials, s)) != hipSuccess)
         return hip_fail(e, "momentum");
-      if ((e = launch_finalize(a, partials, norm_m, nullptr, s)) != hipSuccess)
+      if ((e = launch_finalize(a, partials, norm_m, nullptr, s, nf_flags, MUONH_NONFINITE_MOMENTUM)) !=
+          hipSuccess)
         return hip_fail(e, "momentum finalize");
     }
     for (const EwArgs& a : make_ew(plan, ws, kEwTile, ns_iters))
@@ -559,12 +587,7 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
   }
   if ((e = mark()) != hipSuccess) return hip_fail(e, "event record");
 
-  // Tail counters: both sets zeroed here; each balanced launch uses one set
-  // and zeroes the other for the next.
-  int* sched = reinterpret_cast<int*>(ws + plan->off_sched);
   int parity = 0;
-  if (ns_iters >= 1 && plan->prec == kBf16 && (e = launch_zero_i32(sched, 16, s)) != hipSuccess)
-    return hip_fail(e, "tail counters");
   auto gemm = [&](GemmMode mode, GemmArgs a) -> hipError_t {
     if (a.sched) {
       a.sched = sched + 8 * parity;
@@ -595,7 +618,8 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
     for (const EwArgs& a : stream_args) {
       if ((e = launch_update_norm(a, plan->prec, W, lr, partials, s)) != hipSuccess)
         return hip_fail(e, "update norm");
-      if ((e = launch_finalize(a, partials, norm_w, nullptr, s)) != hipSuccess)
+      if ((e = launch_finalize(a, partials, norm_w, nullptr, s, nf_flags, MUONH_NONFINITE_UPDATE)) !=
+          hipSuccess)
         return hip_fail(e, "update finalize");
       if ((e = launch_project(a, plan->prec, W, R, norm_w, lr, s)) != hipSuccess)
         return hip_fail(e, "project");

@@ -93,9 +93,10 @@ hipError_t launch_sumsq(const EwArgs& a, float* const* W, double* partials, hipS
 hipError_t launch_momentum(const EwArgs& a, StateFmt sf, const void* const* G, void* const* M,
                            float beta, double* partials, hipStream_t s);
 // norms[mat] = sqrt(sum of partials) for the matrices of the batch `a`;
-// if R != nullptr also R[mat] = (float)norms[mat].
+// if R != nullptr also R[mat] = (float)norms[mat]; if flags != nullptr, `bit`
+// is or-ed into *flags when a norm is not finite.
 hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norms, float* R,
-                           hipStream_t s);
+                           hipStream_t s, uint32_t* flags = nullptr, uint32_t bit = 0);
 // X0 = M / (norm + eps) written to D (same orientation) and E (transposed).
 hipError_t launch_normcast(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* M,
                            const double* norms, hipStream_t s);

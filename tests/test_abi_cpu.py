@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("muonh_plan_create", "muonh_plan_destroy", "muonh_workspace_bytes", "muonh_init",
               "muonh_step", "muonh_step_timed", "muonh_step_muon_wd", "muonh_step_muon_wd_timed",
-              "muonh_read_update", "muonh_last_error", "muonh_status_string"):
+              "muonh_read_update", "muonh_step_status", "muonh_last_error",
+              "muonh_status_string"):
         assert n in names
 
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert mh.lib.muonh_abi_version() == 2
+    assert mh.lib.muonh_abi_version() == 3
 
 
 def _create(groups, flags=0):
@@ -244,3 +245,15 @@ def test_adamw_rejects_bad_arguments(kw, code):
 def test_adamw_zero_tensors_is_a_no_op():
     assert mh.lib.muonh_adamw_step(0, None, None, None, None, None, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1,
                                    None) == mh.MUONH_OK
+
+
+def test_step_status_rejects_before_any_device_work():
+    # NULL flags, NULL plan and a workspace that is too small: all host checks
+    p = mh.Plan([(256, 256, 1)])
+    flags = ctypes.c_uint32(7)
+    assert mh.lib.muonh_step_status(p.handle, None, 0, None, None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step_status(None, None, 0, None, ctypes.byref(flags)) == mh.MUONH_EINVAL
+    st = mh.lib.muonh_step_status(p.handle, ctypes.c_void_p(256), 16, None, ctypes.byref(flags))
+    assert st == mh.MUONH_EWORKSPACE
+    assert flags.value == 7  # untouched on error
+    assert mh.lib.muonh_last_error().decode()
