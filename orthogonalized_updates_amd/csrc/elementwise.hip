@@ -17,7 +17,7 @@
 namespace muonh {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kEwThreads;
 
 __device__ __forceinline__ int group_of_block(const EwArgs& a, int b) {
   int gi = 0;
@@ -55,24 +55,42 @@ __device__ __forceinline__ bool aligned16(const void* p) {
 // once: M in the momentum pass (read-modify-write) and W in the updates. On
 // MI355X such streams ran 7-9 % faster with the hint in isolation. Not used
 // for write-only outputs, nor where a line is shared by two reads.
+// The pointers are cast to the global address space: on a generic pointer
+// the hint compiles to flat accesses, which also count against the LDS
+// counter and so make every wait a full one.
 typedef float nt_f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int nt_u2 __attribute__((ext_vector_type(2)));
+#define MUONH_GLOBAL __attribute__((address_space(1)))
 
 __device__ __forceinline__ float4 ld_nt(const float* q) {
-  const nt_f4 x = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(q));
+  const nt_f4 x = __builtin_nontemporal_load((const MUONH_GLOBAL nt_f4*)q);
   return make_float4(x.x, x.y, x.z, x.w);
 }
 __device__ __forceinline__ void st_nt(float* q, const float4& v) {
   const nt_f4 x = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(x, reinterpret_cast<nt_f4*>(q));
+  __builtin_nontemporal_store(x, (MUONH_GLOBAL nt_f4*)q);
+}
+// Plain 16- and 8-byte global accesses (through the builtin vector types,
+// which take an address space where HIP's vector classes do not).
+__device__ __forceinline__ float4 ld_g4(const void* q) {
+  const nt_f4 x = *(const MUONH_GLOBAL nt_f4*)q;
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 ld_g2(const void* q) {
+  const nt_u2 x = *(const MUONH_GLOBAL nt_u2*)q;
+  return make_uint2(x.x, x.y);
+}
+__device__ __forceinline__ void st_g4(void* q, const float4& v) {
+  const nt_f4 x = {v.x, v.y, v.z, v.w};
+  *(MUONH_GLOBAL nt_f4*)q = x;
 }
 __device__ __forceinline__ uint2 ld_nt(const uint2* q) {
-  const nt_u2 x = __builtin_nontemporal_load(reinterpret_cast<const nt_u2*>(q));
+  const nt_u2 x = __builtin_nontemporal_load((const MUONH_GLOBAL nt_u2*)q);
   return make_uint2(x.x, x.y);
 }
 __device__ __forceinline__ void st_nt(uint2* q, uint2 v) {
   const nt_u2 x = {v.x, v.y};
-  __builtin_nontemporal_store(x, reinterpret_cast<nt_u2*>(q));
+  __builtin_nontemporal_store(x, (MUONH_GLOBAL nt_u2*)q);
 }
 
 // 4 bf16 values (the low half of each pair first, as in memory) widened.
@@ -91,12 +109,14 @@ struct St;
 template <>
 struct St<false> {
   static constexpr unsigned kVecAlign = 16;
-  __device__ static float load(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  __device__ static float load(const void* p, int64_t i) {
+    return ((const MUONH_GLOBAL float*)p)[i];
+  }
   __device__ static float4 load4(const void* p, int64_t i) {
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    return ld_g4(static_cast<const float*>(p) + i);
   }
   __device__ static float store(void* p, int64_t i, float v) {
-    static_cast<float*>(p)[i] = v;
+    ((MUONH_GLOBAL float*)p)[i] = v;
     return v;
   }
   __device__ static float4 load4_nt(const void* p, int64_t i) {
@@ -111,10 +131,10 @@ template <>
 struct St<true> {
   static constexpr unsigned kVecAlign = 8;
   __device__ static float load(const void* p, int64_t i) {
-    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[i] << 16);
+    return __uint_as_float((uint32_t)((const MUONH_GLOBAL uint16_t*)p)[i] << 16);
   }
   __device__ static float4 load4(const void* p, int64_t i) {
-    return widen4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i));
+    return widen4(ld_g2(static_cast<const uint16_t*>(p) + i));
   }
   __device__ static float4 load4_nt(const void* p, int64_t i) {
     return widen4(ld_nt(reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i)));
@@ -127,7 +147,7 @@ struct St<true> {
   }
   __device__ static float store(void* p, int64_t i, float v) {
     const __bf16 h = (__bf16)v;
-    static_cast<__bf16*>(p)[i] = h;
+    ((MUONH_GLOBAL __bf16*)p)[i] = h;
     return (float)h;
   }
 };
@@ -256,16 +276,16 @@ struct Fmt<kBf16> {
     return ((((r >> 8) * (ld >> 5)) + (c >> 5)) << 14) + ((r & 255) << 6) + ((c & 31) << 1);
   }
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
-    return (float)*reinterpret_cast<const __bf16*>(base + off(r, c, ld));
+    return (float)*(const MUONH_GLOBAL __bf16*)(base + off(r, c, ld));
   }
   // 4 consecutive elements of a row, c a multiple of 4 (one 8-byte load).
   __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
-    return widen4(*reinterpret_cast<const uint2*>(base + off(r, c, ld)));
+    return widen4(ld_g2(base + off(r, c, ld)));
   }
   __device__ static void store4(char* base, int64_t r, int c, int ld, float4 v) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const bf16x4 h = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
-    *reinterpret_cast<bf16x4*>(base + off(r, c, ld)) = h;
+    *(MUONH_GLOBAL bf16x4*)(base + off(r, c, ld)) = h;
   }
 };
 template <>
@@ -274,7 +294,7 @@ struct Fmt<kSplitBf16> {
     return ((((r >> 8) * (ld >> 4)) + (c >> 4)) << 14) + ((r & 255) << 6) + ((c & 15) << 1);
   }
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
-    const __bf16* p = reinterpret_cast<const __bf16*>(base + off(r, c, ld));
+    const MUONH_GLOBAL __bf16* p = (const MUONH_GLOBAL __bf16*)(base + off(r, c, ld));
     return (float)p[0] + (float)p[16];
   }
   __device__ static void store4(char* base, int64_t r, int c, int ld, float4 v) {
@@ -283,13 +303,12 @@ struct Fmt<kSplitBf16> {
     const bf16x4 l = {(__bf16)(v.x - (float)h[0]), (__bf16)(v.y - (float)h[1]),
                       (__bf16)(v.z - (float)h[2]), (__bf16)(v.w - (float)h[3])};
     char* p = base + off(r, c, ld);
-    *reinterpret_cast<bf16x4*>(p) = h;
-    *reinterpret_cast<bf16x4*>(p + 32) = l;
+    *(MUONH_GLOBAL bf16x4*)p = h;
+    *(MUONH_GLOBAL bf16x4*)(p + 32) = l;
   }
   __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
     const char* p = base + off(r, c, ld);
-    return add4(widen4(*reinterpret_cast<const uint2*>(p)),
-                widen4(*reinterpret_cast<const uint2*>(p + 32)));
+    return add4(widen4(ld_g2(p)), widen4(ld_g2(p + 32)));
   }
   __device__ static float4 add4(float4 h, float4 l) {
     return make_float4(h.x + l.x, h.y + l.y, h.z + l.z, h.w + l.w);
@@ -299,13 +318,13 @@ template <>
 struct Fmt<kFp32> {
   __device__ static int64_t off(int64_t r, int c, int ld) { return (r * ld + c) * 4; }
   __device__ static float load(const char* base, int64_t r, int c, int ld) {
-    return *reinterpret_cast<const float*>(base + off(r, c, ld));
+    return *(const MUONH_GLOBAL float*)(base + off(r, c, ld));
   }
   __device__ static float4 load4(const char* base, int64_t r, int c, int ld) {
-    return *reinterpret_cast<const float4*>(base + off(r, c, ld));
+    return ld_g4(base + off(r, c, ld));
   }
   __device__ static void store4(char* base, int64_t r, int c, int ld, float4 v) {
-    *reinterpret_cast<float4*>(base + off(r, c, ld)) = v;
+    st_g4(base + off(r, c, ld), v);
   }
 };
 
@@ -328,24 +347,40 @@ __device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const vo
   const bool trans = g.offE >= 0;
   float acc = 0.f;
   if (trans) __syncthreads();  // the previous tile's transposed reads are done
+  // The vector loads of all four rows are issued before the first store.
+  const int c = c0 + tx;
+  const bool cvec = vec && c + 3 < g.cols;
+  // Rows past the end reload the last row, so that the loads need no
+  // branch of their own (each branch would end in a wait).
+  float4 mv[4], gv[4];
+  if (cvec) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = min(r0 + ty + 16 * i, g.rows - 1);
+      const int64_t i0 = (int64_t)r * g.cols + c;
+      if (kMomentum) {  // read-modify-write of M: non-temporal
+        mv[i] = St<MB>::load4_nt(mp, i0);
+        gv[i] = St<GB>::load4(gp, i0);
+      } else {
+        mv[i] = St<MB>::load4(mp, i0);
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = ty + 16 * i;
-    const int r = r0 + rr, c = c0 + tx;
+    const int r = r0 + rr;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < g.rows) {
       const int64_t i0 = (int64_t)r * g.cols + c;
-      if (vec && c + 3 < g.cols) {
-        if (kMomentum) {  // read-modify-write of M: non-temporal
-          v = St<MB>::load4_nt(mp, i0);
-          const float4 gv = St<GB>::load4(gp, i0);
-          v.x = fmaf(beta, v.x, gv.x);
-          v.y = fmaf(beta, v.y, gv.y);
-          v.z = fmaf(beta, v.z, gv.z);
-          v.w = fmaf(beta, v.w, gv.w);
+      if (cvec) {
+        v = mv[i];
+        if (kMomentum) {
+          v.x = fmaf(beta, v.x, gv[i].x);
+          v.y = fmaf(beta, v.y, gv[i].y);
+          v.z = fmaf(beta, v.z, gv[i].z);
+          v.w = fmaf(beta, v.w, gv[i].w);
           v = St<MB>::store4_nt(mp, i0, v);
-        } else {
-          v = St<MB>::load4(mp, i0);
         }
       } else {
         float e[4] = {0.f, 0.f, 0.f, 0.f};
@@ -493,6 +528,8 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     // rows' O values share 128-byte lines of the panel layout (panel rows r
     // and r + 1 are adjacent 64-byte halves), so each line is read once.
     // Block c takes units [u0, u1); (pair, column group) walk incrementally.
+    // A thread takes two units per iteration and issues all eight loads
+    // before its first store, to keep enough bytes in flight per CU.
     const int cq = cols >> 2;
     const int64_t npairs = (int64_t)(g.rows + 1) >> 1;
     int64_t u0, u1;
@@ -501,39 +538,68 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     int64_t pr = u / cq;
     int q = (int)(u - pr * cq);
     const int dpr = kThreads / cq, dq = kThreads - (kThreads / cq) * cq;
-    for (; u < u1; u += kThreads) {
-      const int col = q << 2;
+    for (; u < u1; u += 2 * kThreads) {
+      int64_t prs[2] = {pr, pr + dpr};
+      int qs[2] = {q, q + dq};
+      if (qs[1] >= cq) { qs[1] -= cq; ++prs[1]; }
+      const bool has1 = u + kThreads < u1;
+      // The loads are unconditional (a slot past the end reloads the first
+      // unit's first row), so that none of them waits for another.
+      float4 wv[2][2], ov[2][2];
+      float* wp[2][2];  // kept until the store (its address registers stay intact)
+      bool live[2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t r = 2 * pr + h;
-        if (h == 1 && r >= g.rows) break;
-        float* wp = w + r * cols + col;
-        float4 wv = ld_nt(wp);
-        // O plainly: rows r and r + 1 read the two halves of one 128-byte
-        // line, and the second read is served from the cache only when the
-        // first did not carry the non-temporal hint
-        const float4 ov = Fmt<F>::load4(D, r, col, g.cp);
-        if (kMode == kDecay) {
-          wv.x *= keep; wv.y *= keep; wv.z *= keep; wv.w *= keep;
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t r = 2 * prs[j] + h;
+          live[j][h] = (j == 0 || has1) && r < g.rows;
+          const int64_t rl = live[j][h] ? r : 2 * prs[0];
+          const int cl = (j == 0 || has1) ? qs[j] << 2 : qs[0] << 2;
+          wp[j][h] = w + rl * cols + cl;
+          wv[j][h] = ld_nt(wp[j][h]);
+          // O plainly: rows r and r + 1 read the two halves of one 128-byte
+          // line, and the second read is served from the cache only when the
+          // first did not carry the non-temporal hint
+          ov[j][h] = Fmt<F>::load4(D, rl, cl, g.cp);
         }
-        wv.x = fmaf(nlr, ov.x, wv.x);
-        wv.y = fmaf(nlr, ov.y, wv.y);
-        wv.z = fmaf(nlr, ov.z, wv.z);
-        wv.w = fmaf(nlr, ov.w, wv.w);
-        if (kWrite) {
-          if (kProject) {
-            wv.x *= scale; wv.y *= scale; wv.z *= scale; wv.w *= scale;
+      // All four results first, then the stores: a store between two
+      // results would make the next one wait for it.
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float4 v = wv[j][h];
+          const float4 o = ov[j][h];
+          if (kMode == kDecay) {
+            v.x *= keep; v.y *= keep; v.z *= keep; v.w *= keep;
           }
-          st_nt(wp, wv);
-        } else {
-          acc = fmaf(wv.x, wv.x, acc);
-          acc = fmaf(wv.y, wv.y, acc);
-          acc = fmaf(wv.z, wv.z, acc);
-          acc = fmaf(wv.w, wv.w, acc);
+          v.x = fmaf(nlr, o.x, v.x);
+          v.y = fmaf(nlr, o.y, v.y);
+          v.z = fmaf(nlr, o.z, v.z);
+          v.w = fmaf(nlr, o.w, v.w);
+          if (kProject) {
+            v.x *= scale; v.y *= scale; v.z *= scale; v.w *= scale;
+          }
+          if (!kWrite && live[j][h]) {
+            acc = fmaf(v.x, v.x, acc);
+            acc = fmaf(v.y, v.y, acc);
+            acc = fmaf(v.z, v.z, acc);
+            acc = fmaf(v.w, v.w, acc);
+          }
+          wv[j][h] = v;
         }
+      // Unconditional stores: a slot past the end holds the first slot's
+      // address and recomputed value, so it rewrites the same bytes (a
+      // store under a branch would again cost a wait).
+      if (kWrite) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) st_nt(wp[j][h], wv[j][h]);
       }
-      q += dq;
-      pr += dpr;
+      pr = prs[1] + dpr;
+      q = qs[1] + dq;
       if (q >= cq) { q -= cq; ++pr; }
     }
   } else {

@@ -130,15 +130,18 @@ int64_t off_update(const muonh_plan* p, const GroupPlan& G) {
 }
 
 // Launch descriptors of the streaming kernels (kind kEwStream: bpm blocks per
-// matrix), the cast (kEwTile: one block per 64x64 tile of the padded domain)
-// or the fused momentum + cast (kEwFused: blocks of tpb = ceil(tiles / 256)
-// tiles, so at most 256 partial sums per matrix), in batches of at most
-// kMaxEwGroups groups.
+// matrix, at most kMaxPartials), the writing updates (kEwOneShot: one pass of
+// the block per unit of 2 rows x 4 columns and thread, two units per thread,
+// so that no thread issues loads after its stores), the cast (kEwTile: one
+// block per 64x64 tile of the padded domain) or the fused momentum + cast
+// (kEwFused: blocks of tpb = ceil(tiles / 256) tiles, so at most 256 partial
+// sums per matrix), in batches of at most kMaxEwGroups groups (the same
+// batches for every kind).
 // ns_iters < 0: D is O (the update and projection read it); otherwise D and
 // E are what the normalising cast writes before ns_iters iterations: X0 in
 // the buffer the first iteration reads (own orientation in D, transposed in
 // E, -1 where nothing is written); with 0 iterations, O itself.
-enum EwKind { kEwStream = 0, kEwTile = 1, kEwFused = 2 };
+enum EwKind { kEwStream = 0, kEwTile = 1, kEwFused = 2, kEwOneShot = 3 };
 
 std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, EwKind kind, int ns_iters) {
   std::vector<EwArgs> out;
@@ -186,6 +189,9 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, EwKind kind, int ns_i
       if (kind == kEwFused) {
         e.tpb = (e.tiles_per_mat + kMaxPartials - 1) / kMaxPartials;
         e.bpm = (e.tiles_per_mat + e.tpb - 1) / e.tpb;
+      } else if (kind == kEwOneShot) {
+        const int64_t units = (int64_t)((G.rows + 1) / 2) * ((G.cols + 3) / 4);
+        e.bpm = (int)std::max<int64_t>(1, (units + 2 * kEwThreads - 1) / (2 * kEwThreads));
       }
       e.block_begin = (int)blocks;
       blocks += (int64_t)G.count * (kind == kEwTile ? e.tiles_per_mat : e.bpm);
@@ -397,7 +403,7 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
   p->sf.g_bf16 = (flags & MUONH_GRAD_BF16) != 0;
   p->sf.m_bf16 = (flags & MUONH_MOM_BF16) != 0;
 
-  int64_t n_mats = 0;
+  int64_t n_mats = 0, total_tiles = 0;
   for (int32_t i = 0; i < n_groups; ++i) {
     const muonh_group_desc& d = groups[i];
     if (d.rows < 1 || d.rows > MUONH_MAX_DIM || d.cols < 1 || d.cols > MUONH_MAX_DIM) {
@@ -413,6 +419,15 @@ int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t 
     if (n_mats > MUONH_MAX_MATRICES) {
       delete p;
       return fail(MUONH_ESHAPE, "more than %d matrices", MUONH_MAX_MATRICES);
+    }
+    // Elementwise launches index their blocks with 32-bit integers; the
+    // largest per-matrix block count is the cast's 64x64 tiles of the padded
+    // domain (every other kind needs fewer).
+    const int64_t pr = round_up(d.rows, kPad), pc = round_up(d.cols, kPad);
+    total_tiles += (int64_t)d.count * (pr / 64) * (pc / 64);
+    if (total_tiles > INT32_MAX) {
+      delete p;
+      return fail(MUONH_ESHAPE, "plan too large: more than 2^31 elementwise tiles");
     }
   }
   try {
@@ -557,6 +572,7 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
   if ((e = launch_zero_i32(sched, kStatusWord + 1, s)) != hipSuccess) return hip_fail(e, "step status");
 
   const std::vector<EwArgs> stream_args = make_ew(plan, ws, kEwStream, -1);
+  const std::vector<EwArgs> write_args = make_ew(plan, ws, kEwOneShot, -1);
   // bf16 and split operands with at least one iteration: momentum and the
   // unscaled cast in one pass, normalisation deferred to the first GEMMs
   // (see xnorm_deferred); otherwise momentum, its norm, then the cast.
@@ -611,17 +627,18 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
 
   if (var.muon_wd) {
     const float keep = (float)(1.0 - (double)lr * (double)var.weight_decay);
-    for (const EwArgs& a : stream_args)
+    for (const EwArgs& a : write_args)
       if ((e = launch_decay_update(a, plan->prec, W, lr, keep, s)) != hipSuccess)
         return hip_fail(e, "decayed update");
   } else {
-    for (const EwArgs& a : stream_args) {
+    for (size_t b = 0; b < stream_args.size(); ++b) {
+      const EwArgs& a = stream_args[b];
       if ((e = launch_update_norm(a, plan->prec, W, lr, partials, s)) != hipSuccess)
         return hip_fail(e, "update norm");
       if ((e = launch_finalize(a, partials, norm_w, nullptr, s, nf_flags, MUONH_NONFINITE_UPDATE)) !=
           hipSuccess)
         return hip_fail(e, "update finalize");
-      if ((e = launch_project(a, plan->prec, W, R, norm_w, lr, s)) != hipSuccess)
+      if ((e = launch_project(write_args[b], plan->prec, W, R, norm_w, lr, s)) != hipSuccess)
         return hip_fail(e, "project");
     }
   }

@@ -62,11 +62,14 @@ struct StateFmt {
 // Elementwise / reduction kernels (elementwise.hip)
 // ---------------------------------------------------------------------------
 constexpr int kMaxEwGroups = 16;
+// Threads per block of every elementwise kernel.
+constexpr int kEwThreads = 256;
 
 struct EwGroup {
   int rows, cols;       // matrix shape (row-major fp32)
   int count, first;     // number of matrices, global index of the first one
-  int bpm;              // blocks per matrix (= partial sums per matrix)
+  int bpm;              // blocks per matrix (= partial sums per matrix in the
+                        // kernels that take norms)
   int tpb;              // tiles per block (fused momentum + cast)
   int block_begin;      // first block of this group in the launch
   int64_t n;            // rows * cols

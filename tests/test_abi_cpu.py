@@ -53,6 +53,7 @@ def _create(groups, flags=0):
     ([(4, -1, 1)], 0, mh.MUONH_ESHAPE),            # negative cols
     ([(4, 4, 0)], 0, mh.MUONH_ESHAPE),             # empty group
     ([(65537, 4, 1)], 0, mh.MUONH_ESHAPE),         # beyond the max dimension
+    ([(65536, 65536, 2048)], 0, mh.MUONH_ESHAPE),  # 2^31 cast tiles: past 32-bit block indices
 ])
 def test_plan_create_rejects(groups, flags, code):
     st, h = _create(groups, flags)
