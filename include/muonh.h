@@ -133,7 +133,8 @@ int32_t muonh_abi_version(void);
  * that must be released with muonh_plan_destroy. Errors: MUONH_EINVAL (null
  * out/groups, n_groups out of [1, MUONH_MAX_GROUPS], unknown or conflicting
  * flags), MUONH_ESHAPE (a dim out
- * of [1, MUONH_MAX_DIM], count < 1, too many matrices), MUONH_ENOMEM.
+ * of [1, MUONH_MAX_DIM], count < 1, too many matrices, or more than 2^31
+ * 64x64 tiles of the 256-padded matrices in total), MUONH_ENOMEM.
  */
 int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t n_groups,
                       uint32_t flags);
