@@ -130,8 +130,22 @@ def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1, mom_bf16=Fa
                    "full set (%s); est. %.1f s per full step"
                    % (k, "decayed update" if variant == "muon_wd" else "projection", used,
                       "; ".join(parts), total)),
-        "host_cpu": platform.processor() or platform.machine(),
+        "host_cpu": host_cpu(),
     }
+
+
+def host_cpu() -> str:
+    """CPU model from /proc/cpuinfo and the logical CPU count of the host."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
 
 
 def code_sha16(path: str) -> str:
@@ -217,7 +231,7 @@ def adamw_cpu_baseline(n_params, budget_s):
         "sample": ("%d fp64 oracle AdamW steps over a %d-element slice (two gradients "
                    "alternating), %.1f s; numpy elementwise, one thread; est. %.2f s per full "
                    "%d-element step" % (runs, n, el, n_params * el / (n * runs), n_params)),
-        "host_cpu": platform.processor() or platform.machine(),
+        "host_cpu": host_cpu(),
     }
 
 
