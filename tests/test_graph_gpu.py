@@ -1,8 +1,8 @@
 """The MuonH step inside a captured HIP graph.
 
 The step allocates nothing, synchronises nothing and records no memset
-(its tail-balancing counters are cleared by a kernel), so a caller can
-capture it. The graph is replayed several times, with eager work and
+(its tail-balancing counters and its non-finite status word are cleared by
+a kernel), so a caller can capture it. The graph is replayed several times, with eager work and
 synchronisations between the replays, and every replay must leave W and M
 bit for bit where the same number of eager steps leaves them (the kernels
 are deterministic, and each replay runs the same launches on the same
@@ -79,3 +79,5 @@ def test_step_replays_in_a_hip_graph(shapes):
             assert torch.equal(W_g[i], W_ref[i]), f"replay {r}: W of matrix {i}"
             assert torch.equal(M_g[i], M_ref[i]), f"replay {r}: M of matrix {i}"
         say(f"[graph] replay {r} equals eager step {2 + r}")
+    # the status word is cleared by a kernel inside the graph: finite replays report 0
+    assert opt_g.status() == 0
