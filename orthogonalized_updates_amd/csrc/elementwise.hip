@@ -546,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
       // The loads are unconditional (a slot past the end reloads the first
       // unit's first row), so that none of them waits for another.
       float4 wv[2][2], ov[2][2];
-      float* wp[2][2];  // kept until the store (its address registers stay intact)
+      float* wp[2][2];  // the load addresses, reused by the stores
       bool live[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
