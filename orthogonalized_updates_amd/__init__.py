@@ -52,6 +52,16 @@ ADAMW_MAX_TENSORS_PER_LAUNCH = 128
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
 
 
+def find_overlap(spans):
+    """First pair of overlapping byte ranges among `spans`, a list of
+    (start, end, label) with end exclusive; None if they are disjoint."""
+    order = sorted(s for s in spans if s[1] > s[0])
+    for prev, cur in zip(order, order[1:]):
+        if cur[0] < prev[1]:
+            return prev[2], cur[2]
+    return None
+
+
 class MuonHError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"muonh error {status}: {message}")
@@ -219,6 +229,7 @@ class MuonH:
             raise MuonHError(MUONH_EWORKSPACE, "torch returned a workspace that is not 256-aligned")
         self.R = torch.zeros(len(self.shapes), dtype=torch.float32, device=self.device)
         self._ptr_cache: Dict[str, Tuple[Tuple[int, ...], object]] = {}
+        self._disjoint_ok: set = set()  # (W, G, M) pointer tuples already checked
 
     # -- marshalling ------------------------------------------------------
     def _check(self, tensors, name: str):
@@ -233,6 +244,26 @@ class MuonH:
                 raise ValueError(f"{name}[{i}] is on {t.device}, expected {self.device}")
             if tuple(t.shape) != self.shapes[i] or not t.is_contiguous():
                 raise ValueError(f"{name}[{i}] must be a contiguous {self.shapes[i]} tensor")
+
+    def _check_state(self, weights, grads, moms):
+        """Types and shapes of W, G and M, and that no two of their tensors
+        overlap in memory (the step updates W and M in place and reads G;
+        checked on the host, once per combination of pointers)."""
+        self._check(weights, "weights")
+        self._check(grads, "grads")
+        self._check(moms, "moms")
+        key = tuple(tuple(int(t.data_ptr()) for t in ts) for ts in (weights, grads, moms))
+        if key in self._disjoint_ok:
+            return
+        spans = [(int(t.data_ptr()), int(t.data_ptr()) + t.numel() * t.element_size(), f"{nm}[{i}]")
+                 for nm, ts in (("weights", weights), ("grads", grads), ("moms", moms))
+                 for i, t in enumerate(ts)]
+        hit = find_overlap(spans)
+        if hit is not None:
+            raise ValueError(f"{hit[0]} and {hit[1]} overlap in memory; W, G and M must be disjoint")
+        if len(self._disjoint_ok) >= 64:
+            self._disjoint_ok.clear()
+        self._disjoint_ok.add(key)
 
     def _ptr_array(self, name: str, tensors) -> int:
         ptrs = tuple(int(tensors[c].data_ptr()) for c in self.plan_order)
@@ -268,9 +299,7 @@ class MuonH:
 
     def step(self, weights, grads, moms, lr: float, beta: float = 0.95, ns_iters: int = 5) -> None:
         """One MuonH step: moms and weights are updated in place."""
-        self._check(weights, "weights")
-        self._check(grads, "grads")
-        self._check(moms, "moms")
+        self._check_state(weights, grads, moms)
         if not hasattr(self, "_R_plan"):
             raise RuntimeError("call init() (or set_radius()) before step()")
         check(get_lib().muonh_step(self.plan.handle, self._ptr_array("W", weights),
@@ -282,9 +311,7 @@ class MuonH:
                    events) -> None:
         """step() plus hipEventRecord of `events` (torch.cuda.Event list of
         length 3*ns_iters+3, already recorded once) at the phase boundaries."""
-        self._check(weights, "weights")
-        self._check(grads, "grads")
-        self._check(moms, "moms")
+        self._check_state(weights, grads, moms)
         if not hasattr(self, "_R_plan"):
             raise RuntimeError("call init() (or set_radius()) before step_timed()")
         arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
@@ -299,9 +326,7 @@ class MuonH:
         """The baseline MuonH is measured against: Muon with decoupled weight
         decay, W <- (1 - lr*wd) W - lr O (no projection, no radius). With
         `events` (as for step_timed), records the phase boundaries."""
-        self._check(weights, "weights")
-        self._check(grads, "grads")
-        self._check(moms, "moms")
+        self._check_state(weights, grads, moms)
         args = [self.plan.handle, self._ptr_array("W", weights), self._ptr_array("G", grads),
                 self._ptr_array("M", moms), float(lr), float(beta), float(weight_decay),
                 int(ns_iters), self.workspace.data_ptr(), self.workspace.numel(), self._stream()]
@@ -334,7 +359,8 @@ class MuonH:
 __all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
            "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
            "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32", "MUONH_NS_SPLIT_BF16", "MUONH_GRAD_BF16",
-           "MUONH_MOM_BF16", "MUONH_NONFINITE_MOMENTUM", "MUONH_NONFINITE_UPDATE", "AdamW"]
+           "MUONH_MOM_BF16", "MUONH_NONFINITE_MOMENTUM", "MUONH_NONFINITE_UPDATE", "AdamW",
+           "find_overlap"]
 
 
 class AdamW:

@@ -258,3 +258,12 @@ def test_step_status_rejects_before_any_device_work():
     assert st == mh.MUONH_EWORKSPACE
     assert flags.value == 7  # untouched on error
     assert mh.lib.muonh_last_error().decode()
+
+
+def test_find_overlap():
+    assert mh.find_overlap([]) is None
+    assert mh.find_overlap([(0, 16, "a"), (16, 32, "b"), (64, 80, "c")]) is None  # touching is fine
+    assert mh.find_overlap([(0, 16, "a"), (8, 24, "b")]) == ("a", "b")
+    assert mh.find_overlap([(100, 200, "x"), (0, 16, "a"), (120, 130, "y")]) == ("x", "y")  # containment
+    assert mh.find_overlap([(5, 5, "empty"), (0, 16, "a")]) is None  # zero-length spans ignored
+    assert mh.find_overlap([(0, 16, "a"), (0, 16, "b")]) == ("a", "b")  # same buffer twice
