@@ -248,7 +248,8 @@ int muonh_read_update(const muonh_plan* plan, int64_t index, float* dst, const v
 
 /*
  * Non-finite report of the last muonh_step or muonh_step_muon_wd that used
- * this workspace: each step clears the record when it starts and then sets
+ * this workspace (0 after muonh_init on it and before any step): each step
+ * clears the record when it starts and then sets
  *   MUONH_NONFINITE_MOMENTUM  when ||M|| (after the momentum update) of any
  *                             matrix is NaN or infinite: its X0, O and W are
  *                             then not finite either;

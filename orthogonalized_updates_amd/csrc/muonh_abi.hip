@@ -508,6 +508,9 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
   double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
   double* norms = reinterpret_cast<double*>(ws + plan->off_norm_w);
   hipError_t e;
+  // a workspace that no step has used yet reports no non-finite norm
+  int* sched = reinterpret_cast<int*>(ws + plan->off_sched);
+  if ((e = launch_zero_i32(sched, kStatusWord + 1, s)) != hipSuccess) return hip_fail(e, "init status");
   for (const EwArgs& a : make_ew(plan, ws, kEwStream, -1)) {
     if ((e = launch_sumsq(a, W, partials, s)) != hipSuccess) return hip_fail(e, "init sumsq");
     if ((e = launch_finalize(a, partials, norms, R, s)) != hipSuccess)

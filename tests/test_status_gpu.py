@@ -43,6 +43,17 @@ def _state(prec, seed=80):
     return opt, W, G, M, R
 
 
+def test_init_clears_the_record():
+    need_gpu()
+    import orthogonalized_updates_amd as mh
+    opt = mh.MuonH(SHAPES)
+    opt.workspace.fill_(255)  # a workspace full of stale bytes
+    W = [torch.from_numpy(workloads.host_custom(s, 0.02, (80, i))).cuda() for i, s in enumerate(SHAPES)]
+    opt.init(W)
+    assert opt.status() == 0
+    say("[status] init clears the record")
+
+
 @pytest.mark.parametrize("prec", ["bf16", "fp32"])
 def test_finite_step_reports_nothing(prec):
     need_gpu()
