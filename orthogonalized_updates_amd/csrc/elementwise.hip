@@ -543,8 +543,12 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
       int qs[2] = {q, q + dq};
       if (qs[1] >= cq) { qs[1] -= cq; ++prs[1]; }
       const bool has1 = u + kThreads < u1;
-      // The loads are unconditional (a slot past the end reloads the first
-      // unit's first row), so that none of them waits for another.
+      // The loads are unconditional, so that none of them waits for another:
+      // a row past the end (the second row of the last pair of an odd row
+      // count) reloads its own unit's first row, and a unit past the end
+      // reloads the first unit's first row. Either way the address belongs
+      // to one of this thread's own live units, so the store below rewrites
+      // bytes only this thread writes, with the value it already computed.
       float4 wv[2][2], ov[2][2];
       float* wp[2][2];  // the load addresses, reused by the stores
       bool live[2][2];
@@ -552,10 +556,11 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          const bool unit = j == 0 || has1;  // slot j holds a unit of this block
           const int64_t r = 2 * prs[j] + h;
-          live[j][h] = (j == 0 || has1) && r < g.rows;
-          const int64_t rl = live[j][h] ? r : 2 * prs[0];
-          const int cl = (j == 0 || has1) ? qs[j] << 2 : qs[0] << 2;
+          live[j][h] = unit && r < g.rows;
+          const int64_t rl = live[j][h] ? r : 2 * (unit ? prs[j] : prs[0]);
+          const int cl = (unit ? qs[j] : qs[0]) << 2;
           wp[j][h] = w + rl * cols + cl;
           wv[j][h] = ld_nt(wp[j][h]);
           // O plainly: rows r and r + 1 read the two halves of one 128-byte
@@ -589,9 +594,10 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
           }
           wv[j][h] = v;
         }
-      // Unconditional stores: a slot past the end holds the first slot's
-      // address and recomputed value, so it rewrites the same bytes (a
-      // store under a branch would again cost a wait).
+      // Unconditional stores: a slot past the end holds the address and the
+      // recomputed value of one of this thread's live units, so it rewrites
+      // the same bytes with the same value (a store under a branch would
+      // again cost a wait).
       if (kWrite) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
