@@ -10,12 +10,12 @@ bf16 or how values are rounded. Readings taken here:
 
 * A bf16 gradient is an input: its values are exactly the bf16 numbers
   given (bf16 is the upper half of an IEEE binary32), nothing is rounded.
-* A bf16 momentum is storage: the new momentum is beta*M + G evaluated in
-  binary32 with a single rounding (what a fused multiply-add gives, with
-  beta the binary32 value the kernel receives), then rounded to the nearest
-  bf16, ties to even, and stored. The stored (rounded) value is the momentum
-  that Newton-Schulz normalises and orthogonalises. Both roundings decide
-  bits, so this side takes them in the kernel's precision, exactly.
+* A bf16 momentum is storage: the new momentum is the exact real number
+  beta*M + G (beta taken as the binary32 value a caller passes), rounded
+  once to the nearest bf16, ties to even, and stored. The stored (rounded)
+  value is the momentum that Newton-Schulz normalises and orthogonalises.
+  This is the plain definition of storing a result in bf16: no intermediate
+  binary32 rounding is assumed, since the page prints none.
 
 Everything here is numpy: conversions to float32 (IEEE round to nearest
 even) and float64 arithmetic are the library primitives; the rest is
@@ -65,46 +65,61 @@ def round_to_bf16(x) -> np.ndarray:
     return bf16_bits_to_f64(f32_to_bf16_bits(x))
 
 
-def fma_f32(a, b, c) -> np.ndarray:
-    """a*b + c for binary32 a, b, c, computed exactly and rounded once to
-    binary32 (nearest, ties to even).
+def round_real_to_bf16(hi, lo) -> np.ndarray:
+    """The bf16 number nearest to the real number hi + lo, ties to the one
+    with an even last significand bit, as float64.
 
-    The product of two 24-bit significands fits a float64 exactly. The sum s
-    is rounded to float64, and its rounding error e is recovered exactly
-    (Knuth's two-sum), so s + e is the exact result. Rounding s to binary32
-    gives the right answer unless s falls exactly on the midpoint between
-    two binary32 neighbours while e is not zero: then the exact value lies on
-    the side of the midpoint that e points to.
+    hi is float64 and lo is what float64 could not hold of the real number
+    (hi = fl64(hi + lo), so |lo| is at most half a float64 ulp of hi). bf16
+    keeps 8 significant bits; below 2^-126 its spacing stays 2^-133
+    (subnormals). Magnitudes at or past the midpoint above the largest finite
+    bf16 go to infinity; infinities and NaN stay what they are.
+
+    Written out from the definition: the spacing of the bf16 numbers around
+    |hi| is a power of two, so |hi| / spacing is exact and its fractional
+    part says on which side of the midpoint |hi| lies; exactly on it, lo
+    decides, and with lo = 0 it is a tie.
     """
-    a = np.asarray(a, dtype=np.float32).astype(np.float64)
-    b = np.asarray(b, dtype=np.float32).astype(np.float64)
-    c = np.asarray(c, dtype=np.float32).astype(np.float64)
-    p = a * b                      # exact
-    s = p + c
-    bv = s - p
-    e = (p - (s - bv)) + (c - bv)  # s + e == p + c exactly
-    r = s.astype(np.float32)
-    rd = r.astype(np.float64)
-    # binary32 neighbours below and above s (when s is not itself binary32)
-    lo = np.where(rd <= s, r, np.nextafter(r, np.float32(-np.inf)))
-    hi = np.nextafter(lo, np.float32(np.inf))
+    hi = np.asarray(hi, dtype=np.float64)
+    lo = np.asarray(lo, dtype=np.float64)
     with np.errstate(invalid="ignore", over="ignore"):
-        mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0
-    on_mid = (s == mid) & (rd != s) & np.isfinite(s)
-    out = np.where(on_mid & (e > 0), hi, np.where(on_mid & (e < 0), lo, r))
-    return out.astype(np.float32)
+        a = np.abs(hi)
+        sgn = np.where(np.signbit(hi), -1.0, 1.0)
+        lo_out = lo * sgn                   # > 0: the real magnitude is above a
+        _, ex = np.frexp(np.where(np.isfinite(a), a, 0.0))   # a = f * 2^ex, f in [0.5, 1)
+        e = np.maximum(ex - 1, -126)        # exponent of the leading bit
+        spacing = np.ldexp(1.0, e - 7)
+        q = np.where(np.isfinite(a), a, 0.0) / spacing        # exact
+        n = np.floor(q)
+        frac = q - n
+        odd = np.fmod(n, 2.0) == 1.0
+        up = (frac > 0.5) | ((frac == 0.5) & ((lo_out > 0) | ((lo_out == 0) & odd)))
+        mag = (n + up) * spacing
+        mag = np.where(mag >= 2.0 ** 128, np.inf, mag)
+        out = sgn * mag
+    return np.where(np.isfinite(hi), out, hi)
 
 
 def momentum_update_bf16_state(m, g, beta: float) -> np.ndarray:
-    """New momentum kept in bf16: round_to_bf16(fl32(beta32*M + G)).
+    """New momentum kept in bf16: the bf16 number nearest to the exact real
+    beta32*M + G (one rounding, ties to even).
 
     m: the stored momentum (bf16 values, given as any float array); g: the
-    gradient (binary32 or bf16 values). Returns float64 values that are all
-    exactly bf16.
+    gradient (binary32 or bf16 values); beta32: beta as a binary32 number.
+    beta32*M has at most 24 + 8 significant bits, so float64 holds it
+    exactly; the float64 sum s of it and G is rounded, and its rounding
+    error e is recovered exactly (Knuth's two-sum: s + e = beta32*M + G), so
+    round_real_to_bf16(s, e) rounds the exact value once. Returns float64
+    values that are all exactly bf16.
     """
     m32 = np.asarray(m, dtype=np.float64).astype(np.float32)
     if not np.array_equal(round_to_bf16(m32), np.asarray(m, dtype=np.float64), equal_nan=True):
         raise ValueError("a bf16 momentum must hold bf16 values")
-    g32 = np.asarray(g, dtype=np.float64).astype(np.float32)
-    beta32 = np.float32(beta)
-    return round_to_bf16(fma_f32(np.full_like(m32, beta32), m32, g32))
+    g64 = np.asarray(g, dtype=np.float64).astype(np.float32).astype(np.float64)
+    beta64 = float(np.float32(beta))
+    p = beta64 * m32.astype(np.float64)     # exact
+    with np.errstate(invalid="ignore"):
+        s = p + g64
+        bv = s - p
+        e = (p - (s - bv)) + (g64 - bv)     # s + e == p + g exactly
+    return round_real_to_bf16(s, np.where(np.isfinite(s), e, 0.0))

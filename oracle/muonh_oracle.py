@@ -133,11 +133,6 @@ def muonh_step(w, g, m, radius: float, lr: float, beta: float, ns_iters: int,
     return w_new, m_new, o
 
 
-def trial_norm(w, o, lr: float) -> float:
-    """||W - lr*O||_F, the normaliser of the projection (for diagnostics)."""
-    return frobenius_norm(_f64(w) - float(lr) * _f64(o))
-
-
 def muon_wd_step(w, g, m, lr: float, beta: float, weight_decay: float, ns_iters: int,
                  coeffs=NS_COEFFS, eps: float = NS_EPS, mom_bf16: bool = False):
     """Muon with decoupled weight decay: the baseline MuonH is measured against.

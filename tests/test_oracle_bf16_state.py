@@ -1,11 +1,11 @@
 """Pins of the oracle's bf16 storage of the gradient and the momentum.
 
-The oracle (oracle/bf16_state_oracle.py) keeps a bf16 momentum as
-round_to_bf16(fl32(beta32*M + G)): one binary32 rounding of the exact value,
-then round to nearest even at 8 significant bits. Checked here against
-torch's CPU bf16 conversion (a library routine), hand values, and a brute
-force in exact rational arithmetic with its own rounding, on random and on
-constructed near-tie inputs; planted mistakes must fail.
+The oracle (oracle/bf16_state_oracle.py) keeps a bf16 momentum as the bf16
+number nearest to the exact real beta32*M + G (one rounding, ties to even).
+Checked here against torch's CPU bf16 conversion (a library routine), hand
+values, and a brute force in exact rational arithmetic with its own
+rounding, on random and on constructed near-tie inputs; planted mistakes
+(among them the two-step reading that rounds to binary32 first) must fail.
 """
 from __future__ import annotations
 
@@ -47,7 +47,47 @@ def rne_fraction(q: Fraction, sig_bits: int, min_exp: int = -126) -> Fraction:
 
 def exact_momentum(beta32: np.float32, m: float, g: float) -> float:
     q = Fraction(float(beta32)) * Fraction(float(m)) + Fraction(float(g))
-    return float(rne_fraction(rne_fraction(q, 24), 8))
+    return float(rne_fraction(q, 8))
+
+
+def bf16_midpoint_above(v: Fraction) -> Fraction:
+    """The midpoint between the bf16 number v and its neighbour away from zero."""
+    if v == 0:
+        return Fraction(2) ** -134
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    half = Fraction(2) ** (max(e, -126) - 8)
+    return v + (half if v > 0 else -half)
+
+
+def fma_f32(a, b, c) -> np.ndarray:
+    """a*b + c for binary32 a, b, c rounded once to binary32 (a test helper:
+    the planted two-step reading below rounds through it).
+
+    The product of two 24-bit significands fits a float64 exactly; the sum's
+    float64 rounding error e is recovered with two-sum, and a float64 sum
+    that lands exactly on a binary32 midpoint is moved to the side e points
+    to."""
+    a = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a * b
+    s = p + c
+    bv = s - p
+    e = (p - (s - bv)) + (c - bv)
+    r = s.astype(np.float32)
+    rd = r.astype(np.float64)
+    lo = np.where(rd <= s, r, np.nextafter(r, np.float32(-np.inf)))
+    hi = np.nextafter(lo, np.float32(np.inf))
+    with np.errstate(invalid="ignore", over="ignore"):
+        mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0
+    on_mid = (s == mid) & (rd != s) & np.isfinite(s)
+    out = np.where(on_mid & (e > 0), hi, np.where(on_mid & (e < 0), lo, r))
+    return out.astype(np.float32)
 
 
 def bf16_values(rng, n, lo_exp=-20, hi_exp=4):
@@ -78,11 +118,46 @@ def near_tie_cases(rng, beta32, n):
     return np.array(ms, np.float32), np.array(gs, np.float32)
 
 
+def exact_tie_cases(rng, beta32, n):
+    """Two families that only the exact value decides:
+    even i: beta32*m + g is exactly a bf16 midpoint, with beta32*m of about
+      the midpoint's size (g = midpoint - beta32*m is a binary32 number), so
+      the result is the tie's even neighbour, and an error in beta32*m moves it;
+    odd i: g is a bf16 midpoint and beta32*m is below half a float64 ulp of
+      it, so the float64 sum is the midpoint itself and only its rounding
+      error says on which side the exact value lies."""
+    ms, gs = [], []
+    for i in range(n):
+        if i % 2 == 0:
+            while True:
+                m = float(bf16_values(rng, 1, -6, 3)[0])
+                p = Fraction(float(beta32)) * Fraction(m)
+                mid = bf16_midpoint_above(Fraction(float(rne_fraction(p, 8))))
+                g = mid - p
+                if Fraction(float(np.float32(float(g)))) == g:
+                    break
+            ms.append(m)
+            gs.append(float(g))
+        else:
+            h = float(bf16_values(rng, 1, -6, 3)[0])
+            mid = bf16_midpoint_above(Fraction(h))
+            e = abs(h).hex().split("p")[1]
+            m = float(bf16_values(rng, 1, int(e) - 70, int(e) - 60)[0])
+            ms.append(m)
+            gs.append(float(mid))
+    return np.array(ms, np.float32), np.array(gs, np.float32)
+
+
 # the binary32 beta and inputs of a double-rounding trap: beta*m = 2^-24 + 2^-54,
 # so beta*m + g = 1 + 2^-8 + 2^-24 + 2^-54 lies just above a binary32
 # midpoint; rounding the float64 sum (1 + 2^-8 + 2^-24) ties to even instead
 TRAP_BETA = np.float32(16519105 * 2.0 ** -24)   # 16519105 * 65 = 2^30 + 1
 TRAP_M, TRAP_G = np.float32(65 * 2.0 ** -30), np.float32(1 + 2.0 ** -8)
+# a double-rounding case of the two-step reading: beta*m + g = 1 + 2^-8 + 2^-30
+# lies above the bf16 midpoint 1 + 2^-8 (so it rounds up to 1 + 2^-7), but
+# within half a binary32 ulp of it, so a binary32 rounding first lands on the
+# midpoint and the tie then goes to the even 1.0
+DR_BETA, DR_M, DR_G = np.float32(0.5), np.float32(2.0 ** -29), np.float32(1 + 2.0 ** -8)
 
 
 # ---------------------------------------------------------------------------
@@ -128,11 +203,35 @@ def test_fma_f32_against_exact_rationals():
     a = np.concatenate([a, [np.float32(0.75), TRAP_BETA]]).astype(np.float32)
     b = np.concatenate([b, [np.float32(2.0), TRAP_M]]).astype(np.float32)
     c = np.concatenate([c, [np.float32(-1.5), TRAP_G]]).astype(np.float32)
-    got = oracle.fma_f32(a, b, c)
+    got = fma_f32(a, b, c)
     for i in range(len(a)):
         q = Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i]))
         assert Fraction(float(got[i])) == rne_fraction(q, 24), i
     assert got[-1] == np.float32(1 + 2 ** -8 + 2 ** -23)
+
+
+def test_round_real_to_bf16_against_exact_rationals():
+    rng = np.random.default_rng(95)
+    n = 4000
+    hi = rng.standard_normal(n) * 2.0 ** rng.integers(-140, 126, n)
+    # exact bf16 midpoints and bf16 numbers, each with a small lo on either side
+    mid = np.array([float(bf16_midpoint_above(Fraction(float(v))))
+                    for v in oracle.round_to_bf16(hi.astype(np.float32))])
+    hi = np.concatenate([hi, mid, mid, mid, oracle.round_to_bf16(hi[:500].astype(np.float32))])
+    ulp64 = np.abs(np.spacing(hi))
+    lo = np.concatenate([np.zeros(n), 0.25 * ulp64[n:2 * n], -0.25 * ulp64[2 * n:3 * n],
+                         np.zeros(n), -0.5 * ulp64[4 * n:]])
+    got = oracle.round_real_to_bf16(hi, lo)
+    for i in range(len(hi)):
+        q = Fraction(float(hi[i])) + Fraction(float(lo[i]))
+        assert Fraction(float(got[i])) == rne_fraction(q, 8, -126), i
+    # overflow: the midpoint above the largest finite bf16 and beyond
+    big = float(np.uint32(0x7F7F0000).view(np.float32))
+    top_mid = big + 2.0 ** 119
+    out = oracle.round_real_to_bf16([big, top_mid, -top_mid, top_mid], [0.0, 0.0, 0.0, -2.0 ** 60])
+    assert out[0] == big and np.isposinf(out[1]) and np.isneginf(out[2]) and out[3] == big
+    assert np.isnan(oracle.round_real_to_bf16([np.nan], [0.0])[0])
+    assert np.isposinf(oracle.round_real_to_bf16([np.inf], [0.0])[0])
 
 
 # ---------------------------------------------------------------------------
@@ -147,7 +246,10 @@ def _momentum_cases():
         g = (rng.standard_normal(600) * 2.0 ** rng.integers(-12, 2, 600)).astype(np.float32)
         mt, gt = near_tie_cases(rng, b32, 400)
         cases.append((beta, np.concatenate([m, mt]), np.concatenate([g, gt])))
+        mx, gx = exact_tie_cases(rng, b32, 200)
+        cases.append((beta, mx, gx))
     cases.append((float(TRAP_BETA), np.float32([TRAP_M]), np.float32([TRAP_G])))
+    cases.append((float(DR_BETA), np.float32([DR_M]), np.float32([DR_G])))
     return cases
 
 
@@ -173,9 +275,12 @@ def test_bf16_momentum_special_cases():
     assert np.array_equal(oracle.momentum_update_bf16_state(m, g, 0.0), g)
     # G = 0 and beta = 1/2: halving is exact
     assert np.array_equal(oracle.momentum_update_bf16_state(m, np.zeros(500), 0.5), m / 2)
-    # the double-rounding trap lands one bf16 ulp above 1 + 2^-8's tie
+    # both traps lie above the bf16 midpoint 1 + 2^-8: one rounding goes up
     r = oracle.momentum_update_bf16_state(np.array([float(TRAP_M)]), np.array([float(TRAP_G)]),
                                           float(TRAP_BETA))
+    assert r[0] == 1 + 2 ** -7
+    r = oracle.momentum_update_bf16_state(np.array([float(DR_M)]), np.array([float(DR_G)]),
+                                          float(DR_BETA))
     assert r[0] == 1 + 2 ** -7
     with pytest.raises(ValueError):
         oracle.momentum_update_bf16_state(np.array([1 + 2 ** -10]), np.zeros(1), 0.9)
@@ -195,10 +300,11 @@ def _mutant(kind):
         m = np.asarray(m, np.float64)
         g = np.asarray(g, np.float64)
         b = float(np.float32(beta)) if kind != "fp64_beta" else float(beta)
-        if kind in ("double_rounding", "fp64_beta"):   # float64 sum rounded to binary32
-            t = (b * m + g).astype(np.float32)
-        else:
-            t = oracle.fma_f32(np.full(m.shape, np.float32(b)), m.astype(np.float32), g.astype(np.float32))
+        if kind == "fp64_beta":     # beta not taken as its binary32 value
+            return oracle.round_real_to_bf16(b * m + g, np.zeros(m.shape))
+        if kind == "no_sticky":     # the float64 sum rounded, its error dropped
+            return oracle.round_real_to_bf16(b * m + g, np.zeros(m.shape))
+        t = fma_f32(np.full(m.shape, np.float32(b)), m.astype(np.float32), g.astype(np.float32))
         if kind == "truncate":
             u = t.view(np.uint32) & np.uint32(0xFFFF0000)
             return u.view(np.float32).astype(np.float64)
@@ -207,10 +313,11 @@ def _mutant(kind):
             return u.view(np.float32).astype(np.float64)
         if kind == "no_bf16_store":
             return t.astype(np.float64)
-        return oracle.round_to_bf16(t)
+        return oracle.round_to_bf16(t)  # "through_binary32": two roundings
     return fn
 
 
-@pytest.mark.parametrize("kind", ["double_rounding", "fp64_beta", "truncate", "ties_away", "no_bf16_store"])
+@pytest.mark.parametrize("kind", ["through_binary32", "no_sticky", "fp64_beta", "truncate",
+                                  "ties_away", "no_bf16_store"])
 def test_planted_bf16_momentum_mistake_is_caught(kind):
     assert not check_momentum_exact(_mutant(kind))
