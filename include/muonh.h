@@ -80,7 +80,8 @@ enum {
   MUONH_ESHAPE = -2,     /* bad group description or matrix index */
   MUONH_EWORKSPACE = -3, /* workspace missing, too small or misaligned */
   MUONH_EHIP = -4,       /* a HIP runtime call failed (see muonh_last_error) */
-  MUONH_ENOMEM = -5      /* host allocation failed */
+  MUONH_ENOMEM = -5,     /* host allocation failed */
+  MUONH_EALIAS = -6      /* two of the W, G, M matrices overlap in memory */
 };
 
 /* Newton-Schulz plan flags (at most one). Default: operands in bf16, bf16
@@ -88,8 +89,8 @@ enum {
  * iterations, about 2e-2 at 8. With bf16 or split operands and
  * ns_iters >= 1, X0's factor 1/(||M||_F + 1e-7) is applied inside the first
  * iteration's products rather than before rounding M to the operand format
- * (the same value up to that rounding; momentum norms outside
- * [2^-40, 2^40] are normalised first). */
+ * (the same value up to that rounding; matrices of at most 65536 entries,
+ * and momentum norms outside [2^-40, 2^40], are normalised first). */
 enum {
   /* fp32 operands and fp32 MFMA. Debug/reference mode: about 1e-6 relative
    * error, an order of magnitude slower. */
@@ -108,10 +109,10 @@ enum {
 enum {
   /* G is bf16: its values are taken as given. */
   MUONH_GRAD_BF16 = 4u,
-  /* M is stored in bf16: the new momentum beta*M + G is computed in fp32
-   * (one fused multiply-add) and rounded to the nearest bf16, ties to even;
-   * that stored value is the momentum whose norm and Newton-Schulz update
-   * the step uses. Cuts the momentum pass from 12 to 8 bytes per parameter
+  /* M is stored in bf16: the new momentum is the exact beta*M + G (beta
+   * as the fp32 value passed) rounded once to the nearest bf16, ties to
+   * even; that stored value is the momentum whose norm and Newton-Schulz
+   * update the step uses. Cuts the momentum pass from 12 to 8 bytes per parameter
    * (6 with MUONH_GRAD_BF16). */
   MUONH_MOM_BF16 = 8u
 };
@@ -152,7 +153,7 @@ size_t muonh_workspace_bytes(const muonh_plan* plan);
 
 /*
  * R[i] <- ||W[i]||_F for every matrix (fp32 result of a fixed-order
- * reduction: fp32 squares within a block, fp64 across blocks). Capture the
+ * reduction: squares summed 4 at a time in fp32, fp64 beyond that). Capture the
  * radius once, from the initial weights. Deterministic.
  * Errors: MUONH_EINVAL (null plan/W/R), MUONH_EWORKSPACE, MUONH_EHIP.
  */
@@ -270,6 +271,23 @@ enum {
 };
 int muonh_step_status(const muonh_plan* plan, const void* workspace, size_t workspace_bytes,
                       void* stream, uint32_t* flags);
+
+/*
+ * Check that no two of the plan's W, G and M matrices overlap in memory
+ * (model card "Puro", section "Training": the step updates W and M in place,
+ * so W, G and M must be distinct storage). W, G and M are HOST arrays of
+ * n_matrices DEVICE pointers: the values the caller puts into the device
+ * pointer arrays it passes to muonh_step. Each matrix spans rows*cols
+ * elements of its storage type (W fp32; G and M fp32 or bf16 by plan flag).
+ * Host-only: no HIP call, nothing enqueued, and no pointer is dereferenced.
+ * muonh_step itself cannot check this (its pointer arrays live in device
+ * memory); a caller whose pointers change calls this before the step.
+ * O(n log n) in the number of matrices.
+ * Errors: MUONH_EINVAL (NULL plan or array), MUONH_EALIAS (the message names
+ * the first overlapping pair, e.g. "G[3] overlaps W[3]"), MUONH_ENOMEM.
+ */
+int muonh_check_disjoint(const muonh_plan* plan, const void* const* W, const void* const* G,
+                         const void* const* M);
 
 /* Static description of a status code. */
 const char* muonh_status_string(int status);

@@ -21,6 +21,8 @@ the matrix group. Gradients and momenta may be float32 or bfloat16 tensors
 from __future__ import annotations
 
 import ctypes
+import re
+from collections import OrderedDict
 from pathlib import Path
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -34,6 +36,7 @@ MUONH_ESHAPE = -2
 MUONH_EWORKSPACE = -3
 MUONH_EHIP = -4
 MUONH_ENOMEM = -5
+MUONH_EALIAS = -6
 MUONH_NS_FP32 = 1
 MUONH_NS_SPLIT_BF16 = 2
 MUONH_GRAD_BF16 = 4
@@ -52,20 +55,23 @@ ADAMW_MAX_TENSORS_PER_LAUNCH = 128
 NS_COEFFS = (3.4445, -4.7750, 2.0315)
 
 
-def find_overlap(spans):
-    """First pair of overlapping byte ranges among `spans`, a list of
-    (start, end, label) with end exclusive; None if they are disjoint."""
-    order = sorted(s for s in spans if s[1] > s[0])
-    for prev, cur in zip(order, order[1:]):
-        if cur[0] < prev[1]:
-            return prev[2], cur[2]
-    return None
-
-
 class MuonHError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"muonh error {status}: {message}")
         self.status = status
+
+
+class MuonHAliasError(MuonHError, ValueError):
+    """MUONH_EALIAS: two of the W, G, M tensors overlap in memory."""
+
+    def __init__(self, message: str):
+        super().__init__(MUONH_EALIAS, message)
+
+
+# Device pointer arrays kept per pointer tuple (a least-recently-used cache):
+# a training loop that cycles through a few gradient buffers uploads each
+# array once.
+PTR_CACHE_ENTRIES = 64
 
 
 class GroupDesc(ctypes.Structure):
@@ -99,6 +105,7 @@ def _load_library() -> ctypes.CDLL:
         "muonh_adamw_step": (ctypes.c_int, [i32, vp, vp, vp, vp, vp, f32, f32, f32, f32, f32,
                                             i32, vp]),
         "muonh_step_status": (ctypes.c_int, [vp, vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]),
+        "muonh_check_disjoint": (ctypes.c_int, [vp, vp, vp, vp]),
         "muonh_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "muonh_last_error": (ctypes.c_char_p, []),
     }
@@ -189,6 +196,36 @@ class Plan:
             self.handle = None
 
 
+class _PtrArrays:
+    """Device arrays of device pointers, one per pointer tuple, kept in a
+    least-recently-used cache of PTR_CACHE_ENTRIES. A new array is copied
+    from pinned host memory without blocking (the copy is ordered on the
+    current stream before the launch that reads it; torch keeps the pinned
+    buffer until the copy is done), so changing pointers never waits for
+    the GPU. Each use records the current stream on the array, so that an
+    array evicted while a launch on another stream still reads it is not
+    reused before that launch completes."""
+
+    def __init__(self, torch, device):
+        self.torch = torch
+        self.device = device
+        self.cache: "OrderedDict" = OrderedDict()
+
+    def get(self, ptrs: Tuple[int, ...]) -> int:
+        torch = self.torch
+        arr = self.cache.get(ptrs)
+        if arr is None:
+            host = torch.tensor(ptrs, dtype=torch.int64).pin_memory()
+            arr = host.to(self.device, non_blocking=True)
+            self.cache[ptrs] = arr
+            if len(self.cache) > PTR_CACHE_ENTRIES:
+                self.cache.popitem(last=False)
+        else:
+            self.cache.move_to_end(ptrs)
+        arr.record_stream(torch.cuda.current_stream(self.device))
+        return int(arr.data_ptr())
+
+
 class MuonH:
     """MuonH over a list of fp32 weight matrices on one GPU.
 
@@ -228,8 +265,8 @@ class MuonH:
         if self.workspace.data_ptr() % 256:
             raise MuonHError(MUONH_EWORKSPACE, "torch returned a workspace that is not 256-aligned")
         self.R = torch.zeros(len(self.shapes), dtype=torch.float32, device=self.device)
-        self._ptr_cache: Dict[str, Tuple[Tuple[int, ...], object]] = {}
-        self._disjoint_ok: set = set()  # (W, G, M) pointer tuples already checked
+        self._ptrs = _PtrArrays(torch, self.device)
+        self._disjoint_ok: "OrderedDict" = OrderedDict()  # (W, G, M) pointer tuples checked
 
     # -- marshalling ------------------------------------------------------
     def _check(self, tensors, name: str):
@@ -247,31 +284,39 @@ class MuonH:
 
     def _check_state(self, weights, grads, moms):
         """Types and shapes of W, G and M, and that no two of their tensors
-        overlap in memory (the step updates W and M in place and reads G;
-        checked on the host, once per combination of pointers)."""
+        overlap in memory (the step updates W and M in place and reads G).
+        The library checks the byte ranges on the host
+        (muonh_check_disjoint), once per combination of pointers; an overlap
+        raises MuonHAliasError (a ValueError) naming the caller's tensors."""
         self._check(weights, "weights")
         self._check(grads, "grads")
         self._check(moms, "moms")
-        key = tuple(tuple(int(t.data_ptr()) for t in ts) for ts in (weights, grads, moms))
+        ptrs = [tuple(int(ts[c].data_ptr()) for c in self.plan_order)
+                for ts in (weights, grads, moms)]
+        key = tuple(ptrs)
         if key in self._disjoint_ok:
+            self._disjoint_ok.move_to_end(key)
             return
-        spans = [(int(t.data_ptr()), int(t.data_ptr()) + t.numel() * t.element_size(), f"{nm}[{i}]")
-                 for nm, ts in (("weights", weights), ("grads", grads), ("moms", moms))
-                 for i, t in enumerate(ts)]
-        hit = find_overlap(spans)
-        if hit is not None:
-            raise ValueError(f"{hit[0]} and {hit[1]} overlap in memory; W, G and M must be disjoint")
-        if len(self._disjoint_ok) >= 64:
-            self._disjoint_ok.clear()
-        self._disjoint_ok.add(key)
+        arrs = [(ctypes.c_void_p * len(p))(*p) for p in ptrs]
+        st = get_lib().muonh_check_disjoint(self.plan.handle, *arrs)
+        if st == MUONH_EALIAS:
+            raise MuonHAliasError(self._caller_names(get_lib().muonh_last_error().decode()))
+        check(st)
+        self._disjoint_ok[key] = True
+        if len(self._disjoint_ok) > PTR_CACHE_ENTRIES:
+            self._disjoint_ok.popitem(last=False)
+
+    def _caller_names(self, msg: str) -> str:
+        """The library names matrices by plan index ("G[3] overlaps W[3]");
+        translate to the caller's lists and indices."""
+        names = {"W": "weights", "G": "grads", "M": "moms"}
+
+        def repl(m):
+            return f"{names[m.group(1)]}[{self.plan_order[int(m.group(2))]}]"
+        return re.sub(r"\b([WGM])\[(\d+)\]", repl, msg) + "; W, G and M must be disjoint"
 
     def _ptr_array(self, name: str, tensors) -> int:
-        ptrs = tuple(int(tensors[c].data_ptr()) for c in self.plan_order)
-        cached = self._ptr_cache.get(name)
-        if cached is None or cached[0] != ptrs:
-            arr = self.torch.tensor(ptrs, dtype=self.torch.int64).to(self.device)
-            self._ptr_cache[name] = (ptrs, arr)
-        return int(self._ptr_cache[name][1].data_ptr())
+        return self._ptrs.get(tuple(int(tensors[c].data_ptr()) for c in self.plan_order))
 
     def _stream(self) -> int:
         return int(self.torch.cuda.current_stream(self.device).cuda_stream)
@@ -358,9 +403,9 @@ class MuonH:
 
 __all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
            "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
-           "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_NS_FP32", "MUONH_NS_SPLIT_BF16", "MUONH_GRAD_BF16",
+           "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_EALIAS", "MuonHAliasError", "MUONH_NS_FP32", "MUONH_NS_SPLIT_BF16", "MUONH_GRAD_BF16",
            "MUONH_MOM_BF16", "MUONH_NONFINITE_MOMENTUM", "MUONH_NONFINITE_UPDATE", "AdamW",
-           "find_overlap"]
+           "PTR_CACHE_ENTRIES"]
 
 
 class AdamW:
@@ -384,7 +429,7 @@ class AdamW:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.device = dev
         self._sizes = (ctypes.c_int64 * max(len(self.numels), 1))(*self.numels)
-        self._ptr_cache: Dict[str, Tuple[Tuple[int, ...], object]] = {}
+        self._ptrs = _PtrArrays(torch, self.device)
 
     def _check(self, tensors, name: str):
         torch = self.torch
@@ -399,12 +444,7 @@ class AdamW:
                 raise ValueError(f"{name}[{i}] must be contiguous with {self.numels[i]} elements")
 
     def _ptr_array(self, name: str, tensors) -> int:
-        ptrs = tuple(int(t.data_ptr()) for t in tensors)
-        cached = self._ptr_cache.get(name)
-        if cached is None or cached[0] != ptrs:
-            arr = self.torch.tensor(ptrs, dtype=self.torch.int64).to(self.device)
-            self._ptr_cache[name] = (ptrs, arr)
-        return int(self._ptr_cache[name][1].data_ptr())
+        return self._ptrs.get(tuple(int(t.data_ptr()) for t in tensors))
 
     def step(self, params, grads, exp_avg, exp_avg_sq, lr: float, beta1: float = 0.9,
              beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.1,

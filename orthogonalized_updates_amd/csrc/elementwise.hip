@@ -6,9 +6,12 @@
 // fp32. Every kernel is one grouped launch over the matrices of up to 16
 // shape groups; blocks stream contiguous chunks with 16-byte accesses
 // (8-byte for bf16 G and M), non-temporal on the M and W streams. Norms are
-// deterministic two-level reductions: fp32 per thread, a fixed shuffle tree
-// in fp64 per block, then a fixed-order fp64 sum of the per-block partials
-// in a separate finalize kernel (no float atomics).
+// deterministic reductions: each 4 squares summed in fp32 (relative error at
+// most a few fp32 ulps, every term being positive), an fp64 running sum per
+// thread, a fixed shuffle tree in fp64 per block, then a fixed-order fp64 sum
+// of the per-block partials in a separate finalize kernel (no float atomics).
+// So a norm's relative error stays below about 3e-7 however many entries a
+// matrix has.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,6 +28,12 @@ __device__ __forceinline__ int group_of_block(const EwArgs& a, int b) {
     if (b >= a.g[i].block_begin) gi = i;
   return gi;
 }
+
+// Sum of the squares of 4 values in fp32, widened for an fp64 running sum.
+__device__ __forceinline__ double sq4(float4 v) {
+  return (double)fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
+}
+__device__ __forceinline__ double sq1(float v) { return (double)v * (double)v; }
 
 // Fixed-order block sum; the result is valid in thread 0.
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -99,16 +108,50 @@ __device__ __forceinline__ float4 widen4(uint2 u) {
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+// beta*m + g rounded once to the nearest bf16 (ties to even), for a bf16 m:
+// the value a bf16 momentum stores. beta*m has at most 24 + 8 significant
+// bits, so the fp64 product is exact; the fp64 sum s is rounded and its
+// error e recovered exactly (two-sum: s + e = beta*m + g). The step to fp32
+// then rounds to odd (keep the value truncated toward zero, and set its last
+// bit when anything was dropped), which leaves the final rounding to bf16,
+// 16 bits shorter, the same as rounding the exact value. A plain fp32 fma
+// followed by a bf16 conversion would round twice.
+__device__ __forceinline__ float mom_bf16(float beta, float m, float g) {
+  const double p = (double)beta * (double)m;
+  const double gd = (double)g;
+  const double s = p + gd;
+  if (!isfinite(s)) return (float)(__bf16)(float)s;  // inf, NaN
+  const double bv = s - p;
+  const double e = (p - (s - bv)) + (gd - bv);
+  const float r = (float)s;  // nearest
+  const double rd = (double)r;
+  uint32_t t = __float_as_uint(r);
+  bool inexact = true;
+  if (rd == s) {
+    // s is an fp32 value: the exact sum lies beyond it (e with the sign of
+    // s, truncation keeps r) or before it (truncation is r's predecessor)
+    if (e == 0.0) inexact = false;
+    else if ((e < 0.0) != (s < 0.0)) t -= 1u;
+  } else if (fabs(rd) > fabs(s)) {
+    t -= 1u;  // r was rounded away from zero (an fp32 overflow included)
+  }
+  if (inexact) t |= 1u;
+  return (float)(__bf16)__uint_as_float(t);
+}
+
 // Storage of the gradient and the momentum: fp32, or bf16 (BF). Element i of
 // a flat array; load4/load4_nt/store4_nt take 4 consecutive elements from i
-// (a multiple of 4, the address aligned to kVecAlign). A bf16 store rounds to
-// nearest even and returns the value stored, so that what the caller goes on with
-// (the norm, the cast) is exactly the stored momentum.
+// (a multiple of 4, the address aligned to kVecAlign). mom(beta, m, g) is the
+// new momentum as stored: one fp32 fma, or for bf16 storage the exact value
+// rounded once to bf16 (mom_bf16); the stores then write it unchanged, so
+// that what the caller goes on with (the norm, the cast) is exactly the
+// stored momentum.
 template <bool BF>
 struct St;
 template <>
 struct St<false> {
   static constexpr unsigned kVecAlign = 16;
+  __device__ static float mom(float beta, float m, float g) { return fmaf(beta, m, g); }
   __device__ static float load(const void* p, int64_t i) {
     return ((const MUONH_GLOBAL float*)p)[i];
   }
@@ -130,6 +173,7 @@ struct St<false> {
 template <>
 struct St<true> {
   static constexpr unsigned kVecAlign = 8;
+  __device__ static float mom(float beta, float m, float g) { return mom_bf16(beta, m, g); }
   __device__ static float load(const void* p, int64_t i) {
     return __uint_as_float((uint32_t)((const MUONH_GLOBAL uint16_t*)p)[i] << 16);
   }
@@ -170,22 +214,16 @@ __global__ __launch_bounds__(kThreads) void k_sumsq(EwArgs a, float* const* W, d
   const float* w = W[mat];
   int64_t lo, hi;
   chunk_range(g.n, g.bpm, c, lo, hi);
-  float acc = 0.f;
+  double acc = 0.0;
   int64_t mid = lo;
   if (aligned16(w)) {
     const int64_t n4 = (hi - lo) >> 2;
     const float4* w4 = reinterpret_cast<const float4*>(w + lo);
-    for (int64_t i = threadIdx.x; i < n4; i += kThreads) {
-      const float4 v = w4[i];
-      acc = fmaf(v.x, v.x, acc);
-      acc = fmaf(v.y, v.y, acc);
-      acc = fmaf(v.z, v.z, acc);
-      acc = fmaf(v.w, v.w, acc);
-    }
+    for (int64_t i = threadIdx.x; i < n4; i += kThreads) acc += sq4(w4[i]);
     mid = lo + (n4 << 2);
   }
-  for (int64_t e = mid + threadIdx.x; e < hi; e += kThreads) acc = fmaf(w[e], w[e], acc);
-  const double t = block_sum((double)acc, red);
+  for (int64_t e = mid + threadIdx.x; e < hi; e += kThreads) acc += sq1(w[e]);
+  const double t = block_sum(acc, red);
   if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = t;
 }
 
@@ -207,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const void* con
   void* mp = M[mat];
   int64_t lo, hi;
   chunk_range(g.n, g.bpm, c, lo, hi);
-  float acc = 0.f;
+  double acc = 0.0;
   int64_t mid = lo;
   if (vec_aligned<GB>(gp) && vec_aligned<MB>(mp)) {
     const int64_t n4 = (hi - lo) >> 2;
@@ -215,23 +253,20 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const void* con
       const int64_t e = lo + 4 * i;
       const float4 gv = St<GB>::load4(gp, e);
       float4 mv = St<MB>::load4_nt(mp, e);
-      mv.x = fmaf(beta, mv.x, gv.x);
-      mv.y = fmaf(beta, mv.y, gv.y);
-      mv.z = fmaf(beta, mv.z, gv.z);
-      mv.w = fmaf(beta, mv.w, gv.w);
+      mv.x = St<MB>::mom(beta, mv.x, gv.x);
+      mv.y = St<MB>::mom(beta, mv.y, gv.y);
+      mv.z = St<MB>::mom(beta, mv.z, gv.z);
+      mv.w = St<MB>::mom(beta, mv.w, gv.w);
       mv = St<MB>::store4_nt(mp, e, mv);
-      acc = fmaf(mv.x, mv.x, acc);
-      acc = fmaf(mv.y, mv.y, acc);
-      acc = fmaf(mv.z, mv.z, acc);
-      acc = fmaf(mv.w, mv.w, acc);
+      acc += sq4(mv);
     }
     mid = lo + (n4 << 2);
   }
   for (int64_t e = mid + threadIdx.x; e < hi; e += kThreads) {
-    const float v = St<MB>::store(mp, e, fmaf(beta, St<MB>::load(mp, e), St<GB>::load(gp, e)));
-    acc = fmaf(v, v, acc);
+    const float v = St<MB>::store(mp, e, St<MB>::mom(beta, St<MB>::load(mp, e), St<GB>::load(gp, e)));
+    acc += sq1(v);
   }
-  const double t = block_sum((double)acc, red);
+  const double t = block_sum(acc, red);
   if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = t;
 }
 
@@ -339,13 +374,13 @@ struct Fmt<kFp32> {
 // call it (it synchronises when E is written).
 // --------------------------------------------------------------------------
 template <int F, bool kMomentum, bool GB, bool MB>
-__device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const void* gp, void* mp,
+__device__ __forceinline__ double cast_tile(const EwGroup& g, char* blk, const void* gp, void* mp,
                                            float beta, int r0, int c0, float scale,
                                            float (*tile)[65]) {
   const int tx = (threadIdx.x & 15) << 2, ty = threadIdx.x >> 4;
   const bool vec = (g.cols & 3) == 0 && vec_aligned<MB>(mp) && (!kMomentum || vec_aligned<GB>(gp));
   const bool trans = g.offE >= 0;
-  float acc = 0.f;
+  double acc = 0.0;
   if (trans) __syncthreads();  // the previous tile's transposed reads are done
   // The vector loads of all four rows are issued before the first store.
   const int c = c0 + tx;
@@ -376,10 +411,10 @@ __device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const vo
       if (cvec) {
         v = mv[i];
         if (kMomentum) {
-          v.x = fmaf(beta, v.x, gv[i].x);
-          v.y = fmaf(beta, v.y, gv[i].y);
-          v.z = fmaf(beta, v.z, gv[i].z);
-          v.w = fmaf(beta, v.w, gv[i].w);
+          v.x = St<MB>::mom(beta, v.x, gv[i].x);
+          v.y = St<MB>::mom(beta, v.y, gv[i].y);
+          v.z = St<MB>::mom(beta, v.z, gv[i].z);
+          v.w = St<MB>::mom(beta, v.w, gv[i].w);
           v = St<MB>::store4_nt(mp, i0, v);
         }
       } else {
@@ -388,19 +423,14 @@ __device__ __forceinline__ float cast_tile(const EwGroup& g, char* blk, const vo
         for (int q = 0; q < 4; ++q) {
           if (c + q < g.cols) {
             float m = St<MB>::load(mp, i0 + q);
-            if (kMomentum) m = St<MB>::store(mp, i0 + q, fmaf(beta, m, St<GB>::load(gp, i0 + q)));
+            if (kMomentum) m = St<MB>::store(mp, i0 + q, St<MB>::mom(beta, m, St<GB>::load(gp, i0 + q)));
             e[q] = m;
           }
         }
         v = make_float4(e[0], e[1], e[2], e[3]);
       }
     }
-    if (kMomentum) {
-      acc = fmaf(v.x, v.x, acc);
-      acc = fmaf(v.y, v.y, acc);
-      acc = fmaf(v.z, v.z, acc);
-      acc = fmaf(v.w, v.w, acc);
-    }
+    if (kMomentum) acc += sq4(v);
     v.x *= scale;
     v.y *= scale;
     v.z *= scale;
@@ -459,17 +489,18 @@ __global__ __launch_bounds__(kThreads) void k_momentum_cast(EwArgs a, const void
   char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
   const int tcols = g.cp >> 6;
   const int t1 = min((c + 1) * g.tpb, g.tiles_per_mat);
-  float acc = 0.f;
+  double acc = 0.0;
   for (int t = c * g.tpb; t < t1; ++t) {
     const int r0 = (t / tcols) << 6, c0 = (t - (t / tcols) * tcols) << 6;
     acc += cast_tile<F, true, GB, MB>(g, blk, G[mat], M[mat], beta, r0, c0, 1.f, tile);
   }
-  const double tot = block_sum((double)acc, red);
+  const double tot = block_sum(acc, red);
   if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = tot;
 }
 
 // Fallback of the deferred normalisation: 8 blocks per matrix; for the
-// matrices whose norm fails xnorm_deferred they rewrite X0 normalised.
+// matrices whose norm fails xnorm_deferred, and for every matrix of a group
+// that never defers, they rewrite X0 normalised.
 template <int F, bool MB>
 __global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const void* const* M,
                                                             const double* norms) {
@@ -481,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_fallback(EwArgs a, const void
   const int m = b >> 3, j = b & 7;
   const int mat = g.first + m;
   const double n = norms[mat];
-  if (xnorm_deferred(n)) return;  // uniform for the block
+  if (g.defer && xnorm_deferred(n)) return;  // uniform for the block
   const float scale = (float)(1.0 / (n + kNsEps));
   char* blk = g.ns_base + (int64_t)m * g.mat_bytes;
   const int tcols = g.cp >> 6;
@@ -521,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
     const double nrm = norms[mat];
     scale = nrm > 0.0 ? (float)((double)R[mat] / nrm) : 1.f;
   }
-  float acc = 0.f;
+  double acc = 0.0;
   const int cols = g.cols;
   if ((cols & 3) == 0 && aligned16(w)) {
     // Work unit: 4 consecutive columns of the row pair (2p, 2p + 1). The two
@@ -586,12 +617,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
           if (kProject) {
             v.x *= scale; v.y *= scale; v.z *= scale; v.w *= scale;
           }
-          if (!kWrite && live[j][h]) {
-            acc = fmaf(v.x, v.x, acc);
-            acc = fmaf(v.y, v.y, acc);
-            acc = fmaf(v.z, v.z, acc);
-            acc = fmaf(v.w, v.w, acc);
-          }
+          if (!kWrite && live[j][h]) acc += sq4(v);
           wv[j][h] = v;
         }
       // Unconditional stores: a slot past the end holds the address and the
@@ -619,12 +645,12 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
       if (kWrite) {
         w[e] = kProject ? v * scale : v;
       } else {
-        acc = fmaf(v, v, acc);
+        acc += sq1(v);
       }
     }
   }
   if (!kWrite) {
-    const double t = block_sum((double)acc, red);
+    const double t = block_sum(acc, red);
     if (threadIdx.x == 0) partials[(int64_t)mat * kMaxPartials + c] = t;
   }
 }

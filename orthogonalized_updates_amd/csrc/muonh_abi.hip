@@ -5,8 +5,9 @@
 //   bf16 or split operands with ns_iters >= 1:
 //     momentum + cast (M <- beta M + G stored, Y = M unscaled in the
 //     operand layout, partial ||M||^2) -> finalize ||M|| -> cast fallback
-//     (rewrites X0 normalised only for norms outside [2^-40, 2^40]); the
-//     first Gram and apply then scale by 1/(||M||+eps)
+//     (rewrites X0 normalised for norms outside [2^-40, 2^40] and for
+//     matrices of at most 65536 entries); the first Gram and apply then
+//     scale the others by 1/(||M||+eps)
 //   otherwise: momentum -> finalize -> normcast (X0 = M/(||M||+eps))
 //   ns_iters x { Gram A = X X^T ; Poly B = bA + cAA ; Apply X <- aX + BX }
 //   MuonH: update (partial ||W - lr O||^2) -> finalize -> project
@@ -185,6 +186,7 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, EwKind kind, int ns_i
         e.offE = G.trans ? x0 : -1;
       }
       e.tiles_per_mat = (rp / 64) * (cp / 64);
+      e.defer = G.n > kDeferMinElems;
       e.tpb = 1;
       if (kind == kEwFused) {
         e.tpb = (e.tiles_per_mat + kMaxPartials - 1) / kMaxPartials;
@@ -219,6 +221,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     q.count = G.count;
     q.first = G.first;
     q.offE = q.offO1 = q.offO2 = -1;
+    q.defer = G.n > kDeferMinElems;
     const int ts = G.sp / T, tl = G.lp / T;
     const int64_t xcur = p->prec == kFp32 ? G.offX : G.offXs[src];
     if (mode == kGram) {
@@ -377,11 +380,55 @@ const char* muonh_status_string(int status) {
     case MUONH_EWORKSPACE: return "invalid workspace";
     case MUONH_EHIP: return "HIP runtime error";
     case MUONH_ENOMEM: return "out of host memory";
+    case MUONH_EALIAS: return "overlapping matrices";
     default: return "unknown status";
   }
 }
 
 const char* muonh_last_error(void) { return g_last_error.c_str(); }
+
+int muonh_check_disjoint(const muonh_plan* plan, const void* const* W, const void* const* G,
+                         const void* const* M) {
+  if (!plan) return fail(MUONH_EINVAL, "plan is NULL");
+  if (!W || !G || !M) return fail(MUONH_EINVAL, "W, G and M must be host arrays of pointers");
+  struct Span {
+    uintptr_t lo, hi;
+    int kind;   // 0 W, 1 G, 2 M
+    int64_t index;
+  };
+  std::vector<Span> spans;
+  try {
+    spans.reserve((size_t)plan->n_mats * 3);
+  } catch (...) {
+    return fail(MUONH_ENOMEM, "host allocation failed");
+  }
+  const uintptr_t gsz = plan->sf.g_bf16 ? 2 : 4, msz = plan->sf.m_bf16 ? 2 : 4;
+  for (const GroupPlan& g : plan->groups)
+    for (int i = 0; i < g.count; ++i) {
+      const int64_t k = g.first + i;
+      const uintptr_t n = (uintptr_t)g.n;
+      const void* const* arr[3] = {W, G, M};
+      const uintptr_t esz[3] = {4, gsz, msz};
+      for (int t = 0; t < 3; ++t) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(arr[t][k]);
+        spans.push_back(Span{lo, lo + n * esz[t], t, k});
+      }
+    }
+  std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) {
+    return a.lo != b.lo ? a.lo < b.lo : a.hi < b.hi;
+  });
+  // sorted by start: an overlap exists iff some span starts before the
+  // furthest end seen so far
+  static const char* const kName[3] = {"W", "G", "M"};
+  size_t far = 0;
+  for (size_t i = 1; i < spans.size(); ++i) {
+    if (spans[i].lo < spans[far].hi)
+      return fail(MUONH_EALIAS, "%s[%lld] overlaps %s[%lld]", kName[spans[i].kind],
+                  (long long)spans[i].index, kName[spans[far].kind], (long long)spans[far].index);
+    if (spans[i].hi > spans[far].hi) far = i;
+  }
+  return MUONH_OK;
+}
 
 int muonh_plan_create(muonh_plan** out, const muonh_group_desc* groups, int32_t n_groups,
                       uint32_t flags) {

@@ -48,11 +48,16 @@ __host__ __device__ inline bool xnorm_deferred(double n) {
 __host__ __device__ inline float x0_sigma(double n) {
   return xnorm_deferred(n) ? (float)(1.0 / (n + kNsEps)) : 1.f;
 }
+// Matrices of at most this many entries never defer: their X0 is rounded
+// after the normalisation, in the order of the step's definition. For them
+// the extra read of M costs nothing measurable, and with only a few singular
+// values the place of the rounding shows in the result.
+constexpr int64_t kDeferMinElems = 65536;
 
 // Storage of the gradient and the momentum (plan flags MUONH_GRAD_BF16 and
-// MUONH_MOM_BF16): fp32, or bf16. A bf16 momentum is stored rounded to
-// nearest even from the fp32 fma result, and the stored value is the one the
-// norm and Newton-Schulz see.
+// MUONH_MOM_BF16): fp32, or bf16. A bf16 momentum is the exact beta*M + G
+// rounded once to the nearest bf16 (ties to even), and the stored value is
+// the one the norm and Newton-Schulz see.
 struct StateFmt {
   bool g_bf16 = false;
   bool m_bf16 = false;
@@ -83,6 +88,8 @@ struct EwGroup {
   int64_t offD, offE;
   int rp, cp;           // padded rows / cols
   int tiles_per_mat;    // 64x64 tiles of the padded rp x cp domain
+  int defer;            // 1: X0's normalisation may be deferred (more than
+                        // kDeferMinElems entries)
 };
 
 struct EwArgs {
@@ -107,8 +114,9 @@ hipError_t launch_normcast(const EwArgs& a, NsPrec prec, StateFmt sf, const void
 // to D / E as X0 would be (tile launch; bpm blocks of tpb tiles per matrix).
 hipError_t launch_momentum_cast(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* G,
                                 void* const* M, float beta, double* partials, hipStream_t s);
-// For the matrices whose norm fails xnorm_deferred: X0 = M / (norm + eps)
-// written as launch_normcast would (8 blocks per matrix; the others return).
+// For the matrices whose norm fails xnorm_deferred, and every matrix of the
+// groups that never defer: X0 = M / (norm + eps) written as launch_normcast
+// would (8 blocks per matrix; the others return).
 hipError_t launch_cast_fallback(const EwArgs& a, NsPrec prec, StateFmt sf, const void* const* M,
                                 const double* norms, hipStream_t s);
 hipError_t launch_update_norm(const EwArgs& a, NsPrec prec, float* const* W, float lr,
@@ -146,6 +154,7 @@ struct GemmGroup {
   int tile_begin;
   int count;
   int first;            // global index of the group's first matrix
+  int defer;            // 1: the group's X0 may be unscaled (see EwGroup)
 };
 
 struct GemmArgs {

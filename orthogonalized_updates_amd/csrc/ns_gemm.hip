@@ -800,7 +800,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
   // The first iteration after the fused momentum + cast sees X0 unscaled:
   // A = sigma^2 Y Y^T, and the apply's a*Y + B*Y takes sigma.
   float scale = MODE == kPoly ? args.c1 : 1.f;
-  if (MODE != kPoly && args.xnorm) {
+  if (MODE != kPoly && args.xnorm && g.defer) {
     const float sg = x0_sigma(args.xnorm[g.first + mat]);
     scale = MODE == kGram ? sg * sg : sg;
   }
@@ -1164,7 +1164,7 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
     pingpong16<1, MODE != kGram, kQT, 2>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wnc, o, lane, bi, seed, acc);
 
   float scale = MODE == kPoly ? args.c1 : 1.f;
-  if (MODE != kPoly && args.xnorm) {
+  if (MODE != kPoly && args.xnorm && g.defer) {
     const float sg = x0_sigma(args.xnorm[g.first + mat]);
     scale = MODE == kGram ? sg * sg : sg;
   }

@@ -12,9 +12,12 @@ fmt="split_bf16" emulates the split storage instead: a stored value v is
 hi + lo with hi = bf16(v) and lo = bf16(v - hi) (the difference taken in
 fp32), and a product of two split operands omits lo*lo.
 
-deferred=True (the GPU path with at least one iteration) stores M itself
+By default the emulation follows the definition's order: X0 = M/(||M|| + eps)
+is rounded after the normalisation. deferred=True instead stores M itself
 rounded and folds 1/(||M|| + eps) into the first Gram (squared) and the
-first apply, for norms in [2^-40, 2^40] (or 0), as the kernels do.
+first apply, for norms in [2^-40, 2^40] (or 0); with fmt="exact" that checks
+that the rescheduled algebra equals the definition. The parity bars never
+use deferred=True.
 """
 from __future__ import annotations
 
@@ -46,7 +49,7 @@ def _deferred(n: float) -> bool:
     return n == 0.0 or 2.0 ** -40 <= n <= 2.0 ** 40
 
 
-def _ns_emulated(m, k: int, fmt: str, deferred: bool = True) -> np.ndarray:
+def _ns_emulated(m, k: int, fmt: str, deferred: bool = False) -> np.ndarray:
     if fmt == "bf16":
         def store(v):
             r = round_bf16(v)
@@ -104,7 +107,7 @@ def ns_split_bf16(m, k: int) -> np.ndarray:
     return _ns_emulated(m, k, "split_bf16")
 
 
-def floor(m, k: int, reference, fmt: str = "bf16", deferred: bool = True) -> float:
+def floor(m, k: int, reference, fmt: str = "bf16", deferred: bool = False) -> float:
     """Relative Frobenius error of the emulated iteration vs `reference`."""
     e = _ns_emulated(m, k, fmt, deferred)
     nr = np.linalg.norm(reference)

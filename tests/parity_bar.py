@@ -1,0 +1,192 @@
+"""The bar the GPU parity tests hold the HIP path to, against the fp64 oracle,
+and the host side that checks it (test tooling, not the oracle).
+
+Update O (the orthogonalized momentum):
+  * relative Frobenius error of the whole matrix <= TOL_O[prec]: 2e-2 with
+    bf16 operands (the tolerance the method's specification states for bf16
+    MFMA at 5 iterations), 5e-4 with split-bf16 operands (derived: a hi + lo
+    pair carries about 16 significant bits against bf16's 8, so its floor
+    is about 2^-8 of bf16's), 1e-5 in fp32 mode (stated);
+  * and the same bound on every 256 x 256 tile of O (in the matrix's own
+    orientation) that has at least 4096 entries, so that one wrong block
+    cannot hide in a whole-matrix number;
+  * one exception, printed when used: for the explicit TINY_SHAPES, whose
+    Newton-Schulz has one to five singular values and at most 64 entries,
+    bf16 storage alone can cost more than 2e-2 (no averaging), so the bar
+    of the whole matrix is the larger of TOL_O and 1.3x the error of a bf16
+    emulation of the iteration in the definition's own order (X0 rounded
+    after the normalisation; tests/bf16_floor.py). These matrices have no
+    tile of 4096 entries. The library rounds them in that same order.
+bf16 at 8 iterations does not meet 2e-2 (its floor is about 2.1e-2 to
+2.5e-2): the tests that ask for it are marked xfail(strict=True).
+
+Momentum M: <= 1e-6 relative (one fp32 fma per element against fp64); a
+bf16 momentum must equal the oracle's bit for bit.
+Weights W: within 2e-6 (relative Frobenius) of the oracle's projection of the
+GPU's own O (this isolates the elementwise phases from the Newton-Schulz
+rounding), and within the first-order bound of the oracle's full step:
+W = R W'/||W'|| with W' = W - lr O moves by at most R lr ||dO|| / ||W'|| when
+O moves by dO, so ||dW||/R <= 1.5 lr ||dO|| / ||W'|| + 1e-6.
+Sphere: | ||W||_F / R - 1 | <= 1e-5 for every matrix (stated).
+"""
+from __future__ import annotations
+
+import os
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import oracle
+from bf16_floor import floor as emulated_floor
+
+TOL_O = {"bf16": 2e-2, "split_bf16": 5e-4, "fp32": 1e-5}
+TINY_SHAPES = frozenset({(1, 1), (3, 5), (5, 3), (1, 64), (64, 1)})
+TILE = 256
+MIN_TILE_ENTRIES = 4096
+
+
+def describe() -> str:
+    return (f"parity bar: O rel err <= {TOL_O} (whole matrix and every 256x256 tile of >= "
+            f"{MIN_TILE_ENTRIES} entries); tiny-shape floor exception only for "
+            f"{sorted(TINY_SHAPES)}")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def tile_errors(o, ref):
+    """(worst relative error, its tile) over the 256 x 256 tiles of `ref`'s
+    shape with at least MIN_TILE_ENTRIES entries; (0.0, None) if none."""
+    o = np.asarray(o, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    worst, where = 0.0, None
+    for r0 in range(0, ref.shape[0], TILE):
+        for c0 in range(0, ref.shape[1], TILE):
+            t = ref[r0:r0 + TILE, c0:c0 + TILE]
+            if t.size < MIN_TILE_ENTRIES:
+                continue
+            e = rel(o[r0:r0 + TILE, c0:c0 + TILE], t)
+            if e > worst:
+                worst, where = e, (r0 // TILE, c0 // TILE)
+    return worst, where
+
+
+def o_errors(o_gpu, o_ref, m_new, k, prec):
+    """Errors of O and the bars they must meet: dict with e_o, bar_o,
+    floor (None unless the tiny-shape exception applies), e_tile, tile."""
+    shape = tuple(np.shape(o_ref))
+    bar = TOL_O[prec]
+    fl = None
+    if prec != "fp32" and shape in TINY_SHAPES:
+        fl = emulated_floor(m_new, k, o_ref, prec)
+        bar = max(bar, 1.3 * fl)
+    e_tile, tile = tile_errors(o_gpu, o_ref)
+    return {"e_o": rel(o_gpu, o_ref), "bar_o": bar, "floor": fl, "e_tile": e_tile, "tile": tile,
+            "bar_tile": TOL_O[prec]}
+
+
+def assert_o(err, label):
+    if err["floor"] is not None and err["bar_o"] > err["bar_tile"]:
+        say(f"{label}: tiny shape, bar {err['bar_o']:.3e} = 1.3 x oracle-order floor "
+            f"{err['floor']:.3e}")
+    assert err["e_o"] <= err["bar_o"], f"{label}: O rel err {err['e_o']:.3e} > {err['bar_o']:.3e}"
+    assert err["e_tile"] <= err["bar_tile"], (
+        f"{label}: O tile {err['tile']} rel err {err['e_tile']:.3e} > {err['bar_tile']:.3e}")
+
+
+def muonh_errors(o_gpu, w_gpu, m_gpu, g, w_pre, m_pre, r, lr, beta, k, prec, mom_bf16=False):
+    """Every error of one teacher-forced MuonH step of one matrix, with its bar."""
+    w_o, m_o, o_o = oracle.muonh_step(w_pre, g, m_pre, r, lr, beta, k, mom_bf16=mom_bf16)
+    err = o_errors(o_gpu, o_o, m_o, k, prec)
+    m_gpu = np.asarray(m_gpu, dtype=np.float64)
+    if mom_bf16:
+        err["m_bad"] = int(np.count_nonzero(m_gpu != m_o))
+    else:
+        err["e_m"] = rel(m_gpu, m_o)
+    err["e_wp"] = rel(w_gpu, oracle.hyperball_project(w_pre, o_gpu, r, lr))
+    err["e_wf"] = rel(w_gpu, w_o)
+    trial = np.linalg.norm(np.asarray(w_pre, dtype=np.float64) - lr * o_o)
+    err["bar_wf"] = 1.5 * lr * np.linalg.norm(np.asarray(o_gpu, np.float64) - o_o) / max(trial, 1e-30) + 1e-6
+    err["e_s"] = abs(np.linalg.norm(np.asarray(w_gpu, dtype=np.float64)) / r - 1.0) if r > 0 else 0.0
+    return err
+
+
+def assert_muonh(err, label):
+    assert_o(err, label)
+    if "m_bad" in err:
+        assert err["m_bad"] == 0, f"{label}: {err['m_bad']} bf16 momentum elements differ"
+    else:
+        assert err["e_m"] <= 1e-6, f"{label}: M rel err {err['e_m']:.3e}"
+    assert err["e_wp"] <= 2e-6, f"{label}: W vs projection of GPU O {err['e_wp']:.3e}"
+    assert err["e_wf"] <= err["bar_wf"], f"{label}: W vs oracle step {err['e_wf']:.3e} > {err['bar_wf']:.3e}"
+    assert err["e_s"] <= 1e-5, f"{label}: ||W||/R - 1 = {err['e_s']:.3e}"
+
+
+def muon_wd_errors(o_gpu, w_gpu, m_gpu, g, w_pre, m_pre, lr, beta, wd, k, prec, mom_bf16=False):
+    """Errors of one teacher-forced Muon step with decoupled weight decay.
+    W against the decayed update of the GPU's own O within
+    1e-6 (||W|| + lr ||O||) (a few ulps of each term: on small matrices the
+    two terms can cancel, so the bound is relative to them), and against the
+    oracle's full step within 1.5 lr ||dO|| plus that."""
+    w_o, m_o, o_o = oracle.muon_wd_step(w_pre, g, m_pre, lr, beta, wd, k, mom_bf16=mom_bf16)
+    err = o_errors(o_gpu, o_o, m_o, k, prec)
+    m_gpu = np.asarray(m_gpu, dtype=np.float64)
+    if mom_bf16:
+        err["m_bad"] = int(np.count_nonzero(m_gpu != m_o))
+    else:
+        err["e_m"] = rel(m_gpu, m_o)
+    w_pre = np.asarray(w_pre, dtype=np.float64)
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    w_own = (1.0 - lr * wd) * w_pre - lr * o_gpu
+    fp32 = 1e-6 * (np.linalg.norm(w_pre) + lr * np.linalg.norm(o_gpu))
+    err["d_own"], err["bar_own"] = float(np.linalg.norm(w_gpu - w_own)), fp32
+    err["d_full"] = float(np.linalg.norm(w_gpu - w_o))
+    err["bar_full"] = 1.5 * lr * np.linalg.norm(o_gpu - o_o) + fp32
+    return err
+
+
+def assert_muon_wd(err, label):
+    assert_o(err, label)
+    if "m_bad" in err:
+        assert err["m_bad"] == 0, f"{label}: {err['m_bad']} bf16 momentum elements differ"
+    else:
+        assert err["e_m"] <= 1e-6, f"{label}: M rel err {err['e_m']:.3e}"
+    assert err["d_own"] <= err["bar_own"], f"{label}: W vs decayed update of GPU O"
+    assert err["d_full"] <= err["bar_full"], f"{label}: W vs oracle step"
+
+
+def host_workers() -> int:
+    """Worker threads for the oracle: the host's CPUs, at most 16 (the CPU
+    share of one GPU on the test machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_map(fn, jobs, workers=None):
+    """[fn(job) for job in jobs], the jobs spread over `workers` threads
+    (default: host_workers()), each worker's BLAS calls on
+    host_workers() // workers threads. numpy releases the GIL in its loops
+    and in BLAS, so many small matrices check in parallel; workers=1 runs the
+    jobs one at a time on all of BLAS's threads (large matrices)."""
+    jobs = list(jobs)
+    total = host_workers()
+    workers = total if workers is None else max(1, min(int(workers), total))
+    if workers == 1:
+        return [fn(j) for j in jobs]
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=max(1, total // workers), user_api="blas"):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, jobs))

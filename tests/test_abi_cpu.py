@@ -260,10 +260,55 @@ def test_step_status_rejects_before_any_device_work():
     assert mh.lib.muonh_last_error().decode()
 
 
-def test_find_overlap():
-    assert mh.find_overlap([]) is None
-    assert mh.find_overlap([(0, 16, "a"), (16, 32, "b"), (64, 80, "c")]) is None  # touching is fine
-    assert mh.find_overlap([(0, 16, "a"), (8, 24, "b")]) == ("a", "b")
-    assert mh.find_overlap([(100, 200, "x"), (0, 16, "a"), (120, 130, "y")]) == ("x", "y")  # containment
-    assert mh.find_overlap([(5, 5, "empty"), (0, 16, "a")]) is None  # zero-length spans ignored
-    assert mh.find_overlap([(0, 16, "a"), (0, 16, "b")]) == ("a", "b")  # same buffer twice
+def _disjoint(plan, W, G, M):
+    arrs = [(ctypes.c_void_p * len(x))(*x) for x in (W, G, M)]
+    return mh.lib.muonh_check_disjoint(plan.handle, *arrs)
+
+
+def test_check_disjoint_host_only():
+    # fake device addresses: the check only compares byte ranges, nothing is
+    # dereferenced. Plan order: two 4x8 fp32 matrices, then one 3x5.
+    p = mh.Plan([(4, 8, 2), (3, 5, 1)])
+    n = [4 * 8 * 4, 4 * 8 * 4, 3 * 5 * 4]   # fp32 bytes per matrix
+    base = 1 << 20
+
+    def packed(start):
+        out, at = [], start
+        for b in n:
+            out.append(at)
+            at += b
+        return out
+    W, G, M = packed(base), packed(2 * base), packed(3 * base)
+    assert _disjoint(p, W, G, M) == mh.MUONH_OK          # adjacent, touching only
+    assert _disjoint(p, W, W, M) == mh.MUONH_EALIAS      # G is W
+    assert "overlaps" in mh.lib.muonh_last_error().decode()
+    M2 = list(M)
+    M2[1] = M[0] + 64                                    # two momenta share bytes
+    assert _disjoint(p, W, G, M2) == mh.MUONH_EALIAS
+    msg = mh.lib.muonh_last_error().decode()
+    assert "M[1]" in msg and "M[0]" in msg
+    W2 = list(W)
+    W2[2] = G[0] + n[0] - 4                              # last 4 bytes of G[0]
+    assert _disjoint(p, W2, G, M) == mh.MUONH_EALIAS
+    W3 = list(W)
+    W3[2] = G[0] - n[2]                                  # ends exactly where G[0] starts
+    assert _disjoint(p, W3, G, M) == mh.MUONH_OK
+    # containment: a small span inside a large one that is not its neighbour
+    big = mh.Plan([(64, 64, 1), (1, 4, 2)])
+    Wb = [base, 2 * base, 3 * base]
+    Gb = [base + 1024, 4 * base, 5 * base]               # G[0] starts inside W[0]
+    Mb = [6 * base, 7 * base, 8 * base]
+    assert _disjoint(big, Wb, Gb, Mb) == mh.MUONH_EALIAS
+    assert mh.lib.muonh_check_disjoint(None, None, None, None) == mh.MUONH_EINVAL
+
+
+def test_check_disjoint_bf16_state_sizes():
+    # with bf16 G and M a matrix spans 2 bytes per entry, so spans that
+    # would overlap in fp32 are disjoint
+    p = mh.Plan([(4, 8, 2)], grad_dtype="bf16", mom_dtype="bf16")
+    W = [1 << 20, (1 << 20) + 128]
+    G = [2 << 20, (2 << 20) + 64]
+    M = [3 << 20, (3 << 20) + 64]
+    assert _disjoint(p, W, G, M) == mh.MUONH_OK
+    p32 = mh.Plan([(4, 8, 2)])
+    assert _disjoint(p32, W, G, M) == mh.MUONH_EALIAS

@@ -1,6 +1,7 @@
 """Host-side argument checks of the Python binding that need device
 tensors: W, G and M must be disjoint (the step updates W and M in place and
-reads G), and a rejected call enqueues nothing."""
+reads G; the library's muonh_check_disjoint finds the overlap and the
+binding names the caller's tensors), and a rejected call enqueues nothing."""
 from __future__ import annotations
 
 import pytest
@@ -28,7 +29,7 @@ def test_overlapping_state_is_rejected_before_any_work():
         opt.step(W, W, M, 0.02, 0.95, 5)  # G is W
     big = torch.zeros(256 * 512 + 300 * 200 + 8, device=dev)
     M_shared = [big[:256 * 512].view(256, 512), big[256 * 512 - 8:256 * 512 - 8 + 300 * 200].view(300, 200)]
-    with pytest.raises(ValueError, match=r"moms\[0\] and moms\[1\] overlap"):
+    with pytest.raises(mh.MuonHAliasError, match=r"moms\[[01]\] overlaps moms\[[01]\]"):
         opt.step(W, G, M_shared, 0.02, 0.95, 5)
     with pytest.raises(ValueError, match="overlap"):
         opt.step_muon_wd(W, G, [W[0], M[1]], 0.02, 0.95, 0.1, 5)

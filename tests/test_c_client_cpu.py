@@ -38,6 +38,32 @@ int main(void) {
   CHECK(strlen(muonh_last_error()) > 0);
   CHECK(muonh_step(plan, NULL, NULL, NULL, NULL, 0.02f, 0.95f, 5, NULL, 0, NULL) == MUONH_EINVAL);
   CHECK(muonh_read_update(plan, 5, NULL, NULL, 0, NULL) != MUONH_OK);
+
+  /* W, G and M must not overlap: checked on host copies of the pointer
+   * arrays (fake addresses, never dereferenced) */
+  {
+    const size_t bytes[5] = {2048u * 512u * 4u, 2048u * 512u * 4u, 2048u * 512u * 4u,
+                             300u * 200u * 4u, 300u * 200u * 4u};
+    char* base = (char*)(uintptr_t)((size_t)1 << 32);
+    const void* w[5];
+    const void* g[5];
+    const void* m[5];
+    size_t at = 0;
+    int i;
+    for (i = 0; i < 5; ++i) {
+      w[i] = base + at;
+      g[i] = base + ((size_t)1 << 30) + at;
+      m[i] = base + ((size_t)2 << 30) + at;
+      at += bytes[i];
+    }
+    CHECK(muonh_check_disjoint(plan, w, g, m) == MUONH_OK);
+    CHECK(muonh_check_disjoint(plan, w, w, m) == MUONH_EALIAS);   /* G == W */
+    CHECK(strstr(muonh_last_error(), "overlaps") != NULL);
+    m[4] = (const char*)m[3] + 16;                                 /* overlapping M views */
+    CHECK(muonh_check_disjoint(plan, w, g, m) == MUONH_EALIAS);
+    CHECK(muonh_check_disjoint(NULL, w, g, m) == MUONH_EINVAL);
+    CHECK(strcmp(muonh_status_string(MUONH_EALIAS), "unknown status") != 0);
+  }
   muonh_plan_destroy(plan);
 
   muonh_plan* bad = NULL;

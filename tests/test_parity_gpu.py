@@ -2,45 +2,29 @@
 
 Parity is teacher-forced per step: before each GPU step the pre-step fp32
 (W, M) are copied to the host, the oracle runs the same step from them with
-the same G, and the GPU's results after the step are compared:
-  * update O      : relative Frobenius error <= 2e-2 (bf16 MFMA Newton-Schulz),
-                    <= 5e-4 (split-bf16 operands) and <= 1e-5 (fp32 mode).
-                    Where storage rounding alone already costs more (tiny
-                    matrices with a few singular values: the emulated floor
-                    of tests/bf16_floor.py), a bf16 or split result must
-                    instead be within 1.3x of that floor. The split bound:
-                    a hi + lo pair carries ~16 significant bits against
-                    bf16's 8, so its floor is ~2^-8 of bf16's (~2e-2 at 8
-                    iterations -> ~8e-5; emulated 2e-5..6e-5), with margin;
-  * momentum M    : relative Frobenius error <= 1e-6 (fp32 fma vs fp64);
-  * weights W     : within 2e-6 (relative Frobenius) of the oracle's projection
-                    of the GPU's own O (this isolates the elementwise phases
-                    from the Newton-Schulz rounding), and within the first-order
-                    bound of the oracle's full step: W = R W'/||W'|| with
-                    W' = W - lr O moves by at most R lr ||dO|| / ||W'|| when O
-                    moves by dO, so ||dW||/R <= 1.5 lr ||dO|| / ||W'|| + 1e-6;
-  * sphere        : | ||W||_F / R - 1 | <= 1e-5 for every matrix.
-The tolerances for O and the sphere are the ones the method's specification
-states; the others follow from fp32 rounding of a fused multiply-add per
-element (M) and of the two-level fp32/fp64 norm (W).
+the same G, and the GPU's results after the step are compared with the bars
+of tests/parity_bar.py (O within 2e-2 with bf16 operands, 5e-4 split, 1e-5
+fp32, on the whole matrix and on every 256 x 256 tile of 4096 entries or
+more, with an oracle-order floor exception only for a printed list of tiny
+shapes; M within 1e-6; W within 2e-6 of the oracle's projection of the GPU's
+own O and within the first-order bound of the full step; |‖W‖/R - 1| <= 1e-5
+on every matrix). bf16 at 8 iterations misses 2e-2 (its floor is about
+2.1e-2): those cases are xfail(strict=True).
 """
 from __future__ import annotations
-
-import sys
 
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-
-from bf16_floor import floor as bf16_floor
+from parity_bar import (assert_muon_wd, assert_muonh, muon_wd_errors, muonh_errors, oracle_map,
+                        rel, say)
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-TOL_O = {"bf16": 2e-2, "split_bf16": 5e-4, "fp32": 1e-5}
 PRECS = ["fp32", "bf16", "split_bf16"]
 
 
@@ -49,52 +33,35 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def rel(a, b):
-    a = np.asarray(a, dtype=np.float64)
-    b = np.asarray(b, dtype=np.float64)
-    nb = np.linalg.norm(b)
-    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
-
-
-def say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
 def make_opt(shapes, prec):
     import orthogonalized_updates_amd as mh
     return mh.MuonH(shapes, precision=prec)
 
 
-def check_step(opt, W, M, G, W_pre, M_pre, R_gpu, lr, beta, k, prec, indices, label):
-    """Compare the GPU step just taken with the oracle, for matrices `indices`."""
-    worst = {"O": 0.0, "M": 0.0, "Wproj": 0.0, "Wfull": 0.0, "sphere": 0.0}
-    for i in indices:
-        o_gpu = opt.read_update(i).cpu().numpy()
-        w_gpu = W[i].cpu().numpy()
-        m_gpu = M[i].cpu().numpy()
-        g = G[i].cpu().numpy() if hasattr(G[i], "cpu") else G[i]
-        r = float(R_gpu[i])
-        w_o, m_o, o_o = oracle.muonh_step(W_pre[i], g, M_pre[i], r, lr, beta, k)
-        e_o = rel(o_gpu, o_o)
-        e_m = rel(m_gpu, m_o)
-        e_wp = rel(w_gpu, oracle.hyperball_project(W_pre[i], o_gpu, r, lr))
-        e_wf = rel(w_gpu, w_o)
-        trial = np.linalg.norm(W_pre[i].astype(np.float64) - lr * o_o)
-        bound_wf = 1.5 * lr * np.linalg.norm(o_gpu - o_o) / max(trial, 1e-30) + 1e-6
-        e_s = abs(np.linalg.norm(w_gpu.astype(np.float64)) / r - 1.0) if r > 0 else 0.0
-        for key, v in (("O", e_o), ("M", e_m), ("Wproj", e_wp), ("Wfull", e_wf), ("sphere", e_s)):
-            worst[key] = max(worst[key], v)
-        tol_o = TOL_O[prec]
-        if prec != "fp32" and e_o > tol_o:
-            fl = bf16_floor(oracle.momentum_update(M_pre[i], g, beta), k, o_o, prec)
-            tol_o = max(tol_o, 1.3 * fl)
-            say(f"{label} mat {i}: O err {e_o:.3e} above {TOL_O[prec]:.0e}; {prec} floor {fl:.3e}")
-        assert e_o <= tol_o, f"{label} mat {i}: O rel err {e_o:.3e} > {tol_o:.3e}"
-        assert e_m <= 1e-6, f"{label} mat {i}: M rel err {e_m:.3e}"
-        assert e_wp <= 2e-6, f"{label} mat {i}: W vs projection of GPU O {e_wp:.3e}"
-        assert e_wf <= bound_wf, f"{label} mat {i}: W vs oracle step {e_wf:.3e} > {bound_wf:.3e}"
-        assert e_s <= 1e-5, f"{label} mat {i}: ||W||/R - 1 = {e_s:.3e}"
+def host_arr(x):
+    return x.float().cpu().numpy() if hasattr(x, "cpu") else x
+
+
+def check_step(opt, W, M, G, W_pre, M_pre, R_gpu, lr, beta, k, prec, indices, label, workers=1,
+               chunk=64):
+    """Compare the GPU step just taken with the oracle, for matrices
+    `indices` (host copies taken `chunk` matrices at a time, the oracle on
+    `workers` threads). Returns the worst errors."""
+    worst = {"O": 0.0, "O_tile": 0.0, "M": 0.0, "Wproj": 0.0, "Wfull": 0.0, "sphere": 0.0}
+    indices = list(indices)
+    for c0 in range(0, len(indices), chunk):
+        part = indices[c0:c0 + chunk]
+        jobs = [(i, opt.read_update(i).cpu().numpy(), W[i].cpu().numpy(), M[i].cpu().numpy(),
+                 host_arr(G[i]), W_pre[i], M_pre[i], float(R_gpu[i])) for i in part]
+
+        def one(j):
+            i, o, w, m, g, wp, mp, r = j
+            return i, muonh_errors(o, w, m, g, wp, mp, r, lr, beta, k, prec)
+        for i, err in oracle_map(one, jobs, workers):
+            assert_muonh(err, f"{label} mat {i}")
+            for key, v in (("O", err["e_o"]), ("O_tile", err["e_tile"]), ("M", err["e_m"]),
+                           ("Wproj", err["e_wp"]), ("Wfull", err["e_wf"]), ("sphere", err["e_s"])):
+                worst[key] = max(worst[key], v)
     return worst
 
 
@@ -187,10 +154,28 @@ def test_maximum_dimension(prec):
                       label=f"max dim {prec}")
 
 
-@pytest.mark.parametrize("prec", ["bf16", "split_bf16"])
+K8_BF16_FLOOR = ("bf16 storage alone costs 2.05e-2 to 2.18e-2 on these inputs at 8 iterations "
+                 "(oracle-order emulation, tests/bf16_floor.py), above the 2e-2 bound; "
+                 "split_bf16 operands meet it")
+
+
+@pytest.mark.parametrize("prec", [
+    pytest.param("bf16", marks=pytest.mark.xfail(strict=True, reason=K8_BF16_FLOOR)),
+    "split_bf16"])
 def test_eight_iterations(prec):
     run_host_workload([(384, 640), (640, 384)], steps=2, k=8, prec=prec, wid=52,
                       label=f"k8 {prec}")
+
+
+# Odd row counts with many 4-column groups: the vector update path's last
+# row pair is half empty, and its reused slots must write only their own
+# thread's groups (MuonH's projection and Muon's decayed update both write W).
+ODD_ROWS = [(129, 2052), (1001, 1200), (2052, 129)]
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_odd_row_counts(prec):
+    run_host_workload(ODD_ROWS, steps=2, k=5, prec=prec, wid=59, label=f"odd rows {prec}")
 
 
 def test_heavy_tailed_grads():
@@ -426,7 +411,10 @@ def test_caller_stream_is_used():
 # Full-size workloads in the benchmark's launch configuration, sampled
 # ---------------------------------------------------------------------------
 
-def run_device_workload(name, *, steps, k, sample, label, prec="bf16"):
+def run_device_workload(name, *, steps, k, sample, label, prec="bf16", workers=1):
+    """The workload's full matrix set in the benchmark's launch configuration,
+    inputs generated on the device; every step checked against the oracle
+    on the `sample` matrices, and the sphere on every matrix."""
     need_gpu()
     torch.cuda.empty_cache()
     wl = workloads.WORKLOADS[name]
@@ -442,6 +430,7 @@ def run_device_workload(name, *, steps, k, sample, label, prec="bf16"):
     for i in sample:
         r_o = oracle.init_radius(W[i].cpu().numpy())
         assert abs(R_host[i] - r_o) <= 1e-6 * r_o
+    worst_all = {}
     for step in range(steps):
         for i, s in enumerate(wl.shapes):
             workloads.device_grad_(wl, i, step, G[i])
@@ -452,16 +441,25 @@ def run_device_workload(name, *, steps, k, sample, label, prec="bf16"):
         opt.step(W, G, M, wl.lr, wl.beta, k)
         torch.cuda.synchronize()
         worst = check_step(opt, W, M, G_host, W_pre, M_pre, R_host, wl.lr, wl.beta, k, prec,
-                           sample, f"{label} step {step}")
-        say(f"[{label}] step {step} worst: " + ", ".join(f"{a}={b:.2e}" for a, b in worst.items()))
+                           sample, f"{label} step {step}", workers=workers)
+        say(f"[{label}] step {step}: {len(sample)} matrices checked, worst: "
+            + ", ".join(f"{a}={b:.2e}" for a, b in worst.items()))
+        for key, v in worst.items():
+            worst_all[key] = max(worst_all.get(key, 0.0), v)
         norms = torch.stack([torch.linalg.vector_norm(w.double()) for w in W]).cpu().numpy()
         assert np.max(np.abs(norms / R_host - 1.0)) <= 1e-5
+    return worst_all
+
+
+# The 2B-shaped set: all seven projections of layers 0, 13 and 27 (21 of the
+# 196 matrices, every shape of the set), every one of its 10 steps.
+QWEN3_2B_SAMPLE = [7 * layer + j for layer in (0, 13, 27) for j in range(7)]
 
 
 def test_qwen3_2b_full_size_sampled():
-    # layers 0 and 27: q, k, v, o, gate, up, down
-    sample = list(range(0, 7)) + list(range(27 * 7, 28 * 7))
-    run_device_workload("qwen3_2b", steps=2, k=5, sample=sample, label="qwen3_2b")
+    wl = workloads.WORKLOADS["qwen3_2b"]
+    run_device_workload("qwen3_2b", steps=wl.steps, k=5, sample=QWEN3_2B_SAMPLE,
+                        label="qwen3_2b", workers=4)
 
 
 def test_long_run_stays_on_the_sphere():
@@ -498,18 +496,22 @@ def test_long_run_stays_on_the_sphere():
                "long run, last step")
 
 
-def test_occupancy_full_size_sampled():
-    run_device_workload("occupancy_512x1536", steps=2, k=5, sample=[0, 1, 255, 256, 300, 511],
-                        label="occupancy")
+def test_occupancy_every_matrix_every_step():
+    # all 512 matrices (256 wide, 256 tall) at every one of the 10 steps
+    wl = workloads.WORKLOADS["occupancy_512x1536"]
+    run_device_workload("occupancy_512x1536", steps=wl.steps, k=5,
+                        sample=list(range(wl.n_matrices)), label="occupancy", workers=None)
+
+
+# 4096x14336: matrices 0 and 31 of the wide half, 32 and 63 of the tall one,
+# two steps each. At 8 iterations bf16 storage alone costs about 2.5e-2 on
+# these (above the 2e-2 bound), so that count runs with split-bf16 operands.
+LARGE_SAMPLE = [0, 31, 32, 63]
 
 
 @pytest.mark.parametrize("k,prec", [(5, "bf16"), (8, "split_bf16")])
 def test_large_full_size_sampled(k, prec):
-    # 64 matrices of 4096x14336 (32 wide, 32 tall); one step, checked on one
-    # matrix of each orientation. At 8 iterations bf16 storage alone costs
-    # ~2.5e-2 on these (above the 2e-2 bound), so that count runs with
-    # split-bf16 operands.
-    run_device_workload("large_4096x14336", steps=1, k=k, sample=[0, 63], prec=prec,
+    run_device_workload("large_4096x14336", steps=2, k=k, sample=LARGE_SAMPLE, prec=prec,
                         label=f"large k={k} {prec}")
 
 
@@ -591,26 +593,10 @@ def test_momentum_norm_extremes(prec):
 
 def check_muon_step(opt, W, M, G, W_pre, M_pre, lr, beta, wd, k, prec, indices, label):
     for i in indices:
-        o_gpu = opt.read_update(i).cpu().numpy()
-        w_gpu = W[i].cpu().numpy()
-        m_gpu = M[i].cpu().numpy()
-        g = G[i].cpu().numpy() if hasattr(G[i], "cpu") else G[i]
-        w_o, m_o, o_o = oracle.muon_wd_step(W_pre[i], g, M_pre[i], lr, beta, wd, k)
-        e_o = rel(o_gpu, o_o)
-        tol_o = TOL_O[prec]
-        if prec != "fp32" and e_o > tol_o:
-            fl = bf16_floor(oracle.momentum_update(M_pre[i], g, beta), k, o_o, prec)
-            tol_o = max(tol_o, 1.3 * fl)
-        assert e_o <= tol_o, f"{label} mat {i}: O rel err {e_o:.3e} > {tol_o:.3e}"
-        assert rel(m_gpu, m_o) <= 1e-6, f"{label} mat {i}: M"
-        w_pre = W_pre[i].astype(np.float64)
-        w_own = (1.0 - lr * wd) * w_pre - lr * o_gpu
-        fp32 = 1e-6 * (np.linalg.norm(w_pre) + lr * np.linalg.norm(o_gpu))
-        d_own = np.linalg.norm(w_gpu - w_own)
-        assert d_own <= fp32, f"{label} mat {i}: W vs decayed update of GPU O: {d_own:.3e} > {fp32:.3e}"
-        d_full = np.linalg.norm(w_gpu - w_o)
-        bound = 1.5 * lr * np.linalg.norm(o_gpu - o_o) + fp32
-        assert d_full <= bound, f"{label} mat {i}: W vs oracle step: {d_full:.3e} > {bound:.3e}"
+        err = muon_wd_errors(opt.read_update(i).cpu().numpy(), W[i].cpu().numpy(),
+                             M[i].cpu().numpy(), host_arr(G[i]), W_pre[i], M_pre[i], lr, beta, wd,
+                             k, prec)
+        assert_muon_wd(err, f"{label} mat {i}")
 
 
 @pytest.mark.parametrize("prec", PRECS)
@@ -634,6 +620,29 @@ def test_muon_wd_ragged_groups(prec, k):
         torch.cuda.synchronize()
         check_muon_step(opt, W, M, G_host, W_pre, M_pre, 0.02, 0.95, 0.1, k, prec, idx,
                         f"muon-wd {prec} k={k} step {st}")
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_muon_wd_odd_row_counts(prec):
+    # the decayed update writes W through the same vector path as the
+    # projection (see test_odd_row_counts)
+    need_gpu()
+    dev = torch.device("cuda")
+    wl = workloads.Workload(wid=74, name="muon odd", shapes=tuple(ODD_ROWS), steps=2, ns_iters=(5,))
+    opt = make_opt(ODD_ROWS, prec)
+    W = [torch.from_numpy(workloads.host_weight(wl, i)).to(dev) for i in range(len(ODD_ROWS))]
+    M = [torch.zeros(s, device=dev) for s in ODD_ROWS]
+    idx = list(range(len(ODD_ROWS)))
+    for st in range(2):
+        G_host = [workloads.host_grad(wl, i, st) for i in idx]
+        G = [torch.from_numpy(g).to(dev) for g in G_host]
+        W_pre = {i: W[i].cpu().numpy() for i in idx}
+        M_pre = {i: M[i].cpu().numpy() for i in idx}
+        say(f"[muon-wd odd rows {prec}] step {st}")
+        opt.step_muon_wd(W, G, M, 0.02, 0.95, 0.1, 5)
+        torch.cuda.synchronize()
+        check_muon_step(opt, W, M, G_host, W_pre, M_pre, 0.02, 0.95, 0.1, 5, prec, idx,
+                        f"muon-wd odd rows {prec} step {st}")
 
 
 def test_muon_wd_decay_only():
