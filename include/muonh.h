@@ -173,6 +173,32 @@ int muonh_step(const muonh_plan* plan, float* const* W, const void* const* G, vo
                const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed device workspace of muonh_step_noalloc (per GPU). */
+#define MUONH_NOALLOC_WORKSPACE_BYTES (128u << 20)
+
+/*
+ * muonh_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step with the same arguments, but no caller workspace. The library
+ * keeps one fixed array of MUONH_NOALLOC_WORKSPACE_BYTES (128 MiB) of
+ * device memory per GPU for the life of the process, and this call runs in
+ * the current device's array; it calls no allocating routine. Plans whose
+ * muonh_workspace_bytes exceed that size are rejected (MUONH_EWORKSPACE),
+ * before anything is enqueued. `stream` must belong to the current device.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the step clears what must start at zero): calls that may overlap
+ * on one GPU (other streams, other threads) race and must be ordered by the
+ * caller. The update O is not kept for muonh_read_update, and the
+ * non-finite record is not reachable through muonh_step_status. R comes
+ * from muonh_init (with a workspace, at set-up) or from a checkpoint;
+ * muonh_init also looks up this device's array, so that the first
+ * muonh_step_noalloc on a device need not.
+ * Errors: as muonh_step.
+ */
+int muonh_step_noalloc(const muonh_plan* plan, float* const* W, const void* const* G,
+                       void* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+                       void* stream);
+
 /*
  * muonh_step plus phase timing: the same work, with hipEventRecord of the
  * caller's events on `stream` at the phase boundaries, for profiling.

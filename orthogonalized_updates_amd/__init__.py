@@ -43,6 +43,8 @@ MUONH_GRAD_BF16 = 4
 MUONH_MOM_BF16 = 8
 MUONH_NONFINITE_MOMENTUM = 1
 MUONH_NONFINITE_UPDATE = 2
+# Bytes of muonh_step_noalloc's fixed per-GPU workspace (include/muonh.h).
+MUONH_NOALLOC_WORKSPACE_BYTES = 128 << 20
 
 # Newton-Schulz operand precision -> plan flag
 PRECISIONS = {"bf16": 0, "split_bf16": MUONH_NS_SPLIT_BF16, "fp32": MUONH_NS_FP32}
@@ -96,6 +98,7 @@ def _load_library() -> ctypes.CDLL:
         "muonh_workspace_bytes": (sz, [vp]),
         "muonh_init": (ctypes.c_int, [vp, vp, vp, vp, sz, vp]),
         "muonh_step": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp, sz, vp]),
+        "muonh_step_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp]),
         "muonh_step_timed": (ctypes.c_int, [vp, vp, vp, vp, vp, f32, f32, i32, vp, sz, vp,
                                             ctypes.POINTER(vp), i32]),
         "muonh_step_muon_wd": (ctypes.c_int, [vp, vp, vp, vp, f32, f32, f32, i32, vp, sz, vp]),
@@ -352,6 +355,22 @@ class MuonH:
                              self._R_plan.data_ptr(), float(lr), float(beta), int(ns_iters),
                              self.workspace.data_ptr(), self.workspace.numel(), self._stream()))
 
+    def step_noalloc(self, weights, grads, moms, lr: float, beta: float = 0.95,
+                     ns_iters: int = 5) -> None:
+        """step() without this object's workspace (muonh_step_noalloc): the
+        library's fixed per-GPU array of MUONH_NOALLOC_WORKSPACE_BYTES serves
+        instead, for plans that fit it. read_update() and status() do not
+        see such a step. The pointer arrays are still device tensors of this
+        object (uploaded once per pointer combination)."""
+        self._check_state(weights, grads, moms)
+        if not hasattr(self, "_R_plan"):
+            raise RuntimeError("call init() (or set_radius()) before step_noalloc()")
+        check(get_lib().muonh_step_noalloc(self.plan.handle, self._ptr_array("W", weights),
+                                           self._ptr_array("G", grads),
+                                           self._ptr_array("M", moms), self._R_plan.data_ptr(),
+                                           float(lr), float(beta), int(ns_iters),
+                                           self._stream()))
+
     def step_timed(self, weights, grads, moms, lr: float, beta: float, ns_iters: int,
                    events) -> None:
         """step() plus hipEventRecord of `events` (torch.cuda.Event list of
@@ -404,7 +423,8 @@ class MuonH:
 __all__ = ["MuonH", "Plan", "MuonHError", "GroupDesc", "get_lib", "check", "LIB_PATH", "HEADER_PATH",
            "NS_COEFFS", "MUONH_OK", "MUONH_EINVAL", "MUONH_ESHAPE", "MUONH_EWORKSPACE",
            "MUONH_EHIP", "MUONH_ENOMEM", "MUONH_EALIAS", "MuonHAliasError", "MUONH_NS_FP32", "MUONH_NS_SPLIT_BF16", "MUONH_GRAD_BF16",
-           "MUONH_MOM_BF16", "MUONH_NONFINITE_MOMENTUM", "MUONH_NONFINITE_UPDATE", "AdamW",
+           "MUONH_MOM_BF16", "MUONH_NONFINITE_MOMENTUM", "MUONH_NONFINITE_UPDATE",
+           "MUONH_NOALLOC_WORKSPACE_BYTES", "AdamW",
            "PTR_CACHE_ENTRIES"]
 
 

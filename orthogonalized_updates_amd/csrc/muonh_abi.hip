@@ -24,6 +24,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -91,6 +92,36 @@ constexpr int64_t kCUs = 256;
 // Index of the non-finite status word after the 16 tail counters.
 constexpr int kStatusWord = 16;
 
+}  // namespace
+
+// Workspace of muonh_step_noalloc: a fixed device array. Every GPU the library
+// runs on holds its own copy until the process ends. On the host the name is
+// only a stand-in: host code reaches the memory through the address that
+// hipGetSymbolAddress returns for the current device (noalloc_workspace).
+static __device__ __align__(256) char scratch[MUONH_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device.
+int noalloc_workspace(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MUONH_EINVAL, "device %d out of [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MUONH_OK;
+}
 }  // namespace
 
 struct muonh_plan {
@@ -550,6 +581,10 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
   if (!W || !R) return fail(MUONH_EINVAL, "W and R must be device arrays");
   int err = 0;
   if (!check_ws(plan, workspace, workspace_bytes, &err)) return err;
+  // set-up for muonh_step_noalloc on this device (its first call retries
+  // and reports a failure)
+  void* scratch_addr = nullptr;
+  (void)noalloc_workspace(&scratch_addr);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   double* partials = reinterpret_cast<double*>(ws + plan->off_partials);
@@ -577,10 +612,9 @@ struct Variant {
   float weight_decay;
 };
 
-int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, void* const* M,
-              const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
-              size_t workspace_bytes, void* stream, void* const* events, int32_t n_events,
-              Variant var = {false, 0.f}) {
+int check_step_args(const muonh_plan* plan, float* const* W, const void* const* G,
+                    void* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+                    void* const* events, int32_t n_events, Variant var) {
   if (!plan) return fail(MUONH_EINVAL, "plan is NULL");
   if (!W || !G || !M || (!R && !var.muon_wd))
     return fail(MUONH_EINVAL, var.muon_wd ? "W, G and M must be device arrays"
@@ -599,7 +633,15 @@ int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, voi
     for (int i = 0; i < n_events; ++i)
       if (!events[i]) return fail(MUONH_EINVAL, "events[%d] is NULL", i);
   }
-  int err = 0;
+  return MUONH_OK;
+}
+
+int step_impl(const muonh_plan* plan, float* const* W, const void* const* G, void* const* M,
+              const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
+              size_t workspace_bytes, void* stream, void* const* events, int32_t n_events,
+              Variant var = {false, 0.f}) {
+  int err = check_step_args(plan, W, G, M, R, lr, beta, ns_iters, events, n_events, var);
+  if (err != MUONH_OK) return err;
   if (!check_ws(plan, workspace, workspace_bytes, &err)) return err;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -704,6 +746,22 @@ int muonh_step(const muonh_plan* plan, float* const* W, const void* const* G, vo
                const float* R, float lr, float beta, int32_t ns_iters, void* workspace,
                size_t workspace_bytes, void* stream) {
   return step_impl(plan, W, G, M, R, lr, beta, ns_iters, workspace, workspace_bytes, stream,
+                   nullptr, 0);
+}
+
+int muonh_step_noalloc(const muonh_plan* plan, float* const* W, const void* const* G,
+                       void* const* M, const float* R, float lr, float beta, int32_t ns_iters,
+                       void* stream) {
+  int err = check_step_args(plan, W, G, M, R, lr, beta, ns_iters, nullptr, 0, Variant{false, 0.f});
+  if (err != MUONH_OK) return err;
+  if (plan->ws_bytes > (size_t)MUONH_NOALLOC_WORKSPACE_BYTES)
+    return fail(MUONH_EWORKSPACE,
+                "the plan needs %zu bytes of workspace; muonh_step_noalloc has %zu "
+                "(MUONH_NOALLOC_WORKSPACE_BYTES): use muonh_step with a caller workspace",
+                plan->ws_bytes, (size_t)MUONH_NOALLOC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  if ((err = noalloc_workspace(&ws)) != MUONH_OK) return err;
+  return step_impl(plan, W, G, M, R, lr, beta, ns_iters, ws, MUONH_NOALLOC_WORKSPACE_BYTES, stream,
                    nullptr, 0);
 }
 

@@ -312,3 +312,19 @@ def test_check_disjoint_bf16_state_sizes():
     assert _disjoint(p, W, G, M) == mh.MUONH_OK
     p32 = mh.Plan([(4, 8, 2)])
     assert _disjoint(p32, W, G, M) == mh.MUONH_EALIAS
+
+
+def test_noalloc_rejects_plans_beyond_its_array():
+    # the size check runs before any HIP call: fake, never dereferenced
+    # pointers are enough
+    big = mh.Plan([(4096, 14336, 1)])
+    assert big.workspace_bytes > mh.MUONH_NOALLOC_WORKSPACE_BYTES
+    fake = ctypes.c_void_p(1 << 20)
+    st = mh.lib.muonh_step_noalloc(big.handle, fake, fake, fake, fake, 0.02, 0.95, 5, None)
+    assert st == mh.MUONH_EWORKSPACE
+    assert "MUONH_NOALLOC_WORKSPACE_BYTES" in mh.lib.muonh_last_error().decode()
+    # argument errors are reported first, as for muonh_step
+    assert mh.lib.muonh_step_noalloc(big.handle, None, fake, fake, fake, 0.02, 0.95, 5,
+                                     None) == mh.MUONH_EINVAL
+    assert mh.lib.muonh_step_noalloc(big.handle, fake, fake, fake, fake, 0.02, 1.5, 5,
+                                     None) == mh.MUONH_EINVAL
