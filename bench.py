@@ -82,12 +82,17 @@ def elementwise_bytes(n_params, ns_bytes, fused, variant="muonh", g_bytes=4, m_b
     return pre, post
 
 
-def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1, mom_bf16=False):
-    """The fp64 oracle on the host, on one matrix of each distinct shape,
-    extrapolated by count to the whole set (matrices are independent). With
-    mom_bf16 the oracle keeps the momentum in bf16 (exact fma rounding)."""
-    import numpy as np
-
+def cpu_baseline(wl, k, budget_s, sample, variant="muonh", weight_decay=0.1, mom_bf16=False,
+                 prec="bf16"):
+    """The fp64 oracle on the host, timed on one matrix of each distinct
+    shape and extrapolated by count to the whole set (matrices are
+    independent), on the very inputs of one more GPU step taken after the
+    timed ones: `sample` maps a matrix index to its host arrays (pre-step W,
+    M, G and R, and the GPU's O, W, M after that step). Each oracle result is
+    also compared with the GPU's (the parity bar of the tests: O within 2e-2
+    with bf16 operands, on the whole matrix and on every 256 x 256 tile of
+    4096 or more entries). With mom_bf16 the oracle keeps the momentum in
+    bf16 (one rounding of the exact value)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -99,19 +104,19 @@ def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1, mom_bf16=Fa
     total = 0.0
     used = 0.0
     parts = []
+    checks = []
     for (r, c), idx in groups:
         i = idx[0]
-        w = workloads.host_weight(wl, i)
-        g = workloads.host_grad(wl, i, 0)
-        m = np.zeros_like(w)
-        radius = oracle.init_radius(w)
+        x = sample[i]
         runs = 0
         t0 = time.perf_counter()
         while True:
             if variant == "muon_wd":
-                oracle.muon_wd_step(w, g, m, wl.lr, wl.beta, weight_decay, k, mom_bf16=mom_bf16)
+                w_o, m_o, o_o = oracle.muon_wd_step(x["w_pre"], x["g"], x["m_pre"], wl.lr, wl.beta,
+                                                    weight_decay, k, mom_bf16=mom_bf16)
             else:
-                oracle.muonh_step(w, g, m, radius, wl.lr, wl.beta, k, mom_bf16=mom_bf16)
+                w_o, m_o, o_o = oracle.muonh_step(x["w_pre"], x["g"], x["m_pre"], x["r"], wl.lr,
+                                                  wl.beta, k, mom_bf16=mom_bf16)
             runs += 1
             el = time.perf_counter() - t0
             if el >= per_shape_budget or runs >= 5:
@@ -120,18 +125,128 @@ def cpu_baseline(wl, k, budget_s, variant="muonh", weight_decay=0.1, mom_bf16=Fa
         used += el
         total += t * len(idx)
         parts.append(f"{r}x{c}: {t:.3f} s x {len(idx)}")
-    return {
+        checks.append(parity_numbers(i, (r, c), x, o_o, m_o, w_o, mom_bf16))
+    out = {
         "value": wl.n_params / total,
         "unit": "params/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": ("one fp64 oracle step (momentum, Newton-Schulz k=%d, %s) of one matrix "
-                   "per distinct shape, timed over %.1f s and extrapolated by matrix count to the "
-                   "full set (%s); est. %.1f s per full step"
+                   "per distinct shape, on the inputs of a GPU step taken after the timed ones, "
+                   "timed over %.1f s and extrapolated by matrix count to the full set (%s); "
+                   "est. %.1f s per full step"
                    % (k, "decayed update" if variant == "muon_wd" else "projection", used,
                       "; ".join(parts), total)),
         "host_cpu": host_cpu(),
     }
+    tol = {"bf16": 2e-2, "split_bf16": 5e-4, "fp32": 1e-5}[prec]
+    out["parity"] = {"matrices": checks, "o_bar": tol,
+                     "ok": all(cm["o_rel_err"] <= tol and cm["o_worst_tile_rel_err"] <= tol
+                               for cm in checks)}
+    return out
+
+
+def parity_numbers(i, shape, x, o_o, m_o, w_o, mom_bf16):
+    """The GPU's results of one matrix against the oracle's on the same inputs."""
+    import numpy as np
+
+    def rel(a, b):
+        a = np.asarray(a, np.float64)
+        b = np.asarray(b, np.float64)
+        nb = np.linalg.norm(b)
+        return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+    worst_tile = 0.0
+    for r0 in range(0, o_o.shape[0], 256):
+        for c0 in range(0, o_o.shape[1], 256):
+            t = o_o[r0:r0 + 256, c0:c0 + 256]
+            if t.size >= 4096:
+                worst_tile = max(worst_tile, rel(x["o"][r0:r0 + 256, c0:c0 + 256], t))
+    rec = {"index": int(i), "shape": list(shape), "o_rel_err": rel(x["o"], o_o),
+           "o_worst_tile_rel_err": worst_tile, "w_rel_err": rel(x["w"], w_o)}
+    if mom_bf16:
+        rec["m_bits_differing"] = int(np.count_nonzero(np.asarray(x["m"], np.float64) != m_o))
+    else:
+        rec["m_rel_err"] = rel(x["m"], m_o)
+    return rec
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi) on a host thread while the
+    timed steps run; the GEMMs are about 85 % of that time. Reports the
+    mean, min and max of the samples in MHz, or why it could not."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # pragma: no cover - depends on the machine
+            self.error = f"amdsmi unavailable: {e}"[:160]
+
+    def _read(self):
+        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # pragma: no cover
+                self.error = f"clock read failed: {e}"[:160]
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.error is None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        try:
+            if self.error is None:
+                self._smi.amdsmi_shut_down()
+        except Exception:  # pragma: no cover
+            pass
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "amdsmi gfx clock", "mhz_mean": None,
+                    "note": self.error or "no samples"}
+        v = self.samples
+        return {"source": "amdsmi gfx clock, sampled on a host thread during the timed steps",
+                "samples": len(v), "mhz_mean": round(sum(v) / len(v), 1),
+                "mhz_min": min(v), "mhz_max": max(v)}
+
+
+def runtime_versions():
+    """ROCm release of the installation and the HIP runtime torch uses."""
+    rocm = None
+    for path in ("/opt/rocm/.info/version",):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+        except OSError:
+            pass
+    try:
+        import torch
+        hip = torch.version.hip
+        name = torch.cuda.get_device_name(0) if torch.cuda.is_available() else None
+    except Exception:  # pragma: no cover
+        hip, name = None, None
+    return {"rocm": rocm, "hip_runtime": hip, "device": name}
 
 
 def host_cpu() -> str:
@@ -403,17 +518,24 @@ def main() -> int:
         events.append(evs)
     torch.cuda.synchronize(dev)
 
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        if args.variant == "muon_wd":
-            opt.step_muon_wd(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta,
-                             args.weight_decay, k, events=events[s])
-        else:
-            opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
-    torch.cuda.synchronize(dev)
-    t1 = time.perf_counter()
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            if args.variant == "muon_wd":
+                opt.step_muon_wd(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta,
+                                 args.weight_decay, k, events=events[s])
+            else:
+                opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
+        torch.cuda.synchronize(dev)
+        t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = 1e3 * elapsed / args.steps
+
+    # After the timed steps: every matrix still on its sphere (MuonH)
+    sphere = None
+    if args.variant == "muonh":
+        norms = torch.stack([torch.linalg.vector_norm(w.double()) for w in W])
+        sphere = float((norms / opt.R.double() - 1.0).abs().max())
 
     # Phase durations from the events recorded inside the timed steps.
     pre = post = 0.0
@@ -492,10 +614,28 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    result["selfcheck"] = {"sphere_max_abs_dev": sphere, "sphere_bar": 1e-5,
+                           "matrices": wl.n_matrices}
+    result["env"] = {**runtime_versions(), "gfx_clock": clock.summary()}
     if not args.no_cpu_baseline:
+        # one more GPU step, untimed, whose inputs and results the oracle
+        # leg takes for one matrix of each distinct shape
+        idx = [ids[0] for _, ids in wl.shape_groups()]
+        gs = G[(args.warmup + args.steps) % pool]
+        sample = {i: {"w_pre": W[i].cpu().numpy(), "m_pre": M[i].float().cpu().numpy(),
+                      "g": gs[i].float().cpu().numpy(), "r": float(opt.R[i])} for i in idx}
+        if args.variant == "muon_wd":
+            opt.step_muon_wd(W, gs, M, wl.lr, wl.beta, args.weight_decay, k)
+        else:
+            opt.step(W, gs, M, wl.lr, wl.beta, k)
+        torch.cuda.synchronize(dev)
+        for i in idx:
+            sample[i].update({"o": opt.read_update(i).cpu().numpy(), "w": W[i].cpu().numpy(),
+                              "m": M[i].float().cpu().numpy()})
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, k, args.cpu_budget, args.variant,
-                                              args.weight_decay, args.mom_dtype == "bf16")
+        result["cpu_baseline"] = cpu_baseline(wl, k, args.cpu_budget, sample, args.variant,
+                                              args.weight_decay, args.mom_dtype == "bf16",
+                                              args.precision)
     print(json.dumps(result), flush=True)
     return 0
 

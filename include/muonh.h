@@ -86,11 +86,14 @@ enum {
 
 /* Newton-Schulz plan flags (at most one). Default: operands in bf16, bf16
  * MFMA with fp32 accumulation; about 1e-2 relative error of O at 5
- * iterations, about 2e-2 at 8. With bf16 or split operands and
+ * iterations, about 1.8e-2 at 8. With bf16 or split operands and
  * ns_iters >= 1, X0's factor 1/(||M||_F + 1e-7) is applied inside the first
  * iteration's products rather than before rounding M to the operand format
  * (the same value up to that rounding; matrices of at most 65536 entries,
- * and momentum norms outside [2^-40, 2^40], are normalised first). */
+ * and momentum norms outside [2^-40, 2^40], are normalised first). For
+ * matrices of more than 65536 entries the polynomial stores
+ * B' = a*I + b*A + c*A*A and the update is X <- B' X: the same algebra as
+ * a*X + B*X, with a better-conditioned rounding of B'. */
 enum {
   /* fp32 operands and fp32 MFMA. Debug/reference mode: about 1e-6 relative
    * error, an order of magnitude slower. */

@@ -6,12 +6,12 @@
 // fp32. Every kernel is one grouped launch over the matrices of up to 16
 // shape groups; blocks stream contiguous chunks with 16-byte accesses
 // (8-byte for bf16 G and M), non-temporal on the M and W streams. Norms are
-// deterministic reductions: each 4 squares summed in fp32 (relative error at
-// most a few fp32 ulps, every term being positive), an fp64 running sum per
-// thread, a fixed shuffle tree in fp64 per block, then a fixed-order fp64 sum
-// of the per-block partials in a separate finalize kernel (no float atomics).
-// So a norm's relative error stays below about 3e-7 however many entries a
-// matrix has.
+// deterministic reductions: at most 16 squares summed in fp32 (relative error
+// at most 16 fp32 ulps, about 1e-6, every term being positive), an fp64
+// running sum per thread, a fixed shuffle tree in fp64 per block, then a
+// fixed-order fp64 sum of the per-block partials in a separate finalize
+// kernel (no float atomics). So a norm's relative error stays below about
+// 5e-7 however many entries a matrix has.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,10 +29,12 @@ __device__ __forceinline__ int group_of_block(const EwArgs& a, int b) {
   return gi;
 }
 
-// Sum of the squares of 4 values in fp32, widened for an fp64 running sum.
-__device__ __forceinline__ double sq4(float4 v) {
-  return (double)fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
+// Sum of the squares of 4 values in fp32 (sq4f), widened for an fp64
+// running sum (sq4).
+__device__ __forceinline__ float sq4f(float4 v, float acc = 0.f) {
+  return fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, acc))));
 }
+__device__ __forceinline__ double sq4(float4 v) { return (double)sq4f(v); }
 __device__ __forceinline__ double sq1(float v) { return (double)v * (double)v; }
 
 // Fixed-order block sum; the result is valid in thread 0.
@@ -380,7 +382,7 @@ __device__ __forceinline__ double cast_tile(const EwGroup& g, char* blk, const v
   const int tx = (threadIdx.x & 15) << 2, ty = threadIdx.x >> 4;
   const bool vec = (g.cols & 3) == 0 && vec_aligned<MB>(mp) && (!kMomentum || vec_aligned<GB>(gp));
   const bool trans = g.offE >= 0;
-  double acc = 0.0;
+  float acc = 0.f;  // the squares of this thread's 16 values
   if (trans) __syncthreads();  // the previous tile's transposed reads are done
   // The vector loads of all four rows are issued before the first store.
   const int c = c0 + tx;
@@ -430,7 +432,7 @@ __device__ __forceinline__ double cast_tile(const EwGroup& g, char* blk, const v
         v = make_float4(e[0], e[1], e[2], e[3]);
       }
     }
-    if (kMomentum) acc += sq4(v);
+    if (kMomentum) acc = sq4f(v, acc);
     v.x *= scale;
     v.y *= scale;
     v.z *= scale;
@@ -453,7 +455,7 @@ __device__ __forceinline__ double cast_tile(const EwGroup& g, char* blk, const v
       Fmt<F>::store4(blk + g.offE, c0 + cc, r0 + tx, g.rp, v);
     }
   }
-  return acc;
+  return (double)acc;
 }
 
 // X0 = M / (||M|| + eps): one tile per block.
@@ -601,6 +603,7 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
         }
       // All four results first, then the stores: a store between two
       // results would make the next one wait for it.
+      float part = 0.f;  // squares of this pass's (up to) 16 values
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -617,9 +620,10 @@ __global__ __launch_bounds__(kThreads) void k_update(EwArgs a, float* const* W, 
           if (kProject) {
             v.x *= scale; v.y *= scale; v.z *= scale; v.w *= scale;
           }
-          if (!kWrite && live[j][h]) acc += sq4(v);
+          if (!kWrite && live[j][h]) part = sq4f(v, part);
           wv[j][h] = v;
         }
+      if (!kWrite) acc += (double)part;
       // Unconditional stores: a slot past the end holds the address and the
       // recomputed value of one of this thread's live units, so it rewrites
       // the same bytes with the same value (a store under a branch would

@@ -217,7 +217,7 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, EwKind kind, int ns_i
         e.offE = G.trans ? x0 : -1;
       }
       e.tiles_per_mat = (rp / 64) * (cp / 64);
-      e.defer = G.n > kDeferMinElems;
+      e.defer = G.n > kSmallMatElems;
       e.tpb = 1;
       if (kind == kEwFused) {
         e.tpb = (e.tiles_per_mat + kMaxPartials - 1) / kMaxPartials;
@@ -252,7 +252,8 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     q.count = G.count;
     q.first = G.first;
     q.offE = q.offO1 = q.offO2 = -1;
-    q.defer = G.n > kDeferMinElems;
+    q.defer = G.n > kSmallMatElems;
+    q.fold = G.n > kSmallMatElems;
     const int ts = G.sp / T, tl = G.lp / T;
     const int64_t xcur = p->prec == kFp32 ? G.offX : G.offXs[src];
     if (mode == kGram) {
@@ -286,7 +287,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
       q.tm = ts;
       q.tn = tl;
       q.tiles_per_mat = ts * tl;
-      q.offE = xin;
+      q.offE = q.fold ? -1 : xin;  // folded: B carries a*I
       q.lde = G.lp;
       if (last && G.trans) {
         q.offO2 = xout;
@@ -306,7 +307,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
       q.tm = ts;
       q.tn = tl;
       q.tiles_per_mat = ts * tl;
-      q.offE = G.offX;
+      q.offE = q.fold ? -1 : G.offX;
       q.lde = G.lp;
       if (!(last && G.trans)) {
         q.offO1 = G.offX;
@@ -368,6 +369,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     if (mode == kPoly) {
       a.c0 = kNsB;
       a.c1 = kNsC;
+      a.diag = kNsA;
     } else if (mode == kApply) {
       a.c0 = kNsA;
       a.c1 = 1.f;

@@ -48,11 +48,13 @@ __host__ __device__ inline bool xnorm_deferred(double n) {
 __host__ __device__ inline float x0_sigma(double n) {
   return xnorm_deferred(n) ? (float)(1.0 / (n + kNsEps)) : 1.f;
 }
-// Matrices of at most this many entries never defer: their X0 is rounded
-// after the normalisation, in the order of the step's definition. For them
-// the extra read of M costs nothing measurable, and with only a few singular
-// values the place of the rounding shows in the result.
-constexpr int64_t kDeferMinElems = 65536;
+// Matrices of at most this many entries follow the order of the step's
+// definition exactly: their X0 is rounded after the normalisation (never
+// deferred), and the apply adds a*X in fp32 (B is not folded, see
+// GemmGroup::fold). For them the extra read of M costs nothing measurable,
+// and with only a few singular values the place of a rounding shows in the
+// result.
+constexpr int64_t kSmallMatElems = 65536;
 
 // Storage of the gradient and the momentum (plan flags MUONH_GRAD_BF16 and
 // MUONH_MOM_BF16): fp32, or bf16. A bf16 momentum is the exact beta*M + G
@@ -89,7 +91,7 @@ struct EwGroup {
   int rp, cp;           // padded rows / cols
   int tiles_per_mat;    // 64x64 tiles of the padded rp x cp domain
   int defer;            // 1: X0's normalisation may be deferred (more than
-                        // kDeferMinElems entries)
+                        // kSmallMatElems entries)
 };
 
 struct EwArgs {
@@ -155,6 +157,12 @@ struct GemmGroup {
   int count;
   int first;            // global index of the group's first matrix
   int defer;            // 1: the group's X0 may be unscaled (see EwGroup)
+  // 1 (more than kSmallMatElems entries): the polynomial writes
+  // B' = a*I + b*A + c*A*A and the apply computes X <- B' X with no a*X term.
+  // The same algebra as a*X + B X; B' has eigenvalues p(sigma)/sigma near 1
+  // instead of B's near -2.7, so its bf16 rounding costs less accuracy (a
+  // bf16 emulation of 5 iterations: 1.07e-2 against 1.17e-2 on 512x1536).
+  int fold;
 };
 
 struct GemmArgs {
@@ -164,6 +172,7 @@ struct GemmArgs {
   int grid;      // blocks launched (>= ntiles when the XCD mapping pads)
   int xcd_map;   // 1: deal each group's tiles to the 8 XCDs in contiguous eighths
   float c0, c1;
+  float diag;    // polynomial: added to the diagonal of B in groups that fold
   // First iteration after the fused momentum + cast: per-matrix ||M||; the
   // output is scaled by x0_sigma (Gram: squared). nullptr: no scaling.
   const double* xnorm;

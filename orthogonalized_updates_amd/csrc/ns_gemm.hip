@@ -245,8 +245,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm(Gem
             v[q] = a;
           } else if (MODE == kPoly) {
             v[q] = fmaf(c1, a, c0 * ld_f(E + (int64_t)(row0 + q) * g.lde + col));
+            if (g.fold && row0 + q == col) v[q] += args.diag;
           } else {
-            v[q] = fmaf(c0, ld_f(E + (int64_t)(row0 + q) * g.lde + col), a);
+            v[q] = E ? fmaf(c0, ld_f(E + (int64_t)(row0 + q) * g.lde + col), a) : a;
           }
         }
         if (O1) {
@@ -654,7 +655,7 @@ __device__ __forceinline__ void pingpong(const bf::DmaSrc& dsrc, const bf::QtSrc
       load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, lo.f[0], fa);
       load_frags<MT, NT>(buf, buf + kPanel, wm0, wn0, lo.f[1], fb);
     }
-    if (E_TERM) take_e(buf, kt);
+    if (E_TERM && seed != 0.f) take_e(buf, kt);
   };
   auto mul = [&]() {
     if (SPLIT) {
@@ -782,7 +783,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
     else issue_share(dsrc, st, ring_lds + st * kStage);
   }
   phase_barrier<12>();  // this wave's share of stage 0 has landed
-  const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
+  // the E term: a*X in the apply (none where B carries a*I), (b/c)*A in the
+  // polynomial
+  const float seed = MODE == kApply ? (g.fold ? 0.f : args.c0)
+                     : MODE == kPoly ? args.c0 / args.c1 : 0.f;
   if (wave < 4)
     pingpong<0, kMT, kNT, MODE != kGram, SPLIT, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0,
                                                      wn0, lo, lane, bi, seed, acc);
@@ -812,9 +816,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         bf16x4 h, l;
+        const int row0 = wm0 + mi * 32 + 8 * rg + 4 * (lane >> 5);
+        const int col = wn0 + ni * 32 + (lane & 31);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float v = scale * acc[mi][ni][rg * 4 + q];
+          float v = scale * acc[mi][ni][rg * 4 + q];
+          if (MODE == kPoly && g.fold && bi == bj && row0 + q == col) v += args.diag;
           h[q] = (__bf16)v;
           if (SPLIT) l[q] = (__bf16)(v - (float)h[q]);
         }
@@ -1029,7 +1036,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
         f.b[ni] = *reinterpret_cast<const bf16x8*>(buf + kPanel + n0 * kPRow + o.f);
       }
     }
-    if (E_TERM) take_e(buf, kt);
+    if (E_TERM && seed != 0.f) take_e(buf, kt);
   };
   auto mul = [&]() {
 #pragma unroll
@@ -1148,7 +1155,10 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
     else issue_share(dsrc, st, ring_lds + st * kStage);
   }
   phase_barrier<12>();
-  const float seed = MODE == kApply ? args.c0 : MODE == kPoly ? args.c0 / args.c1 : 0.f;
+  // the E term: a*X in the apply (none where B carries a*I), (b/c)*A in the
+  // polynomial
+  const float seed = MODE == kApply ? (g.fold ? 0.f : args.c0)
+                     : MODE == kPoly ? args.c0 / args.c1 : 0.f;
   // Diagonal tile of a symmetric product: its lower-left quadrant is the
   // transpose of the upper-right one, so the second group computes only the
   // lower-right quadrant (a 128 x 32 strip per wave, half the MFMAs) and the
@@ -1168,13 +1178,20 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
     const float sg = x0_sigma(args.xnorm[g.first + mat]);
     scale = MODE == kGram ? sg * sg : sg;
   }
+  // B' = B + a*I on the diagonal of the polynomial's diagonal tiles
+  const bool add_diag = MODE == kPoly && g.fold && diag;
   bf16x4 vh[kMT][kNT];
 #pragma unroll
   for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kNT; ++ni)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) vh[mi][ni][q] = (__bf16)(scale * acc[mi][ni][q]);
+      for (int q = 0; q < 4; ++q) {
+        float v = scale * acc[mi][ni][q];
+        if (add_diag && wm0 + 16 * mi + 4 * (lane >> 4) + q == wnc + 16 * ni + (lane & 15))
+          v += args.diag;
+        vh[mi][ni][q] = (__bf16)v;
+      }
   char* stg = const_cast<char*>(ring);
   auto srow = [&](int row) -> char* { return stg + (row >> 6) * kStage + (row & 63) * 512; };
   char* O1 = g.offO1 < 0 ? nullptr : const_cast<char*>(blk) + g.offO1;

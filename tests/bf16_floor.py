@@ -15,9 +15,10 @@ fp32), and a product of two split operands omits lo*lo.
 By default the emulation follows the definition's order: X0 = M/(||M|| + eps)
 is rounded after the normalisation. deferred=True instead stores M itself
 rounded and folds 1/(||M|| + eps) into the first Gram (squared) and the
-first apply, for norms in [2^-40, 2^40] (or 0); with fmt="exact" that checks
-that the rescheduled algebra equals the definition. The parity bars never
-use deferred=True.
+first apply, for norms in [2^-40, 2^40] (or 0), and fold=True stores
+B' = a*I + b*A + c*A*A and computes X <- B' X (the library's order for
+matrices of more than 65536 entries); with fmt="exact" these check that the
+rescheduled algebra equals the definition. The parity bars never use them.
 """
 from __future__ import annotations
 
@@ -49,7 +50,7 @@ def _deferred(n: float) -> bool:
     return n == 0.0 or 2.0 ** -40 <= n <= 2.0 ** 40
 
 
-def _ns_emulated(m, k: int, fmt: str, deferred: bool = False) -> np.ndarray:
+def _ns_emulated(m, k: int, fmt: str, deferred: bool = False, fold: bool = False) -> np.ndarray:
     if fmt == "bf16":
         def store(v):
             r = round_bf16(v)
@@ -78,6 +79,14 @@ def _ns_emulated(m, k: int, fmt: str, deferred: bool = False) -> np.ndarray:
     if t:
         x = x.T
     nrm = float(np.linalg.norm(x))
+    eye = np.eye(x.shape[0])
+
+    def poly(a):
+        # B = b*A + c*A*A, or B' = a*I + B when folded
+        return store(B_ * a[0] + C_ * mul(a, a) + (A_ * eye if fold else 0.0))
+
+    def apply(b, y):
+        return mul(b, y) if fold else A_ * y[0] + mul(b, y)
     first = 0
     if deferred and int(k) >= 1 and _deferred(nrm):
         # the stored operand is M itself; the first Gram takes sigma^2 and
@@ -86,16 +95,14 @@ def _ns_emulated(m, k: int, fmt: str, deferred: bool = False) -> np.ndarray:
         y = store(x)
         yt = tuple(None if v is None else v.T for v in y)
         a = store(sigma * sigma * mul(y, yt))
-        b = store(B_ * a[0] + C_ * mul(a, a))
-        x = store(sigma * (A_ * y[0] + mul(b, y)))
+        x = store(sigma * apply(poly(a), y))
         first = 1
     else:
         x = store(x / (nrm + EPS))
     for _ in range(first, int(k)):
         xt = tuple(None if v is None else v.T for v in x)
         a = store(mul(x, xt))
-        b = store(B_ * a[0] + C_ * mul(a, a))
-        x = store(A_ * x[0] + mul(b, x))
+        x = store(apply(poly(a), x))
     return x[0].T if t else x[0]
 
 

@@ -17,8 +17,9 @@ Update O (the orthogonalized momentum):
     emulation of the iteration in the definition's own order (X0 rounded
     after the normalisation; tests/bf16_floor.py). These matrices have no
     tile of 4096 entries. The library rounds them in that same order.
-bf16 at 8 iterations does not meet 2e-2 (its floor is about 2.1e-2 to
-2.5e-2): the tests that ask for it are marked xfail(strict=True).
+bf16 at 8 iterations in the definition's order would not meet 2e-2 (its
+floor is about 2.1e-2 to 2.5e-2); the library folds a*I into the polynomial's
+output for matrices of more than 65536 entries, which keeps it within 2e-2.
 
 Momentum M: <= 1e-6 relative (one fp32 fma per element against fp64); a
 bf16 momentum must equal the oracle's bit for bit.

@@ -84,11 +84,44 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
+def _bench_sample(wl, k, spoil_tile=False):
+    """Host arrays shaped like bench.py's sample: pre-step inputs of one matrix
+    per shape, and 'GPU' results made from the oracle's own, rounded to fp32
+    (optionally with one 256x256 tile of O negated)."""
+    import numpy as np
+
+    import oracle
+    out = {}
+    for _, idx in wl.shape_groups():
+        i = idx[0]
+        w = workloads.host_weight(wl, i)
+        g = workloads.host_grad(wl, i, 0)
+        m = np.zeros_like(w)
+        r = oracle.init_radius(w)
+        w1, m1, o1 = oracle.muonh_step(w, g, m, r, wl.lr, wl.beta, k)
+        o = o1.astype(np.float32)
+        if spoil_tile:
+            o[:256, :256] *= -1
+        out[i] = {"w_pre": w, "m_pre": m, "g": g, "r": r, "o": o, "w": w1.astype(np.float32),
+                  "m": m1.astype(np.float32)}
+    return out
+
+
 def test_cpu_baselines_report_the_oracle():
     wl = workloads.WORKLOADS["single_128x256"]
-    r = bench.cpu_baseline(wl, 5, 0.05)
+    r = bench.cpu_baseline(wl, 5, 0.05, _bench_sample(wl, 5))
     assert r["kind"] == "oracle" and r["unit"] == "params/s" and r["value"] > 0 and r["cores"] >= 1
-    r = bench.cpu_baseline(wl, 5, 0.05, variant="muon_wd", mom_bf16=True)
-    assert r["value"] > 0 and "decayed update" in r["sample"]
+    assert r["parity"]["ok"] and r["parity"]["matrices"][0]["o_rel_err"] < 1e-6
+    bad = bench.cpu_baseline(wl, 5, 0.05, _bench_sample(wl, 5, spoil_tile=True))
+    assert not bad["parity"]["ok"]
+    assert bad["parity"]["matrices"][0]["o_worst_tile_rel_err"] > 1.0
     a = bench.adamw_cpu_baseline(1000, 0.05)
     assert a["kind"] == "oracle" and a["value"] > 0 and a["cores"] == 1
+
+
+def test_clock_sampler_without_a_gpu_reports_why():
+    with bench.ClockSampler(period_s=0.001) as c:
+        pass
+    rec = c.summary()
+    assert rec["source"].startswith("amdsmi") and (rec["mhz_mean"] is not None or rec["note"])
+    assert bench.runtime_versions()["rocm"]

@@ -436,6 +436,21 @@ def test_deferred_normalisation_is_exact_algebra(scale, shape):
         assert np.linalg.norm(_ns_emulated(m, 1, "exact") - no_eps) > 1e-3 * np.linalg.norm(no_eps)
 
 
+@pytest.mark.parametrize("shape", [(48, 80), (80, 48), (64, 64)])
+def test_folded_polynomial_is_exact_algebra(shape):
+    # Matrices of more than 65536 entries take B' = a*I + b*A + c*A*A and
+    # X <- B' X (no a*X term): without rounding, the oracle's iteration, also
+    # combined with the deferred normalisation. A missing or misplaced a*I
+    # (off the diagonal, or also kept as a*X) would not match.
+    from bf16_floor import _ns_emulated
+    m = rand(shape, (24, shape[0]), 0.01)
+    for k in (1, 2, 5):
+        ref = oracle.newton_schulz(m, k)
+        for deferred in (False, True):
+            got = _ns_emulated(m, k, "exact", deferred=deferred, fold=True)
+            assert np.linalg.norm(got - ref) <= 1e-11 * np.linalg.norm(ref)
+
+
 def test_split_bf16_pair_carries_sixteen_bits():
     # hi + lo represents an fp32 value to within about 2^-17 of its magnitude
     # (hi has 8 significant bits, lo the next 8 and a rounding bit), and lo is
