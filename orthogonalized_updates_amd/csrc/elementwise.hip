@@ -274,26 +274,32 @@ __global__ __launch_bounds__(kThreads) void k_momentum(EwArgs a, const void* con
 
 // --------------------------------------------------------------------------
 // norms[mat] = sqrt(sum_c partials[mat][c]) in a fixed order, for exactly the
-// matrices of the launch's groups (thread t takes the t-th of them). The
-// groups need not cover a contiguous range of matrices: launches for other
-// matrices may run concurrently and own the rest of the arrays.
+// matrices of the launch's groups: one wave per matrix (the t-th of them),
+// lane l summing partials l, l + 64, ... in order, then a fixed shuffle tree.
+// The groups need not cover a contiguous range of matrices: launches for
+// other matrices may run concurrently and own the rest of the arrays.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_finalize(EwArgs a, const double* partials,
                                                        double* norms, float* R, uint32_t* flags,
                                                        uint32_t bit) {
-  int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   int gi = 0;
   while (gi < a.ngroups && t >= a.g[gi].count) t -= a.g[gi++].count;
-  if (gi >= a.ngroups) return;
+  if (gi >= a.ngroups) return;  // uniform for the wave
   const int64_t mat = (int64_t)a.g[gi].first + t;
   const int bpm = a.g[gi].bpm;
   const double* p = partials + mat * kMaxPartials;
   double s = 0.0;
-  for (int c = 0; c < bpm; ++c) s += p[c];
-  const double nrm = sqrt(s);
-  norms[mat] = nrm;
-  if (R) R[mat] = (float)nrm;
-  if (flags && !isfinite(nrm)) atomicOr(flags, bit);
+  for (int c = lane; c < bpm; c += 64) s += p[c];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) {
+    const double nrm = sqrt(s);
+    norms[mat] = nrm;
+    if (R) R[mat] = (float)nrm;
+    if (flags && !isfinite(nrm)) atomicOr(flags, bit);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -703,7 +709,8 @@ hipError_t launch_finalize(const EwArgs& a, const double* partials, double* norm
                            hipStream_t s, uint32_t* flags, uint32_t bit) {
   int64_t n = 0;
   for (int i = 0; i < a.ngroups; ++i) n += a.g[i].count;
-  const int blocks = (int)((n + kThreads - 1) / kThreads);
+  const int per_block = kThreads / 64;  // one wave per matrix
+  const int blocks = (int)((n + per_block - 1) / per_block);
   hipLaunchKernelGGL(k_finalize, dim3(blocks), dim3(kThreads), 0, s, a, partials, norms, R, flags,
                      bit);
   return hipGetLastError();
