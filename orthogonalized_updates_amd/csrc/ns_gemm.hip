@@ -19,8 +19,10 @@
 // stages. The apply reads its X operand K-major with
 // transposed LDS reads (ds_read_b64_tr_b16), so X has one layout; the fp32
 // a*X or b*A term is folded into the accumulators from the operand stream.
-// Row-major outputs are stored straight from registers, transposed ones
-// (mirrored tiles, O of tall matrices) staged through the idle ring.
+// Row-major outputs are stored straight from registers; transposed ones
+// (mirrored tiles, O of tall matrices) too in the bf16 kernel (after a lane
+// exchange), and staged through the idle ring in the split one. Where the
+// polynomial is folded (B' = a*I + B), the apply has no a*X term.
 // In the bf16 kernel, diagonal tiles of the symmetric products compute three
 // quadrants and mirror the fourth, and the last positions of every XCD's
 // tile list are claimed at run time (tail balancing, see GemmArgs::sched).
@@ -973,16 +975,6 @@ __device__ __forceinline__ u32x4 pair_halves(uint32_t x0, uint32_t x1, uint32_t 
   return hi ? u32x4{b0, b1, y0, y1} : u32x4{x0, x1, a0, a1};
 }
 
-// Chunk permutation of the transposed-output staging (row r: 512 bytes, 32
-// chunks of 16 bytes; chunk k stored at k ^ ot_swz(r)). The writes of one
-// 16-lane pass cover 16 consecutive rows with one chunk each, the reads 4
-// consecutive rows with 4 chunks each: rotating the low 4 bits of r keeps
-// both on 16 distinct 16-byte slots (r & 31 left the reads 4-way
-// conflicted).
-__device__ __forceinline__ int ot_swz(int r) {
-  return (r & 16) | ((r & 3) << 2) | ((r >> 2) & 3);
-}
-
 // Main loop: as pingpong (same phases, barriers and refills), with one
 // 32-k fragment set per stage. The E term: accumulator rows 16 mi .. +15 lie
 // in one stage, read as 4 consecutive k of the lane's column (transposed
@@ -1073,7 +1065,8 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
 // The kernel: tile mapping, operand pointers, DMA prologue and scaling as in
 // k_ns_gemm_bf16; the epilogue stores row-major output from registers after
 // a quad transpose and a pairwise exchange (lane: 8 columns of one row, 16
-// bytes) and stages the transposed output through the ring.
+// bytes), and transposed output from registers after an exchange between
+// lanes l and l^16 (lane: 8 rows of one column, 16 bytes).
 template <int MODE>
 __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   constexpr bool kSym = (MODE != kApply);
@@ -1192,8 +1185,6 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
           v += args.diag;
         vh[mi][ni][q] = (__bf16)v;
       }
-  char* stg = const_cast<char*>(ring);
-  auto srow = [&](int row) -> char* { return stg + (row >> 6) * kStage + (row & 63) * 512; };
   char* O1 = g.offO1 < 0 ? nullptr : const_cast<char*>(blk) + g.offO1;
   char* O2 = g.offO2 < 0 ? nullptr : const_cast<char*>(blk) + g.offO2;
   char* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;
@@ -1223,56 +1214,40 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
         *reinterpret_cast<u32x4*>(region + (int64_t)((wnc + 32 * p) >> 5) * kPanel + row * kPRow + (chunk << 4)) = d;
       }
   }
-  if (diag && O1) {
-    // lower-left quadrant (rows 128-255, columns 0-127) = transpose of the
-    // upper-right one: staging row i holds column 128 + i of the tile's rows
-    // 0-127, i.e. row 128 + i of the quadrant (the main loop's last barrier
-    // retired every fragment read, so the ring is free)
-    if (wave == 2 || wave == 3) {
+  // Transposed outputs (the mirror of an off-diagonal Gram or polynomial
+  // tile, the lower-left quadrant of a diagonal one, O of a tall matrix)
+  // straight from registers. Element (R, C) of the tile goes to row C,
+  // column R of the transposed tile: panel R/32, panel row C. For blocks
+  // 2m and 2m+1 (tile rows 32m .. 32m+31 of the wave) and one block column,
+  // lane l holds rows 4g .. 4g+3 of each (g = l/16) in column l%16; lanes l
+  // and l^16 swap one block's values so that each holds 8 consecutive rows
+  // of its column (g = 0, 1, 2, 3: rows 0-7, 16-23, 8-15, 24-31), and one
+  // 16-byte store per lane writes 16 whole 64-byte panel rows (1 KB,
+  // contiguous), as the row-major pass does. Staging through the ring cost
+  // two barriers and an LDS round trip per tile.
+  auto store_transposed = [&](char* region) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int g = lane >> 4;
+    const bool odd = (g & 1) != 0;
+    const int cbyte = ((g & 1) << 5) | ((g & 2) << 3);  // 0, 32, 16, 48
 #pragma unroll
-      for (int mi = 0; mi < kMT; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < kNT; ++ni) {
-          const int r = wn0 + 16 * ni + (lane & 15) - 128;
-          const int row0 = 16 * mi + 4 * (lane >> 4);
-          const int off = ((((row0 >> 3) ^ ot_swz(r & 31)) << 4) | ((row0 & 7) << 1));
-          *reinterpret_cast<bf16x4*>(srow(r) + off) = vh[mi][ni];
-        }
-    }
-    phase_barrier<>();
-    char* region = O1 + (int64_t)bi * kBM * g.ldo1 * 2 + (int64_t)bj * 8 * kPanel;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + i * 512;
-      const int row = id >> 4, c = id & 15;  // quadrant row, 16-byte chunk (8 columns)
-      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ ot_swz(row & 31)) << 4));
-      *reinterpret_cast<u32x4*>(region + (int64_t)(c >> 2) * kPanel + (128 + row) * kPRow + ((c & 3) << 4)) = d;
-    }
-  }
-  if (OT) {
-    // staging only: the ring is free after the main loop's last barrier, and a
-    // barrier without a vmcnt wait lets the row-major stores above drain
-    phase_barrier<>();
-#pragma unroll
-    for (int mi = 0; mi < kMT; ++mi)
+    for (int m = 0; m < kMT / 2; ++m)
 #pragma unroll
       for (int ni = 0; ni < kNT; ++ni) {
-        const int col = wn0 + 16 * ni + (lane & 15);
-        const int row0 = wm0 + 16 * mi + 4 * (lane >> 4);
-        const int off = ((((row0 >> 3) ^ ot_swz(col & 31)) << 4) | ((row0 & 7) << 1));
-        *reinterpret_cast<bf16x4*>(srow(col) + off) = vh[mi][ni];
+        const u32x2 x = __builtin_bit_cast(u32x2, vh[2 * m][ni]);
+        const u32x2 y = __builtin_bit_cast(u32x2, vh[2 * m + 1][ni]);
+        const u32x2 send = odd ? x : y;
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)send.x, 16, 64);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)send.y, 16, 64);
+        const u32x4 d = odd ? u32x4{r0, r1, y.x, y.y} : u32x4{x.x, x.y, r0, r1};
+        char* dst = region + (int64_t)((wm0 >> 5) + m) * kPanel +
+                    (wnc + 16 * ni + (lane & 15)) * kPRow + cbyte;
+        *reinterpret_cast<u32x4*>(dst) = d;
       }
-    phase_barrier<>();
-    char* region = OT + (int64_t)bj * kBM * ldT * 2 + (int64_t)bi * 8 * kPanel;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int id = tid + i * 512;
-      const int row = (id & 1023) >> 2;
-      const int c = ((id >> 10) << 2) | (id & 3);
-      const u32x4 d = *reinterpret_cast<const u32x4*>(srow(row) + ((c ^ ot_swz(row & 31)) << 4));
-      *reinterpret_cast<u32x4*>(region + (int64_t)id * 16) = d;
-    }
-  }
+  };
+  if (diag && O1 && (wave == 2 || wave == 3))
+    store_transposed(O1 + (int64_t)bj * kBM * g.ldo1 * 2 + (int64_t)bi * 8 * kPanel);
+  if (OT) store_transposed(OT + (int64_t)bj * kBM * ldT * 2 + (int64_t)bi * 8 * kPanel);
 }
 }  // namespace m16
 
