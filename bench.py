@@ -171,15 +171,24 @@ def parity_numbers(i, shape, x, o_o, m_o, w_o, mom_bf16):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi) on a host thread while the
-    timed steps run; the GEMMs are about 85 % of that time. Reports the
-    mean, min and max of the samples in MHz, or why it could not."""
+    """Samples the GPU's graphics clock and socket power (amdsmi) on a host
+    thread while the timed steps run, and reads the firmware's power-limit
+    residency counters before and after. Reports the clock's mean, min and
+    max in MHz, the mean of the power samples in W against the power cap, and
+    the share of the firmware's accumulation ticks spent at the package power
+    limit (the firmware refreshes these about once a second, so a short timed
+    region gives few distinct power values), or why it could not."""
 
-    def __init__(self, period_s=0.002):
+    def __init__(self, period_s=0.002, power_every=25):
         import threading
         self.period = period_s
+        self.power_every = power_every
         self.samples = []
+        self.power = []
         self.error = None
+        self.cap_w = None
+        self.m0 = self.m1 = None
+        self.t0 = self.t1 = None
         self._stop = threading.Event()
         self._thread = None
         try:
@@ -189,23 +198,52 @@ class ClockSampler:
             self._h = amdsmi.amdsmi_get_processor_handles()[0]
         except Exception as e:  # pragma: no cover - depends on the machine
             self.error = f"amdsmi unavailable: {e}"[:160]
+            return
+        try:
+            cap = amdsmi.amdsmi_get_power_cap_info(self._h)["power_cap"]
+            self.cap_w = round(cap / 1e6, 1) if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception:  # pragma: no cover
+            self.cap_w = None
 
     def _read(self):
         info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
         return float(info["clk"])
 
+    def _read_power(self):
+        try:
+            w = self._smi.amdsmi_get_power_info(self._h)["current_socket_power"]
+            return float(w) if isinstance(w, (int, float)) else None
+        except Exception:  # pragma: no cover
+            return None
+
+    def _metrics(self):
+        try:
+            m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+            return {k: m.get(k) for k in ("accumulation_counter", "ppt_residency_acc",
+                                          "socket_thm_residency_acc")}
+        except Exception:  # pragma: no cover
+            return None
+
     def _run(self):
+        n = 0
         while not self._stop.is_set():
             try:
                 self.samples.append(self._read())
             except Exception as e:  # pragma: no cover
                 self.error = f"clock read failed: {e}"[:160]
                 return
+            if n % self.power_every == 0:
+                w = self._read_power()
+                if w is not None:
+                    self.power.append(w)
+            n += 1
             self._stop.wait(self.period)
 
     def __enter__(self):
         import threading
         if self.error is None:
+            self.m0 = self._metrics()
+            self.t0 = time.perf_counter()
             self._thread = threading.Thread(target=self._run, daemon=True)
             self._thread.start()
         return self
@@ -214,12 +252,34 @@ class ClockSampler:
         self._stop.set()
         if self._thread is not None:
             self._thread.join()
+            self.t1 = time.perf_counter()
+            self.m1 = self._metrics()
         try:
             if self.error is None:
                 self._smi.amdsmi_shut_down()
         except Exception:  # pragma: no cover
             pass
         return False
+
+    def power_summary(self):
+        out = {"source": "amdsmi current socket power, sampled during the timed steps",
+               "cap_w": self.cap_w, "w_mean": None, "w_max": None, "samples": len(self.power),
+               "ppt_limit_share": None}
+        if self.power:
+            out["w_mean"] = round(sum(self.power) / len(self.power), 1)
+            out["w_max"] = max(self.power)
+        try:
+            dacc = self.m1["accumulation_counter"] - self.m0["accumulation_counter"]
+            dppt = self.m1["ppt_residency_acc"] - self.m0["ppt_residency_acc"]
+            if dacc > 0:
+                out["ppt_limit_share"] = round(dppt / dacc, 3)
+                out["ppt_ticks"] = int(dacc)
+            else:
+                out["note"] = "the firmware's residency counters did not advance in the timed region"
+        except Exception:
+            out["note"] = "power-limit residency counters unavailable"
+        out["window_s"] = round(self.t1 - self.t0, 3) if self.t0 and self.t1 else None
+        return out
 
     def summary(self):
         if not self.samples:
@@ -616,7 +676,8 @@ def main() -> int:
     }
     result["selfcheck"] = {"sphere_max_abs_dev": sphere, "sphere_bar": 1e-5,
                            "matrices": wl.n_matrices}
-    result["env"] = {**runtime_versions(), "gfx_clock": clock.summary()}
+    result["env"] = {**runtime_versions(), "gfx_clock": clock.summary(),
+                     "power": clock.power_summary()}
     if not args.no_cpu_baseline:
         # one more GPU step, untimed, whose inputs and results the oracle
         # leg takes for one matrix of each distinct shape

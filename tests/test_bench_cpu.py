@@ -124,4 +124,7 @@ def test_clock_sampler_without_a_gpu_reports_why():
         pass
     rec = c.summary()
     assert rec["source"].startswith("amdsmi") and (rec["mhz_mean"] is not None or rec["note"])
+    pw = c.power_summary()
+    assert {"cap_w", "w_mean", "ppt_limit_share", "window_s"} <= set(pw)
+    assert pw["ppt_limit_share"] is not None or pw["note"]
     assert bench.runtime_versions()["rocm"]
