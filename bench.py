@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -44,6 +45,9 @@ METRIC_ADAMW = ("AdamW step time & params updated/s (non-matrix parameters of th
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+
+POWER_SETTLE_S = 1.2
 
 
 def ns_flops(shapes, k):
@@ -172,17 +176,19 @@ def parity_numbers(i, shape, x, o_o, m_o, w_o, mom_bf16):
 
 class ClockSampler:
     """Samples the GPU's graphics clock and socket power (amdsmi) on a host
-    thread while the timed steps run, and reads the firmware's power-limit
-    residency counters before and after. Reports the clock's mean, min and
-    max in MHz, the mean of the power samples in W against the power cap, and
-    the share of the firmware's accumulation ticks spent at the package power
-    limit (the firmware refreshes these about once a second, so a short timed
-    region gives few distinct power values), or why it could not."""
+    thread while steps run, after dropping the first `settle_s` seconds, and
+    reads the firmware's power-limit residency counters at the start and end
+    of the sampled window. Reports the clock's mean, min and max in MHz, the
+    mean of the power samples in W against the power cap, and the share of
+    the firmware's accumulation ticks spent at the package power limit, or
+    why it could not. The firmware refreshes all of these about once a
+    second, so the window has to span a few seconds."""
 
-    def __init__(self, period_s=0.002, power_every=25):
+    def __init__(self, period_s=0.002, power_every=25, settle_s=0.0):
         import threading
         self.period = period_s
         self.power_every = power_every
+        self.settle = settle_s
         self.samples = []
         self.power = []
         self.error = None
@@ -226,6 +232,13 @@ class ClockSampler:
 
     def _run(self):
         n = 0
+        start = time.perf_counter()
+        while not self._stop.is_set() and time.perf_counter() - start < self.settle:
+            self._stop.wait(self.period)
+        if self._stop.is_set():
+            return
+        self.m0 = self._metrics()
+        self.t0 = time.perf_counter()
         while not self._stop.is_set():
             try:
                 self.samples.append(self._read())
@@ -242,8 +255,6 @@ class ClockSampler:
     def __enter__(self):
         import threading
         if self.error is None:
-            self.m0 = self._metrics()
-            self.t0 = time.perf_counter()
             self._thread = threading.Thread(target=self._run, daemon=True)
             self._thread.start()
         return self
@@ -252,8 +263,9 @@ class ClockSampler:
         self._stop.set()
         if self._thread is not None:
             self._thread.join()
-            self.t1 = time.perf_counter()
-            self.m1 = self._metrics()
+            if self.t0 is not None:
+                self.t1 = time.perf_counter()
+                self.m1 = self._metrics()
         try:
             if self.error is None:
                 self._smi.amdsmi_shut_down()
@@ -262,7 +274,7 @@ class ClockSampler:
         return False
 
     def power_summary(self):
-        out = {"source": "amdsmi current socket power, sampled during the timed steps",
+        out = {"source": "amdsmi current socket power, sampled on a host thread",
                "cap_w": self.cap_w, "w_mean": None, "w_max": None, "samples": len(self.power),
                "ppt_limit_share": None}
         if self.power:
@@ -286,7 +298,7 @@ class ClockSampler:
             return {"source": "amdsmi gfx clock", "mhz_mean": None,
                     "note": self.error or "no samples"}
         v = self.samples
-        return {"source": "amdsmi gfx clock, sampled on a host thread during the timed steps",
+        return {"source": "amdsmi gfx clock, sampled on a host thread",
                 "samples": len(v), "mhz_mean": round(sum(v) / len(v), 1),
                 "mhz_min": min(v), "mhz_max": max(v)}
 
@@ -508,6 +520,9 @@ def main() -> int:
     ap.add_argument("--weight-decay", type=float, default=0.1,
                     help="weight decay of the muon_wd variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power-window", type=float, default=3.5,
+                    help="seconds of untimed steps after the timed ones over which the clock, "
+                         "power and power-limit residency are read (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
@@ -578,16 +593,15 @@ def main() -> int:
         events.append(evs)
     torch.cuda.synchronize(dev)
 
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            if args.variant == "muon_wd":
-                opt.step_muon_wd(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta,
-                                 args.weight_decay, k, events=events[s])
-            else:
-                opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
-        torch.cuda.synchronize(dev)
-        t1 = time.perf_counter()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        if args.variant == "muon_wd":
+            opt.step_muon_wd(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta,
+                             args.weight_decay, k, events=events[s])
+        else:
+            opt.step_timed(W, G[(args.warmup + s) % pool], M, wl.lr, wl.beta, k, events[s])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = 1e3 * elapsed / args.steps
 
@@ -596,6 +610,21 @@ def main() -> int:
     if args.variant == "muonh":
         norms = torch.stack([torch.linalg.vector_norm(w.double()) for w in W])
         sphere = float((norms / opt.R.double() - 1.0).abs().max())
+
+    # Clock and power under this load. The firmware refreshes amdsmi's
+    # readings about once a second, which the timed steps (under a second by
+    # default) do not span, so they are read over untimed steps of the same
+    # work run after them, dropping the first POWER_SETTLE_S seconds.
+    n_pw = 0
+    if args.power_window > 0:
+        n_pw = max(1, int(math.ceil(args.power_window / max(elapsed / args.steps, 1e-4))))
+    with ClockSampler(settle_s=min(POWER_SETTLE_S, 0.4 * args.power_window)) as clock:
+        for s in range(n_pw):
+            if args.variant == "muon_wd":
+                opt.step_muon_wd(W, G[s % pool], M, wl.lr, wl.beta, args.weight_decay, k)
+            else:
+                opt.step(W, G[s % pool], M, wl.lr, wl.beta, k)
+        torch.cuda.synchronize(dev)
 
     # Phase durations from the events recorded inside the timed steps.
     pre = post = 0.0
@@ -677,7 +706,9 @@ def main() -> int:
     result["selfcheck"] = {"sphere_max_abs_dev": sphere, "sphere_bar": 1e-5,
                            "matrices": wl.n_matrices}
     result["env"] = {**runtime_versions(), "gfx_clock": clock.summary(),
-                     "power": clock.power_summary()}
+                     "power": clock.power_summary(),
+                     "clock_power_window": f"{n_pw} untimed steps after the timed ones; samples "
+                                           f"after the first {min(POWER_SETTLE_S, 0.4 * args.power_window):.1f} s"}
     if not args.no_cpu_baseline:
         # one more GPU step, untimed, whose inputs and results the oracle
         # leg takes for one matrix of each distinct shape
