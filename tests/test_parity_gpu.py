@@ -128,6 +128,32 @@ def test_ragged_groups(prec, k):
     run_host_workload(RAGGED, steps=3, k=k, prec=prec, wid=51, label=f"ragged k={k} {prec}")
 
 
+def random_shapes(seed: int = 2024, groups: int = 16):
+    """Seeded shape groups that land on and next to tile boundaries: each
+    side is 256k - 1, 256k or 256k + 1 (k = 1 .. 4) or uniform in [32, 1300);
+    every side at least 32 (the bf16 floor of these stays near 1e-2, below
+    the 2e-2 bar); odd-numbered groups hold two matrices."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for gi in range(groups):
+        dims = []
+        for _ in range(2):
+            if rng.random() < 0.5:
+                d = 256 * int(rng.integers(1, 5)) + int(rng.integers(-1, 2))
+            else:
+                d = int(rng.integers(32, 1300))
+            dims.append(max(32, d))
+        shapes += [tuple(dims)] * (1 + gi % 2)
+    return shapes
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_random_shape_sweep(prec):
+    shapes = random_shapes()
+    say(f"[random shapes] {shapes}")
+    run_host_workload(shapes, steps=2, k=5, prec=prec, wid=77, label=f"random shapes {prec}")
+
+
 # 40 distinct shapes: more shape groups than one launch descriptor holds
 # (16), so every phase runs as several grouped launches, and the finalize
 # kernels see matrix ranges that are not the whole plan.
@@ -617,6 +643,28 @@ def test_muon_wd_ragged_groups(prec, k):
         torch.cuda.synchronize()
         check_muon_step(opt, W, M, G_host, W_pre, M_pre, 0.02, 0.95, 0.1, k, prec, idx,
                         f"muon-wd {prec} k={k} step {st}")
+
+
+def test_muon_wd_random_shape_sweep():
+    need_gpu()
+    dev = torch.device("cuda")
+    shapes = random_shapes()
+    wl = workloads.Workload(wid=78, name="muon", shapes=tuple(shapes), steps=2, ns_iters=(5,),
+                            lr=0.02, beta=0.95, w_std=0.02, g_std=0.01, heavy_tail=False)
+    opt = make_opt(shapes, "bf16")
+    W = [torch.from_numpy(workloads.host_weight(wl, i)).to(dev) for i in range(len(shapes))]
+    M = [torch.zeros(s, device=dev) for s in shapes]
+    idx = list(range(len(shapes)))
+    for st in range(2):
+        G_host = [workloads.host_grad(wl, i, st) for i in idx]
+        G = [torch.from_numpy(g).to(dev) for g in G_host]
+        W_pre = {i: W[i].cpu().numpy() for i in idx}
+        M_pre = {i: M[i].cpu().numpy() for i in idx}
+        say(f"[muon-wd random shapes] step {st}")
+        opt.step_muon_wd(W, G, M, 0.02, 0.95, 0.1, 5)
+        torch.cuda.synchronize()
+        check_muon_step(opt, W, M, G_host, W_pre, M_pre, 0.02, 0.95, 0.1, 5, "bf16", idx,
+                        f"muon-wd random shapes step {st}")
 
 
 @pytest.mark.parametrize("prec", ["bf16", "fp32"])
