@@ -169,7 +169,11 @@ int muonh_init(const muonh_plan* plan, float* const* W, float* R, void* workspac
  * lr: finite, >= 0 (the caller's effective rate; the model card applies a
  *     10x multiplier to the matrix group, section "Training").
  * beta: in [0, 1).  ns_iters: in [0, MUONH_MAX_NS_ITERS].
- * Results are bitwise deterministic for a given plan and input.
+ * Results are bitwise deterministic for a given plan and input. A matrix's
+ * result does not depend on the other matrices of the plan, except that bf16
+ * Newton-Schulz phases whose GEMMs have few 256x256 tiles (at most 128)
+ * run 128x128 tiles, which can change the last bits of the polynomial's
+ * diagonal blocks and so of O (well within the tolerances).
  * Errors: MUONH_EINVAL, MUONH_EWORKSPACE, MUONH_EHIP.
  */
 int muonh_step(const muonh_plan* plan, float* const* W, const void* const* G, void* const* M,

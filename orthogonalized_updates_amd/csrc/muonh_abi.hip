@@ -239,7 +239,22 @@ std::vector<EwArgs> make_ew(const muonh_plan* p, char* ws, EwKind kind, int ns_i
 // GEMM descriptors for one Newton-Schulz phase, heaviest groups first.
 std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, int it, int iters,
                                 const double* xnorm = nullptr) {
-  const int T = gemm_tile(p->prec);
+  // bf16 phases whose 256x256 tiles would occupy at most half of the CUs
+  // run 128x128 tiles (GemmArgs::small): four times as many, so that a
+  // single matrix or a few small ones still spread over the chip
+  int T = gemm_tile(p->prec);
+  bool small = false;
+  if (p->prec == kBf16) {
+    int64_t big = 0;
+    for (const GroupPlan& G : p->groups) {
+      const int64_t ts = G.sp / 256, tl = G.lp / 256;
+      big += (int64_t)G.count * (mode == kApply ? ts * tl : ts * (ts + 1) / 2);
+    }
+    if (2 * big <= kCUs) {
+      T = 128;
+      small = true;
+    }
+  }
   // bf16 / split: the buffer iteration `it` reads X from (X0 goes to buffer
   // 1 - iters%2, so that the last apply writes buffer 1)
   const int src = (1 - (iters & 1)) ^ (it & 1);
@@ -335,6 +350,7 @@ std::vector<GemmArgs> make_gemm(const muonh_plan* p, char* ws, GemmMode mode, in
     }
     a.ngroups = (int)(g1 - g0);
     a.ntiles = (int)tiles;
+    a.small = small ? 1 : 0;
     a.xnorm = mode == kPoly ? nullptr : xnorm;
     a.xcd_map = p->prec == kFp32 ? 0 : 1;
     if (a.xcd_map) {

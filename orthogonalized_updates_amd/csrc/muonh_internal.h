@@ -185,6 +185,9 @@ struct GemmArgs {
   int* sched;
   int* sched_clear;
   int xlen[8], xstatic[8];
+  // bf16 launches that 256x256 tiles cannot spread over the CUs run
+  // 128x128 tiles (the group's tm, tn and tiles_per_mat count those).
+  int small;
 };
 
 // Sets the calling thread's muonh_last_error() message; returns `code`.

@@ -26,6 +26,10 @@
 // In the bf16 kernel, diagonal tiles of the symmetric products compute three
 // quadrants and mirror the fourth, and the last positions of every XCD's
 // tile list are claimed at run time (tail balancing, see GemmArgs::sched).
+// Phases with few tiles (a single matrix or a few small ones) run the same
+// kernel on 128x128 tiles (GemmArgs::small): 4 waves in two groups, the same
+// 64-byte panel rows (half of a 256-row panel per tile), a ring of 16 KB
+// stages.
 // fp32 debug: a simpler 128x128 kernel on v_mfma_f32_32x32x2f32 with
 // register-staged double buffering and direct epilogue stores; it reads both
 // operands along K, so that mode keeps X and X^T copies.
@@ -351,13 +355,16 @@ struct DmaSrc {
   uint32_t lds;   // LDS offset of this wave's share within a stage buffer
 };
 
-template <int SH = 2>
+// TM: tile rows (256, or 128 with 4 waves: group 1 is waves 2-3, a stage's
+// B half starts at TM rows).
+template <int SH = 2, int TM = 256>
 __device__ __forceinline__ DmaSrc dma_src(const char* P, const char* Q, int wave, int lane) {
-  const bool isA = wave >= 4;
+  constexpr int kWPG = TM / 64;  // waves per group
+  const bool isA = wave >= kWPG;
   DmaSrc d;
-  d.g = (isA ? P : Q) + (wave & 3) * 4096 + (lane >> 2) * kPRow +
+  d.g = (isA ? P : Q) + (wave & (kWPG - 1)) * 4096 + (lane >> 2) * kPRow +
         (((lane & 3) ^ ((lane >> (2 + SH)) & 3)) << 4);
-  d.lds = (uint32_t)((isA ? 0 : kPanel) + (wave & 3) * 4096);
+  d.lds = (uint32_t)((isA ? 0 : TM * kPRow) + (wave & (kWPG - 1)) * 4096);
   return d;
 }
 
@@ -409,14 +416,14 @@ __device__ __forceinline__ QtSrc qt_src(const char* X, int ldx, int bj, int wave
   return d;
 }
 
-template <bool SPLIT>
+template <bool SPLIT, int TM = 256>
 __device__ __forceinline__ void issue_share_qt(const QtSrc& d, int wave, int kt, uint32_t buf) {
   constexpr int kPK = SPLIT ? 16 : 32;
   const int k0 = kt * kPK;
   const int64_t row_part = (int64_t)(k0 >> 8) * d.rbs + (k0 & 255) * kPRow;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int j = 4 * (wave & 3) + i;  // instruction of the stage
+    const int j = 4 * (wave & (TM / 64 - 1)) + i;  // instruction of the stage
     // bf16: piece j/2, its half j%2 (16 rows each); split: piece j
     const int64_t piece = SPLIT ? (int64_t)j * kPanel : (int64_t)(j >> 1) * kPanel + (j & 1) * 1024;
     const char* g = d.g[i & 1] + row_part + piece;
@@ -940,8 +947,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, (WGM * WGN) / 4) void k_ns_gemm_bf1
 // ---------------------------------------------------------------------------
 namespace m16 {
 using namespace bf;
-constexpr int kMT = 8, kNT = 4;  // 16x16 blocks of a 128 x 64 wave tile
-struct F { bf16x8 a[kMT], b[kNT]; };
+// 16x16 blocks of a wave tile of (TM / 2) x 64: TM / 32 rows of kNT blocks
+constexpr int kNT = 4;
+template <int MT>
+struct F { bf16x8 a[MT], b[kNT]; };
 // Lane parts of LDS addresses: f row fragments (row l%16, chunk l/16,
 // swizzled); q transposed B fragment reads of the apply (rows 8(l/16) +
 // (l%16)/4, columns 4(l%4) .. +3 of a 16-column block); e transposed E reads
@@ -951,13 +960,14 @@ struct Offs { int f, q, e; };
 // QT stage for this kernel: as qt_src (bf16), but rows with bit 3 set hold
 // their two 32-byte halves swapped, so that the two 16-lane groups of a
 // transposed read (rows 8 apart, same columns) use different banks.
+template <int TM = 256>
 __device__ __forceinline__ QtSrc qt_src16(const char* X, int ldx, int bj, int wave, int lane) {
   QtSrc d;
-  const char* base = X + (int64_t)bj * 8 * kPanel;
+  const char* base = X + (int64_t)bj * (TM / 32) * kPanel;
   const int lo = (lane >> 2) * kPRow + (((lane & 3) ^ (2 * ((lane >> 5) & 1))) << 4);
   d.g[0] = d.g[1] = base + lo;
   d.rbs = (int64_t)(ldx / 32) * kPanel;
-  d.lds = (uint32_t)(kPanel + (wave & 3) * 4096);
+  d.lds = (uint32_t)(TM * kPRow + (wave & (TM / 64 - 1)) * 4096);
   return d;
 }
 
@@ -981,18 +991,20 @@ __device__ __forceinline__ u32x4 pair_halves(uint32_t x0, uint32_t x1, uint32_t 
 // read for the apply, a plain 8-byte read of A's row for the polynomial).
 // NT: 16-column blocks the wave computes (kNT, or 2 for the second group on
 // a diagonal tile of the symmetric modes).
-template <int G, bool E_TERM, bool QT, int NT = kNT>
+template <int TM, int G, bool E_TERM, bool QT, int NT = kNT>
 __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc, int nk,
                                            const char* ring, uint32_t ring_lds, int wave, int wm0,
                                            int wn0, const Offs& o, int lane, int bi, float seed,
-                                           f32x4 (&acc)[kMT][kNT]) {
-  F f;
+                                           f32x4 (&acc)[TM / 32][kNT]) {
+  constexpr int kMT = TM / 32;
+  constexpr int kStg = 2 * TM * kPRow;  // stage bytes: A rows, then B rows
+  F<kMT> f;
   const int g = lane >> 4;
   auto take_e = [&](const char* buf, int kt) {
     // accumulator row rho (from wm0) takes its E value from stage row rho - r
-    const int r = kt * 32 - 256 * bi - wm0;  // a multiple of 32
+    const int r = kt * 32 - TM * bi - wm0;  // a multiple of 32
     if (r < 0 || r >= kMT * 16) return;
-    const char* lb = buf + kPanel;
+    const char* lb = buf + TM * kPRow;
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi) {
       if (16 * mi < r || 16 * mi >= r + 32) continue;
@@ -1014,7 +1026,7 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
     }
   };
   auto load = [&](int kt) {
-    const char* buf = ring + (kt & (kNBuf - 1)) * kStage;
+    const char* buf = ring + (kt & (kNBuf - 1)) * kStg;
 #pragma unroll
     for (int mi = 0; mi < kMT; ++mi)
       f.a[mi] = *reinterpret_cast<const bf16x8*>(buf + (wm0 + 16 * mi) * kPRow + o.f);
@@ -1022,10 +1034,10 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
     for (int ni = 0; ni < NT; ++ni) {
       const int n0 = wn0 + 16 * ni;
       if (QT) {
-        const char* p = buf + kPanel + (n0 >> 5) * 2048 + o.q + ((((n0 & 31) << 1) ^ (32 * (g & 1))));
+        const char* p = buf + TM * kPRow + (n0 >> 5) * 2048 + o.q + ((((n0 & 31) << 1) ^ (32 * (g & 1))));
         f.b[ni] = cat8(read_tr(p), read_tr(p + 4 * kPRow));
       } else {
-        f.b[ni] = *reinterpret_cast<const bf16x8*>(buf + kPanel + n0 * kPRow + o.f);
+        f.b[ni] = *reinterpret_cast<const bf16x8*>(buf + TM * kPRow + n0 * kPRow + o.f);
       }
     }
     if (E_TERM && seed != 0.f) take_e(buf, kt);
@@ -1038,8 +1050,8 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
   };
   auto refill = [&](int kt) {
-    const uint32_t buf = ring_lds + (kt & (kNBuf - 1)) * kStage;
-    if (QT && G == 1) issue_share_qt<false>(qsrc, wave, kt, buf);
+    const uint32_t buf = ring_lds + (kt & (kNBuf - 1)) * kStg;
+    if (QT && G == 1) issue_share_qt<false, TM>(qsrc, wave, kt, buf);
     else issue_share(dsrc, kt, buf);
   };
   if (G == 0) load(0);
@@ -1067,14 +1079,17 @@ __device__ __forceinline__ void pingpong16(const DmaSrc& dsrc, const QtSrc& qsrc
 // a quad transpose and a pairwise exchange (lane: 8 columns of one row, 16
 // bytes), and transposed output from registers after an exchange between
 // lanes l and l^16 (lane: 8 rows of one column, 16 bytes).
-template <int MODE>
-__global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
+template <int MODE, int TM>
+__global__ __launch_bounds__(2 * TM, 2) void k_ns_gemm_m16(GemmArgs args) {
   constexpr bool kSym = (MODE != kApply);
   constexpr bool kQT = (MODE == kApply);
-  __shared__ __attribute__((aligned(1024))) char ring[kNBuf * kStage];
+  constexpr int kMT = TM / 32;        // 16-row blocks of a wave tile
+  constexpr int kWPG = TM / 64;       // waves per group
+  constexpr int kStg = 2 * TM * kPRow;
+  __shared__ __attribute__((aligned(1024))) char ring[kNBuf * kStg];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / 4, wn = wave - (wave / 4) * 4;
+  const int wm = wave / kWPG, wn = wave - (wave / kWPG) * kWPG;
   int gi, local;
   int vb = blockIdx.x;  // position 8 * slot + XCD in the XCD lists
   if (args.sched) {
@@ -1122,15 +1137,24 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   int bi, bj;
   tile_coords<kSym>(g, local - mat * g.tiles_per_mat, bi, bj);
   const char* blk = g.base + (int64_t)mat * g.mat_bytes;
-  const char* P = blk + g.offP + (int64_t)bi * kBM * g.ldp * 2;
-  const char* Q = blk + g.offQ + (kQT ? 0 : (int64_t)bj * kBN * g.ldq * 2);
+  // operand rows of the tile: a 256-row panel block, and for 128-row tiles
+  // the half of it (panel rows are 64 bytes)
+  const char* P;
+  const char* Q;
+  if constexpr (TM == 256) {
+    P = blk + g.offP + (int64_t)bi * kBM * g.ldp * 2;
+    Q = blk + g.offQ + (kQT ? 0 : (int64_t)bj * kBN * g.ldq * 2);
+  } else {
+    P = blk + g.offP + (int64_t)(bi >> 1) * 256 * g.ldp * 2 + (bi & 1) * TM * kPRow;
+    Q = blk + g.offQ + (kQT ? 0 : (int64_t)(bj >> 1) * 256 * g.ldq * 2 + (bj & 1) * TM * kPRow);
+  }
   f32x4 acc[kMT][kNT];
 #pragma unroll
   for (int mi = 0; mi < kMT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < kNT; ++ni) acc[mi][ni] = f32x4{};
   const int nk = g.K / 32;
-  const int wm0 = wm * 128, wn0 = wn * 64;
+  const int wm0 = wm * (TM / 2), wn0 = wn * 64;
   Offs o;
   {
     const int i = lane & 15, gg = lane >> 4;
@@ -1138,14 +1162,15 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
     o.q = (8 * gg + (i >> 2)) * kPRow + 8 * (i & 3);
     o.e = (4 * gg + (i >> 2)) * kPRow + 8 * (i & 3);
   }
-  // apply: waves 0-3 refill the A panel (dma_src takes waves 4-7 for A)
-  const DmaSrc dsrc = dma_src<1>(P, Q, kQT ? (wave ^ 4) : wave, lane);
-  const QtSrc qsrc = qt_src16(Q, g.ldq, bj, wave, lane);
+  // apply: the first group refills the A panel (dma_src takes the second
+  // group for A)
+  const DmaSrc dsrc = dma_src<1, TM>(P, Q, kQT ? (wave ^ kWPG) : wave, lane);
+  const QtSrc qsrc = qt_src16<TM>(Q, g.ldq, bj, wave, lane);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
 #pragma unroll
   for (int st = 0; st < kNBuf; ++st) {
-    if (kQT && wave >= 4) issue_share_qt<false>(qsrc, wave, st, ring_lds + st * kStage);
-    else issue_share(dsrc, st, ring_lds + st * kStage);
+    if (kQT && wave >= kWPG) issue_share_qt<false, TM>(qsrc, wave, st, ring_lds + st * kStg);
+    else issue_share(dsrc, st, ring_lds + st * kStg);
   }
   phase_barrier<12>();
   // the E term: a*X in the apply (none where B carries a*I), (b/c)*A in the
@@ -1154,17 +1179,18 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
                      : MODE == kPoly ? args.c0 / args.c1 : 0.f;
   // Diagonal tile of a symmetric product: its lower-left quadrant is the
   // transpose of the upper-right one, so the second group computes only the
-  // lower-right quadrant (a 128 x 32 strip per wave, half the MFMAs) and the
-  // epilogue mirrors the upper-right quadrant (first group, waves 2 and 3).
+  // lower-right quadrant (a (TM/2) x 32 strip per wave, half the MFMAs) and
+  // the epilogue mirrors the upper-right quadrant (the first group's waves
+  // on its right half).
   const bool diag = kSym && bi == bj;
-  const bool half = diag && wave >= 4;
-  const int wnc = half ? 128 + 32 * (wave - 4) : wn0;  // first column of the wave's strip
-  if (wave < 4)
-    pingpong16<0, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
+  const bool half = diag && wave >= kWPG;
+  const int wnc = half ? TM / 2 + 32 * (wave - kWPG) : wn0;  // first column of the wave's strip
+  if (wave < kWPG)
+    pingpong16<TM, 0, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
   else if (!half)
-    pingpong16<1, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
+    pingpong16<TM, 1, MODE != kGram, kQT>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wn0, o, lane, bi, seed, acc);
   else
-    pingpong16<1, MODE != kGram, kQT, 2>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wnc, o, lane, bi, seed, acc);
+    pingpong16<TM, 1, MODE != kGram, kQT, 2>(dsrc, qsrc, nk, ring, ring_lds, wave, wm0, wnc, o, lane, bi, seed, acc);
 
   float scale = MODE == kPoly ? args.c1 : 1.f;
   if (MODE != kPoly && args.xnorm && g.defer) {
@@ -1189,6 +1215,14 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
   char* O2 = g.offO2 < 0 ? nullptr : const_cast<char*>(blk) + g.offO2;
   char* OT = kSym ? (bi != bj ? O1 : nullptr) : O2;
   const int ldT = kSym ? g.ldo1 : g.ldo2;
+  // output tile (r, c) of a panel-major buffer of leading dimension ld: its
+  // 256-row panel block (and the half of it for 128-row tiles), then its
+  // 32-column panels
+  auto tile_at = [&](char* base, int r, int c, int ld) -> char* {
+    if constexpr (TM == 256) return base + (int64_t)r * kBM * ld * 2 + (int64_t)c * 8 * kPanel;
+    return base + (int64_t)(r >> 1) * 256 * ld * 2 + (r & 1) * TM * kPRow +
+           (int64_t)c * (TM / 32) * kPanel;
+  };
   if (O1) {
     // Blocks ni = 2p and 2p + 1 share one 64-byte panel row: after the
     // exchange, lane l holds columns 8 * (l/8 % 2) .. +7 of block 2p + (l/4 % 2)
@@ -1196,7 +1230,7 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
     // 16 whole panel rows (1 KB, contiguous). With 8-byte stores (half rows)
     // a CU wrote its 128 KB tile 3.5 times slower, and the L2 fetched part of
     // the partially written lines from HBM.
-    char* region = O1 + (int64_t)bi * kBM * g.ldo1 * 2 + (int64_t)bj * 8 * kPanel;
+    char* region = tile_at(O1, bi, bj, g.ldo1);
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const int chunk = ((lane >> 1) & 2) | ((lane >> 3) & 1);  // 16-byte chunk of the panel row
 #pragma unroll
@@ -1245,9 +1279,10 @@ __global__ __launch_bounds__(512, 2) void k_ns_gemm_m16(GemmArgs args) {
         *reinterpret_cast<u32x4*>(dst) = d;
       }
   };
-  if (diag && O1 && (wave == 2 || wave == 3))
-    store_transposed(O1 + (int64_t)bj * kBM * g.ldo1 * 2 + (int64_t)bi * 8 * kPanel);
-  if (OT) store_transposed(OT + (int64_t)bj * kBM * ldT * 2 + (int64_t)bi * 8 * kPanel);
+  // the mirror: waves of the first group on its right half
+  const bool mirror = TM == 256 ? (wave == 2 || wave == 3) : (wave < kWPG && wn >= kWPG / 2);
+  if (diag && O1 && mirror) store_transposed(tile_at(O1, bj, bi, g.ldo1));
+  if (OT) store_transposed(tile_at(OT, bj, bi, ldT));
 }
 }  // namespace m16
 
@@ -1259,11 +1294,14 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s, bool split) {
   if constexpr (std::is_same<T, __bf16>::value) {
     // 256x256 tiles, 8 waves in a 2 x 4 grid (wave tile 128 x 64): bf16 on
     // 16x16x32 MFMAs, split bf16 (hi + lo per 64-byte panel row, three
-    // products per stage) on 32x32x16.
+    // products per stage) on 32x32x16; bf16 launches with few tiles on
+    // 128x128 tiles, 4 waves in a 2 x 2 grid (wave tile 64 x 64).
     if (split)
       hipLaunchKernelGGL((k_ns_gemm_bf16<MODE, 2, 4, true>), dim3(a.grid), dim3(512), 0, s, a);
+    else if (a.small)
+      hipLaunchKernelGGL((m16::k_ns_gemm_m16<MODE, 128>), dim3(a.grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((m16::k_ns_gemm_m16<MODE>), dim3(a.grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((m16::k_ns_gemm_m16<MODE, 256>), dim3(a.grid), dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL((k_ns_gemm<T, kTile32, kTile32, 2, 2, MODE>), dim3(a.ntiles), dim3(256), 0,
                        s, a);

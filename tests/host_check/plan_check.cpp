@@ -35,7 +35,7 @@ int64_t g_nmats = 0;
 int g_eb = 2;       // bytes per logical Newton-Schulz element
 int g_tile = 256;   // GEMM tile edge
 int g_failures = 0;
-long g_gemm_launches = 0, g_ew_launches = 0, g_events = 0;
+long g_gemm_launches = 0, g_ew_launches = 0, g_events = 0, g_small_launches = 0;
 const char* g_case = "";
 
 #define EXPECT(c)                                                                    \
@@ -131,7 +131,10 @@ void check_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a) {
   int64_t tiles = 0;
   for (int i = 0; i < a.ngroups; ++i) {
     const GemmGroup& g = a.g[i];
-    const int T = g_tile;
+    // 128x128 tiles only for bf16 launches whose 256x256 tiles would fill at
+    // most half of the 256 CUs
+    const int T = a.small ? 128 : g_tile;
+    if (a.small) EXPECT(prec == kBf16 && g_tile == 256);
     EXPECT(g.count >= 1 && g.first >= 0 && g.first + g.count <= g_nmats);
     EXPECT(g.K % kPad == 0 && g.K >= kPad);
     EXPECT(g.tile_begin == tiles);
@@ -172,6 +175,19 @@ void check_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a) {
     if (mode == kPoly) EXPECT(g.offE >= 0);
   }
   EXPECT(a.ntiles == tiles);
+  if (prec == kBf16) {
+    // the choice of tile: the phase's 256-tile count (this launch's, when
+    // the phase is one launch) against half of the CUs
+    int64_t big = 0;
+    for (int i = 0; i < a.ngroups; ++i) {
+      const GemmGroup& g = a.g[i];
+      const int64_t f = a.small ? 2 : 1;  // 128-tile grid -> 256-tile grid
+      const int64_t ts = (g.tm + f - 1) / f, tl = (g.tn + f - 1) / f;
+      big += (int64_t)g.count * (sym ? ts * (ts + 1) / 2 : ts * tl);
+    }
+    if (a.small) EXPECT(2 * big <= 256);
+    if (a.small) ++g_small_launches;
+  }
   if (a.xnorm) check_norms(a.xnorm);
   if (mode == kPoly) EXPECT(a.xnorm == nullptr && a.diag == kNsA);
   // every tile exactly once: static slots, then tail claims
@@ -449,7 +465,9 @@ int main() {
     run_plan("4096x14336 set", large, p);
   }
   check_disjoint_brute(12345);
-  std::printf("%ld GEMM launches, %ld elementwise launches checked\n", g_gemm_launches, g_ew_launches);
+  std::printf("%ld GEMM launches (%ld with 128x128 tiles), %ld elementwise launches checked\n",
+              g_gemm_launches, g_small_launches, g_ew_launches);
+  EXPECT(g_small_launches > 0);
   if (g_failures) {
     std::printf("%d failures\n", g_failures);
     return 1;

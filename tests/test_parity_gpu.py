@@ -346,8 +346,11 @@ def test_bitwise_determinism_and_batch_invariance(prec):
 def test_tail_balanced_launches_compute_every_tile():
     # 192 small matrices: every GEMM launch has two or more rounds of tiles,
     # so the last positions of each XCD's tile list are claimed at run time.
-    # Each matrix must come out bit for bit as it does alone (a launch of a
-    # few tiles, fixed deal), over two steps (both counter sets in use).
+    # Each matrix must come out bit for bit as it does in a batch of 64 (one
+    # round of 256x256 tiles or less, fixed deal), over two steps (both
+    # counter sets in use). A matrix alone would run 128x128 tiles, whose
+    # polynomial adds its b*A term into a different triangle of the diagonal
+    # blocks first, so its last bits differ (test_small_tiles_match_large).
     need_gpu()
     shapes = [(512, 512)] * 96 + [(768, 512)] * 96
     dev = torch.device("cuda")
@@ -367,9 +370,43 @@ def test_tail_balanced_launches_compute_every_tile():
 
     w_all, o_all = run(list(range(len(shapes))))
     say("[tail balance] batch done")
-    for i in range(len(shapes)):
+    for b0 in range(0, len(shapes), 64):
+        sel = list(range(b0, b0 + 64))
+        w_b, o_b = run(sel)
+        for j, i in enumerate(sel):
+            assert torch.equal(w_b[j], w_all[i]) and torch.equal(o_b[j], o_all[i]), f"matrix {i}"
+
+
+def test_small_tiles_match_large():
+    # A 512x512 matrix alone runs its Newton-Schulz GEMMs on 128x128 tiles;
+    # in a batch of 64 on 256x256 tiles. Both are parity-tested against the
+    # oracle elsewhere; here the two agree to the bf16 rounding of the
+    # polynomial's diagonal blocks (its b*A term is added into the
+    # accumulator at the stage of the output row, and the two tile sizes
+    # compute different triangles of those blocks directly).
+    need_gpu()
+    shapes = [(512, 512)] * 64
+    dev = torch.device("cuda")
+    W_init = [torch.from_numpy(workloads.host_custom(s, 0.02, (92, i))) for i, s in enumerate(shapes)]
+    G_host = [torch.from_numpy(workloads.host_custom(s, 0.01, (93, i))) for i, s in enumerate(shapes)]
+
+    def run(sel):
+        opt = make_opt([shapes[i] for i in sel], "bf16")
+        W = [W_init[i].to(dev) for i in sel]
+        M = [torch.zeros(shapes[i], device=dev) for i in sel]
+        G = [G_host[i].to(dev) for i in sel]
+        opt.init(W)
+        opt.step(W, G, M, 0.02, 0.95, 5)
+        torch.cuda.synchronize()
+        return [w.cpu() for w in W], [opt.read_update(j).cpu() for j in range(len(sel))]
+
+    w_big, o_big = run(list(range(64)))
+    for i in (0, 17, 63):
         w_1, o_1 = run([i])
-        assert torch.equal(w_1[0], w_all[i]) and torch.equal(o_1[0], o_all[i]), f"matrix {i}"
+        e_o = rel(o_1[0].numpy(), o_big[i].numpy())
+        e_w = rel(w_1[0].numpy(), w_big[i].numpy())
+        say(f"[small vs large tiles] matrix {i}: O {e_o:.2e}, W {e_w:.2e}")
+        assert e_o <= 2e-2 and e_w <= 1e-3, f"matrix {i}: O {e_o:.3e} W {e_w:.3e}"
 
 
 # the tall matrix runs on the transposed layout: equal up to summation order
