@@ -344,12 +344,13 @@ __device__ __forceinline__ void phase_barrier_n(int n) {
 
 // One wave's share of a refill: 64 rows (4 KB) of one operand panel, as 4
 // DMA instructions of 16 rows (1 KB, contiguous in the panel). Group 1
-// (waves 4-7) refills the A panels, group 0 the B panels; wave w takes rows
-// 64*(w%4) .. +63. Lane l fills LDS bytes 16l .. 16l+15 of an instruction's
-// 1 KB block: panel row l/4 of the instruction's 16, position l%4, which must
-// hold chunk (l%4) ^ ((row >> SH) & 3); for every instruction of every wave
-// (row >> SH) & 3 = (l >> (2 + SH)) & 3, so the per-lane source offset is
-// fixed.
+// (waves 4-7; 2-3 for 128-row tiles) refills the A panels, group 0 the B
+// panels; wave w takes rows 64*(w%4) .. +63 (64*(w%2) for 128-row tiles,
+// within the tile's half of the panel). Lane l fills LDS bytes 16l ..
+// 16l+15 of an instruction's 1 KB block: panel row l/4 of the instruction's
+// 16, position l%4, which must hold chunk (l%4) ^ ((row >> SH) & 3); for
+// every instruction of every wave (row >> SH) & 3 = (l >> (2 + SH)) & 3, so
+// the per-lane source offset is fixed.
 struct DmaSrc {
   const char* g;  // per-lane source address of instruction 0, stage 0
   uint32_t lds;   // LDS offset of this wave's share within a stage buffer
@@ -394,7 +395,8 @@ __device__ __forceinline__ void issue_share(const DmaSrc& d, int kt, uint32_t bu
 // mode the two 16-lane groups of a read fall on consecutive pieces, so odd
 // pieces store their two 32-byte halves swapped (chunk ^ 2) to keep the two
 // groups on different banks. Group 0 refills these; wave w takes the 16
-// 1 KB instructions 4*(w%4) .. 4*(w%4)+3 of the stage.
+// 1 KB instructions 4*(w%4) .. 4*(w%4)+3 of the stage (128 columns: the 8
+// instructions 4*(w%2) .. +3).
 struct QtSrc {
   const char* g[2];  // per-lane source of even / odd instructions, tile column block included
   int64_t rbs;       // bytes per 256-row block of X
