@@ -32,8 +32,11 @@ Sphere: | ||W||_F / R - 1 | <= 1e-5 for every matrix (stated).
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import sys
+import threading
+from collections import OrderedDict
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -105,9 +108,54 @@ def assert_o(err, label):
         f"{label}: O tile {err['tile']} rel err {err['e_tile']:.3e} > {err['bar_tile']:.3e}")
 
 
+# The oracle's O depends on the new momentum and the iteration count alone,
+# and on full-size matrices its Newton-Schulz takes seconds to minutes on the
+# host. Runs that differ only in the device's operand precision (bf16 and
+# split-bf16 at the same iteration count, on the same seeded inputs: the fp32
+# momentum does not depend on it) ask for the same O, so the result is kept,
+# keyed on the exact bytes of the new momentum. Only matrices of at least
+# NS_MEMO_MIN_ENTRIES entries are kept, at most NS_MEMO_MAX_BYTES of them
+# (least recently used first out).
+NS_MEMO_MIN_ENTRIES = 1 << 22
+NS_MEMO_MAX_BYTES = 8 << 30
+_ns_memo: "OrderedDict[tuple, np.ndarray]" = OrderedDict()
+_ns_memo_lock = threading.Lock()
+
+
+def oracle_newton_schulz(m_new, k):
+    """oracle.newton_schulz(m_new, k), memoised for large matrices. The
+    returned array is read-only."""
+    m_new = np.ascontiguousarray(m_new, dtype=np.float64)
+    if m_new.size < NS_MEMO_MIN_ENTRIES:
+        return oracle.newton_schulz(m_new, k)
+    digest = hashlib.blake2b(m_new.reshape(-1).view(np.uint8), digest_size=32).digest()
+    key = (m_new.shape, int(k), digest)
+    with _ns_memo_lock:
+        hit = _ns_memo.get(key)
+        if hit is not None:
+            _ns_memo.move_to_end(key)
+            return hit
+    o = oracle.newton_schulz(m_new, k)
+    o.setflags(write=False)
+    with _ns_memo_lock:
+        _ns_memo[key] = o
+        while sum(v.nbytes for v in _ns_memo.values()) > NS_MEMO_MAX_BYTES and len(_ns_memo) > 1:
+            _ns_memo.popitem(last=False)
+    return o
+
+
+def oracle_muonh_step(w, g, m, r, lr, beta, k, mom_bf16=False):
+    """oracle.muonh_step as its three stages, in its order (momentum,
+    Newton-Schulz, projection), with the Newton-Schulz stage memoised.
+    Returns (W_new, M_new, O)."""
+    m_new = oracle.momentum_update(m, g, beta, mom_bf16)
+    o = oracle_newton_schulz(m_new, k)
+    return oracle.hyperball_project(w, o, r, lr), m_new, o
+
+
 def muonh_errors(o_gpu, w_gpu, m_gpu, g, w_pre, m_pre, r, lr, beta, k, prec, mom_bf16=False):
     """Every error of one teacher-forced MuonH step of one matrix, with its bar."""
-    w_o, m_o, o_o = oracle.muonh_step(w_pre, g, m_pre, r, lr, beta, k, mom_bf16=mom_bf16)
+    w_o, m_o, o_o = oracle_muonh_step(w_pre, g, m_pre, r, lr, beta, k, mom_bf16=mom_bf16)
     err = o_errors(o_gpu, o_o, m_o, k, prec)
     m_gpu = np.asarray(m_gpu, dtype=np.float64)
     if mom_bf16:
