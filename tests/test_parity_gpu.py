@@ -400,6 +400,35 @@ def test_tail_balanced_launches_compute_every_tile():
             assert torch.equal(w_b[j], w_all[i]) and torch.equal(o_b[j], o_all[i]), f"matrix {i}"
 
 
+def test_small_tile_launch_with_tail_claims():
+    # Two 2048x2048 matrices: every phase runs 128x128 tiles (at most 128
+    # tiles of 256x256), and the apply's 512 of them are two rounds on 256
+    # CUs, so the last positions of each XCD's list are claimed at run time.
+    # A matrix alone runs the same 128x128 tiles in one round with a fixed
+    # deal, so each must come out bit for bit the same, over two steps.
+    need_gpu()
+    shapes = [(2048, 2048)] * 2
+    dev = torch.device("cuda")
+    W_init = [torch.from_numpy(workloads.host_custom(s, 0.02, (94, i))) for i, s in enumerate(shapes)]
+    G_host = [torch.from_numpy(workloads.host_custom(s, 0.01, (95, i))) for i, s in enumerate(shapes)]
+
+    def run(sel):
+        opt = make_opt([shapes[i] for i in sel], "bf16")
+        W = [W_init[i].to(dev) for i in sel]
+        M = [torch.zeros(shapes[i], device=dev) for i in sel]
+        G = [G_host[i].to(dev) for i in sel]
+        opt.init(W)
+        for _ in range(2):
+            opt.step(W, G, M, 0.02, 0.95, 5)
+        torch.cuda.synchronize()
+        return [w.cpu() for w in W], [opt.read_update(j).cpu() for j in range(len(sel))]
+
+    w_pair, o_pair = run([0, 1])
+    for i in (0, 1):
+        w_1, o_1 = run([i])
+        assert torch.equal(w_1[0], w_pair[i]) and torch.equal(o_1[0], o_pair[i]), f"matrix {i}"
+
+
 def test_small_tiles_match_large():
     # A 512x512 matrix alone runs its Newton-Schulz GEMMs on 128x128 tiles;
     # in a batch of 64 on 256x256 tiles. Both are parity-tested against the
