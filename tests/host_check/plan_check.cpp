@@ -139,7 +139,10 @@ void check_gemm(GemmMode mode, NsPrec prec, const GemmArgs& a) {
     EXPECT(g.K % kPad == 0 && g.K >= kPad);
     EXPECT(g.tile_begin == tiles);
     EXPECT(g.tiles_per_mat == (sym ? g.tm * (g.tm + 1) / 2 : g.tm * g.tn));
-    if (sym) EXPECT(g.tm == g.tn);
+    // a symmetric product reads one operand on both sides (P P^T): the
+    // kernels compute upper tiles only, and a diagonal tile's lower-left
+    // quadrant as the mirror of its upper-right one
+    if (sym) EXPECT(g.tm == g.tn && g.offP == g.offQ && g.ldp == g.ldq);
     if (i > 0) EXPECT(a.g[i - 1].K >= g.K);   // heaviest groups first
     tiles += (int64_t)g.count * g.tiles_per_mat;
     const uintptr_t base = reinterpret_cast<uintptr_t>(g.base);
