@@ -453,6 +453,8 @@ int main() {
   std::vector<muonh_group_desc> occ = {{512, 1536, 256}, {1536, 512, 256}};
   std::vector<muonh_group_desc> large = {{4096, 14336, 32}, {14336, 4096, 32}};
   std::vector<muonh_group_desc> maxdim = {{65536, 256, 1}, {256, 65536, 1}, {65536, 1, 2}};
+  // the largest square matrix: 2^32 entries, 32896 symmetric and 65536 apply tiles
+  std::vector<muonh_group_desc> maxsq = {{65536, 65536, 1}};
   std::vector<muonh_group_desc> tail = {{512, 512, 96}, {768, 512, 96}};
   for (uint32_t p : precs)
     for (uint32_t s : states) {
@@ -463,6 +465,7 @@ int main() {
       run_plan("tail balanced", tail, f);
     }
   for (uint32_t p : precs) {
+    run_plan("largest square matrix", maxsq, p);
     run_plan("2B-shaped set", qwen, p);
     run_plan("occupancy set", occ, p);
     run_plan("4096x14336 set", large, p);

@@ -202,6 +202,83 @@ def test_maximum_dimension(prec):
                       label=f"max dim {prec}")
 
 
+@pytest.mark.parametrize("shape", [(65536, 65536), (65536, 65535)])
+def test_largest_matrices_in_closed_form(shape):
+    # The largest plans: 65536 x 65536 and, on the transposed path with a
+    # column count that is not a multiple of 4 (the scalar streaming loops),
+    # 65536 x 65535; both past 2^32 entries, so every offset past 2^31 and
+    # 2^32 in the streaming kernels, K = 65536 in all three products, 32896
+    # Gram and 65536 apply tiles. The oracle cannot run at this size, so the
+    # input has a closed form: with M0 = 0 and G holding one 1 per column in
+    # distinct rows (a permutation matrix when square), G^T G = I, so the new
+    # momentum is G, every singular value of X0 = G / (||G|| + eps) is
+    # s = 1 / (sqrt(cols) + eps), and O = p^5(s) G exactly (the odd quintic
+    # applied to equal singular values), zero elsewhere. The scalar p^5(s)
+    # comes from the oracle on diag(1, sqrt(cols - 1)), whose first entry
+    # normalises to the same s (a diagonal matrix is orthogonalised entry by
+    # entry). Checked: M equals G bit for bit; every entry of O within the
+    # bf16 bar of p^5(s) G (bf16 rounds the scalar at each stage: about 3e-3
+    # by emulation); W within 2e-6 of the projection of the GPU's own O,
+    # computed in fp64 from the same W0; R and the sphere as everywhere else.
+    import orthogonalized_updates_amd as mh
+    need_gpu()
+    mh.get_lib()
+    torch.cuda.empty_cache()
+    nr, nc = shape
+    lr, k = 0.02, 5
+    c = float(oracle.newton_schulz(np.diag([1.0, np.sqrt(nc - 1.0)]), k)[0, 0])
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(nr + nc)
+    rows_of = torch.randperm(nr, generator=torch.Generator().manual_seed(4099))[:nc].to(dev)
+    cols = torch.arange(nc, device=dev)
+    say(f"[largest {nr}x{nc}] generating W0 and a one-per-column gradient")
+    W0 = torch.randn((nr, nc), generator=gen, device=dev) * 0.02
+    W = W0.clone()
+    M = torch.zeros((nr, nc), device=dev)
+    G = torch.zeros((nr, nc), device=dev)
+    G[rows_of, cols] = 1.0
+    opt = make_opt([(nr, nc)], "bf16")
+    R = float(opt.init([W])[0])
+    rows = 4096
+    r2 = sum(float(torch.sum(W0[i:i + rows].double() ** 2)) for i in range(0, nr, rows))
+    assert abs(R / np.sqrt(r2) - 1.0) <= 1e-6
+    say(f"[largest {nr}x{nc}] step (K = {k})")
+    opt.step([W], [G], [M], lr, 0.95, k)
+    torch.cuda.synchronize()
+    assert torch.equal(M, G)
+    del M
+    O = opt.read_update(0)
+    torch.cuda.synchronize()
+    say(f"[largest {nr}x{nc}] checking O against p^5(s) G and W against the projection")
+    err_max, err2, t2 = 0.0, 0.0, 0.0
+    for i in range(0, nr, rows):
+        exp = torch.zeros((rows, nc), device=dev)
+        sel = (rows_of >= i) & (rows_of < i + rows)
+        exp[rows_of[sel] - i, cols[sel]] = c
+        d = O[i:i + rows] - exp
+        err_max = max(err_max, float(d.abs().max()))
+        err2 += float(torch.sum(d.double() ** 2))
+        t2 += float(torch.sum(exp.double() ** 2))
+    assert err_max <= 2e-2 * c, f"O entry off by {err_max:.3e} (c = {c:.6f})"
+    assert np.sqrt(err2 / t2) <= 2e-2
+    w2 = sum(float(torch.sum((W0[i:i + rows].double() - lr * O[i:i + rows].double()) ** 2))
+             for i in range(0, nr, rows))
+    scale = R / np.sqrt(w2)
+    dw2, ww2 = 0.0, 0.0
+    for i in range(0, nr, rows):
+        ref = (W0[i:i + rows].double() - lr * O[i:i + rows].double()) * scale
+        dw2 += float(torch.sum((W[i:i + rows].double() - ref) ** 2))
+        ww2 += float(torch.sum(ref ** 2))
+    assert np.sqrt(dw2 / ww2) <= 2e-6
+    nw2 = sum(float(torch.sum(W[i:i + rows].double() ** 2)) for i in range(0, nr, rows))
+    assert abs(np.sqrt(nw2) / R - 1.0) <= 1e-5
+    say(f"[largest {nr}x{nc}] O max entry error {err_max / c:.2e} of p^5(s) = {c:.6f}, "
+        f"W vs projection {np.sqrt(dw2 / ww2):.2e}")
+    del W, W0, G, O, opt
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("prec", ["bf16", "split_bf16"])
 def test_eight_iterations(prec):
     # bf16 storage in the definition's order costs 2.05e-2 to 2.18e-2 here at
