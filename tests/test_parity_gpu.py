@@ -37,6 +37,11 @@ def make_opt(shapes, prec):
     return mh.MuonH(shapes, precision=prec)
 
 
+def mh_opt(shapes, **kw):
+    import orthogonalized_updates_amd as mh
+    return mh.MuonH(shapes, **kw)
+
+
 def host_arr(x):
     return x.float().cpu().numpy() if hasattr(x, "cpu") else x
 
@@ -652,37 +657,37 @@ def test_qwen3_2b_full_size_sampled():
                         label="qwen3_2b", workers=4)
 
 
-def weighted_lines(shape, seed, dev):
+def weighted_lines(shape, seed, dev, dtype=torch.float32):
     """An s x l (or l x s) matrix whose long-side lines (rows of a wide
     matrix, columns of a tall one) each hold k = l / s equal entries on
     disjoint supports at seeded random positions, each line with its own
-    fp32 weight in [0.5, 1.5). M M^T (wide) or M^T M (tall) is then
-    diagonal: the singular values are the line norms w sqrt(k), the singular
-    vectors the lines themselves. Returns the matrix, k and the weights (fp64
-    of the fp32 values)."""
+    weight in [0.5, 1.5) (a value `dtype` holds exactly). M M^T (wide) or
+    M^T M (tall) is then diagonal: the singular values are the line norms
+    w sqrt(k), the singular vectors the lines themselves. Returns the matrix
+    and k."""
     r, c = shape
     s, l = min(r, c), max(r, c)
     assert l % s == 0
     k = l // s
     rng = np.random.default_rng(seed)
     perm = torch.from_numpy(rng.permutation(l)).to(dev)
-    w = (0.5 + rng.random(s)).astype(np.float32)
-    wt = torch.from_numpy(w).to(dev)
+    wt = torch.from_numpy((0.5 + rng.random(s)).astype(np.float32)).to(dev).to(dtype)
     owner = torch.arange(l, device=dev) // k
-    g = torch.zeros(shape, device=dev)
+    g = torch.zeros(shape, device=dev, dtype=dtype)
     if r <= c:
         g[owner, perm] = wt[owner]
     else:
         g[perm, owner] = wt[owner]
-    return g, k, w.astype(np.float64)
+    return g, k
 
 
 def line_factors(k, w, k_it, chunk=255):
-    """Per line, p^K(sigma) / norm: O = factor * (the line) for the matrix of
-    weighted_lines. The oracle orthogonalises a diagonal matrix entry by
-    entry after one Frobenius normalisation, so it runs on chunks of the line
-    norms, each with one more entry that restores the full Frobenius norm."""
-    n_line = w * np.sqrt(k)
+    """Per line, p^K(sigma) / norm for a matrix of weighted_lines' structure
+    whose lines hold the values w: O = factor * (the line). The oracle
+    orthogonalises a diagonal matrix entry by entry after one Frobenius
+    normalisation, so it runs on chunks of the line norms, each with one more
+    entry that restores the full Frobenius norm."""
+    n_line = np.asarray(w, dtype=np.float64) * np.sqrt(k)
     total = float(np.sum(n_line ** 2))
     out = np.empty_like(n_line)
     for i in range(0, len(n_line), chunk):
@@ -693,74 +698,97 @@ def line_factors(k, w, k_it, chunk=255):
     return out
 
 
-def test_qwen3_2b_every_matrix_closed_form():
+@pytest.mark.parametrize("variant", ["muonh", "muonh_bf16_state", "muon_wd"])
+def test_qwen3_2b_every_matrix_closed_form(variant):
     # All 196 matrices of the 2B-shaped set in the benchmark's plan, at full
-    # size, every entry of every update checked. With M0 = 0 and each G built
-    # by weighted_lines, the momentum's singular values are its line norms
-    # and O is each line scaled by p^5(sigma) / norm (line_factors, from the
-    # oracle), zero off the lines; a second step with the same G scales M by
-    # (1 + beta) and leaves O unchanged. Checked, for every matrix and both
-    # steps: O within the bf16 bar on the whole matrix (measured at most
-    # 1.54e-2 over the set, the 512-wide matrices; bf16 emulation of single
-    # matrices: 0.9e-2 to 1.45e-2); every entry on the lines within
-    # 25 % of its value and every entry off them exactly zero, which a
-    # misplaced, missing or stale tile cannot meet. (On this input each
-    # line's entries share one scalar, so rounding errors are coherent along
-    # a line: single entries reach 6.6e-2 by emulation, and a 256 x 256 tile
-    # holds only tens to a hundred lines, so the per-tile bar of random
-    # inputs does not apply; the oracle-checked tests keep it.) Also M (bit
-    # for bit at the first step, within 1e-6 at the second), W within 2e-6
-    # of the fp64 projection of the GPU's own O, and the sphere.
+    # size, every entry of every update checked: MuonH with fp32 and with
+    # bf16 gradient and momentum storage, and the Muon baseline. With M0 = 0
+    # and each G built by weighted_lines, the momentum keeps that structure
+    # (beta M + G scales each line by one value), its singular values are its
+    # line norms, and O is each line of M scaled by p^5(sigma) / norm
+    # (line_factors, from the oracle, on the line values of the GPU's own
+    # M), zero off the lines. Checked, for every matrix and both steps: O
+    # within the bf16 bar on the whole matrix (measured at most 1.54e-2 over
+    # the set, the 512-wide matrices; bf16 emulation of single matrices:
+    # 0.9e-2 to 1.45e-2); every entry on the lines within 25 % of its value
+    # and every entry off them exactly zero, which a misplaced, missing or
+    # stale tile cannot meet. (On this input each line's entries share one
+    # scalar, so rounding errors are coherent along a line: single entries
+    # reach 6.6e-2 by emulation, and a 256 x 256 tile holds only tens to a
+    # hundred lines, so the per-tile bar of random inputs does not apply; the
+    # oracle-checked tests keep it.) M: bit for bit at the first step (beta 0
+    # + G), within 1e-6 at the second (fp32; bf16: within its rounding,
+    # 2^-8). W: MuonH within 2e-6 of the fp64 projection of the GPU's own O,
+    # and the sphere; Muon within 1e-6 (||W|| + lr ||O||) of its decayed
+    # update of the GPU's own O.
     need_gpu()
     torch.cuda.empty_cache()
     wl = workloads.WORKLOADS["qwen3_2b"]
     dev = torch.device("cuda")
-    lr, beta, k_it = wl.lr, wl.beta, 5
+    lr, beta, wd, k_it = wl.lr, wl.beta, 0.1, 5
     tol = TOL_O["bf16"]
-    opt = make_opt(wl.shapes, "bf16")
-    say(f"[2B closed form] generating {wl.n_matrices} matrices")
+    sdt = torch.bfloat16 if variant == "muonh_bf16_state" else torch.float32
+    if variant == "muonh_bf16_state":
+        opt = mh_opt(wl.shapes, grad_dtype="bf16", mom_dtype="bf16")
+    else:
+        opt = make_opt(wl.shapes, "bf16")
+    say(f"[2B closed form {variant}] generating {wl.n_matrices} matrices")
     W = [workloads.device_weight_(wl, i, torch.empty(s, device=dev)) for i, s in enumerate(wl.shapes)]
-    M = [torch.zeros(s, device=dev) for s in wl.shapes]
-    G, F = [], []
+    M = [torch.zeros(s, device=dev, dtype=sdt) for s in wl.shapes]
+    G, K = [], []
     for i, shp in enumerate(wl.shapes):
-        g, k, w = weighted_lines(shp, 7000 + i, dev)
-        f = torch.from_numpy(line_factors(k, w, k_it)).to(dev)
+        g, k = weighted_lines(shp, 7000 + i, dev, sdt)
         G.append(g)
-        F.append(f[:, None] if shp[0] <= shp[1] else f[None, :])
+        K.append(k)
     R = opt.init(W).cpu().numpy()
     worst_o, worst_e, worst_w, worst_s = 0.0, 0.0, 0.0, 0.0
     for step in range(2):
         W_pre = [w.clone() for w in W]
         M_pre = [m.clone() for m in M]
-        opt.step(W, G, M, lr, beta, k_it)
+        if variant == "muon_wd":
+            opt.step_muon_wd(W, G, M, lr, beta, wd, k_it)
+        else:
+            opt.step(W, G, M, lr, beta, k_it)
         torch.cuda.synchronize()
-        for i in range(wl.n_matrices):
+        for i, (r, c) in enumerate(wl.shapes):
             if step == 0:
                 assert torch.equal(M[i], G[i]), f"mat {i}: M"
             else:
                 m_ref = float(np.float32(beta)) * M_pre[i].double() + G[i].double()
-                e_m = float(torch.linalg.vector_norm(M[i].double() - m_ref) / torch.linalg.vector_norm(m_ref))
-                assert e_m <= 1e-6, f"step 1 mat {i}: M rel err {e_m:.3e}"
+                d_m = (M[i].double() - m_ref).abs().max() / m_ref.abs().max()
+                bar_m = 1e-6 if sdt == torch.float32 else 2.0 ** -8
+                assert float(d_m) <= bar_m, f"step 1 mat {i}: M off by {float(d_m):.3e}"
+            wide = r <= c
+            v = (M[i].amax(dim=1) if wide else M[i].amax(dim=0)).double().cpu().numpy()
+            f = torch.from_numpy(line_factors(K[i], v, k_it)).to(dev)
             o = opt.read_update(i).double()
-            ref = G[i].double() * F[i]
-            on = G[i] != 0
+            ref = M[i].double() * (f[:, None] if wide else f[None, :])
+            on = M[i] != 0
             assert float(o[~on].abs().max()) == 0.0, f"step {step} mat {i}: O off the lines"
             e_e = float(((o[on] - ref[on]).abs() / ref[on].abs()).max())
             e_o = float(torch.linalg.vector_norm(o - ref) / torch.linalg.vector_norm(ref))
             assert e_o <= tol, f"step {step} mat {i}: O rel err {e_o:.3e}"
             assert e_e <= 0.25, f"step {step} mat {i}: an O entry off by {e_e:.3e} of its value"
-            trial = W_pre[i].double() - lr * o
-            wref = trial * (float(R[i]) / float(torch.linalg.vector_norm(trial)))
-            e_w = float(torch.linalg.vector_norm(W[i].double() - wref) / torch.linalg.vector_norm(wref))
-            assert e_w <= 2e-6, f"step {step} mat {i}: W vs projection {e_w:.3e}"
-            e_s = abs(float(torch.linalg.vector_norm(W[i].double())) / float(R[i]) - 1.0)
-            assert e_s <= 1e-5, f"step {step} mat {i}: sphere {e_s:.3e}"
-            worst_o, worst_e = max(worst_o, e_o), max(worst_e, e_e)
-            worst_w, worst_s = max(worst_w, e_w), max(worst_s, e_s)
-        say(f"[2B closed form] step {step}: {wl.n_matrices} matrices checked")
+            wp = W_pre[i].double()
+            if variant == "muon_wd":
+                wref = (1.0 - lr * wd) * wp - lr * o
+                bar = 1e-6 * (float(torch.linalg.vector_norm(wp)) + lr * float(torch.linalg.vector_norm(o)))
+                d_w = float(torch.linalg.vector_norm(W[i].double() - wref))
+                assert d_w <= bar, f"step {step} mat {i}: W vs decayed update {d_w:.3e} > {bar:.3e}"
+                e_w = d_w / float(torch.linalg.vector_norm(wref))
+            else:
+                trial = wp - lr * o
+                wref = trial * (float(R[i]) / float(torch.linalg.vector_norm(trial)))
+                e_w = float(torch.linalg.vector_norm(W[i].double() - wref) / torch.linalg.vector_norm(wref))
+                assert e_w <= 2e-6, f"step {step} mat {i}: W vs projection {e_w:.3e}"
+                e_s = abs(float(torch.linalg.vector_norm(W[i].double())) / float(R[i]) - 1.0)
+                assert e_s <= 1e-5, f"step {step} mat {i}: sphere {e_s:.3e}"
+                worst_s = max(worst_s, e_s)
+            worst_o, worst_e, worst_w = max(worst_o, e_o), max(worst_e, e_e), max(worst_w, e_w)
+        say(f"[2B closed form {variant}] step {step}: {wl.n_matrices} matrices checked")
         del W_pre, M_pre
-    say(f"[2B closed form] worst: O {worst_o:.2e}, O entry {worst_e:.2e} of its value, "
-        f"W vs projection {worst_w:.2e}, sphere {worst_s:.2e}")
+    say(f"[2B closed form {variant}] worst: O {worst_o:.2e}, O entry {worst_e:.2e} of its value, "
+        f"W {worst_w:.2e}, sphere {worst_s:.2e}")
 
 
 def test_long_run_stays_on_the_sphere():
